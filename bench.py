@@ -1,0 +1,322 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+One step = gate prep + chunkwise prefill of the packed varlen batch of four
+sequences {512, 1024, 2048, 4096} (H=32, K=V=128, bf16 q/k/v, fp32 gates and
+states, chunk 64), inputs resident in HBM.  ``value`` is prefill tokens/s of
+that step.  The same run also measures, each on its own workload:
+  decode  - 256 single-token requests on a 512-slot fp32 state pool
+            (tokens/s and state GB/s against HBM peak);
+  verify  - 64 requests x 8 draft tokens on a 128-slot pool;
+  long    - one 65536-token sequence as 16 carried 4096-token segments;
+and the fp64 CPU oracle on the prefill workload (``cpu_baseline``).
+
+Timing uses HIP events on the stream the library launches on (torch's
+current stream): W untimed warm-up steps, then K steps bracketed by
+synchronisations.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import kda_gated_delta_amd as kda  # noqa: E402
+import kda_synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
+
+
+def _dev(x, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
+
+
+def _time(fn, steps: int, warmup: int) -> float:
+    """Average milliseconds per call of fn over `steps` calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+# ------------------------------------------------------------ byte models
+
+def prefill_bytes(T, N, H, K, V, io_bytes=2):
+    """Algorithmic HBM bytes of one prefill call: q, k, v, o in the io dtype,
+    g fp32, beta fp32 per token-head; h0 read and ht written per sequence."""
+    per_tok_head = (2 * K + 2 * V) * io_bytes + 4 * K + 4
+    return T * H * per_tok_head + 2 * N * H * K * V * 4
+
+
+def gate_bytes(T, H, K):
+    """a read, g written (fp32, per channel); b read, beta written."""
+    return T * H * (8 * K + 8)
+
+
+def prefill_flops(T, H, K, V, C):
+    """Algorithmic flops per token-head of the chunk form (triangle-aware):
+    2 (3 K V + C K + (C-1) K / 2 + C V)."""
+    return T * H * 2 * (3 * K * V + C * K + (C - 1) * K / 2 + C * V)
+
+
+def decode_bytes(B, H, K, V, io_bytes=2):
+    """State read + write (fp32) plus q, k, v, o, g, beta per request-head."""
+    return B * H * (2 * K * V * 4 + (2 * K + 2 * V) * io_bytes + 4 * K + 4)
+
+
+def verify_bytes(B, Tv, H, K, V, io_bytes=2):
+    """One state read, Tv state writes, and the per-token inputs/outputs."""
+    return B * H * (K * V * 4 * (1 + Tv) + Tv * ((2 * K + 2 * V) * io_bytes + 4 * K + 4))
+
+
+# -------------------------------------------------------------- workloads
+
+def prefill_setup(name):
+    w = kda_synth.WORKLOADS[name]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"], seed=w["seed"],
+                               dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+    io = torch.bfloat16 if w["io"] == "bf16" else torch.float32
+    t = dict(q=_dev(c["q"], io), k=_dev(c["k"], io), v=_dev(c["v"], io), a=_dev(c["a"]),
+             b=_dev(c["b"]), A_log=_dev(c["A_log"]), dt_bias=_dev(c["dt_bias"]),
+             cu=_dev(c["cu"], torch.int32), h0=_dev(c["h0"]))
+    return w, c, t
+
+
+def bench_prefill(steps, warmup):
+    w, c, t = prefill_setup("varlen_prefill_7680")
+    T, N, H, K, V, C = c["T"], c["N"], w["H"], w["K"], w["V"], w["chunk"]
+    scale = K ** -0.5
+    g = torch.empty_like(t["a"])
+    beta = torch.empty_like(t["b"])
+    o = torch.empty_like(t["v"])
+    ht = torch.empty_like(t["h0"])
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_size(T, N, H, K, V, C),
+                     dtype=torch.uint8, device="cuda")
+
+    def gate():
+        kda.kda_gate_prep(t["a"], t["b"], t["A_log"], t["dt_bias"], g=g, beta=beta)
+
+    def prefill():
+        kda.kda_chunk_prefill(t["q"], t["k"], t["v"], g, beta, t["cu"], scale, h0=t["h0"],
+                              chunk=C, o=o, ht=ht, workspace=ws)
+
+    def step():
+        gate()
+        prefill()
+
+    ms_step = _time(step, steps, warmup)
+    ms_gate = _time(gate, steps, warmup)
+    ms_prefill = _time(prefill, steps, warmup)
+    pb = prefill_bytes(T, N, H, K, V)
+    gb = gate_bytes(T, H, K)
+    return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_gate=ms_gate,
+                ms_prefill=ms_prefill, prefill_bytes=pb, gate_bytes=gb,
+                flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
+
+
+def bench_decode(steps, warmup):
+    w = kda_synth.WORKLOADS["decode_256"]
+    c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
+                              seed=w["seed"], dt_bias_std=w["dt_bias_std"],
+                              state_std=w["state_std"])
+    a, b = _dev(c["a"]), _dev(c["b"])
+    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+    o = torch.empty_like(v)
+    fn = lambda: kda.kda_recurrent_decode(q, k, v, g, beta, w["K"] ** -0.5, pool, idx, o=o)
+    ms = _time(fn, max(steps, 20), warmup)
+    B, H, K, V = w["B"], w["H"], w["K"], w["V"]
+    nbytes = decode_bytes(B, H, K, V)
+    state = 2 * B * H * K * V * 4
+    return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9)
+
+
+def bench_verify(steps, warmup):
+    w = kda_synth.WORKLOADS["verify_64x8"]
+    c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
+                              seed=w["seed"], dt_bias_std=w["dt_bias_std"],
+                              state_std=w["state_std"], Tv=w["Tv"])
+    B, Tv, H, K, V = w["B"], w["Tv"], w["H"], w["K"], w["V"]
+    a, b = _dev(c["a"]).reshape(B * Tv, H, K), _dev(c["b"]).reshape(B * Tv, H)
+    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+    g, beta = g.reshape(B, Tv, H, K), beta.reshape(B, Tv, H)
+    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+    inter = torch.empty((B, Tv, H, K, V), device="cuda")
+    o = torch.empty_like(v)
+    fn = lambda: kda.kda_verify(q, k, v, g, beta, K ** -0.5, pool, idx, inter_states=inter, o=o)
+    ms = _time(fn, max(steps, 20), warmup)
+    nbytes = verify_bytes(B, Tv, H, K, V)
+    return dict(ms=ms, tokens_per_s=B * Tv / (ms * 1e-3), bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
+def bench_long(steps, warmup):
+    w = kda_synth.WORKLOADS["long_prefill_65536"]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"], seed=w["seed"],
+                               dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+    H, K, V, C, nseg = w["H"], w["K"], w["V"], w["chunk"], w["segments"]
+    T = c["T"]
+    seg = T // nseg
+    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+    g, beta = kda.kda_gate_prep(_dev(c["a"]), _dev(c["b"]), _dev(c["A_log"]),
+                                _dev(c["dt_bias"]))
+    h0 = _dev(c["h0"])
+    state = torch.empty_like(h0)
+    o = torch.empty_like(v)
+    cu_seg = torch.tensor([0, seg], dtype=torch.int32, device="cuda")
+    cu_full = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_size(T, 1, H, K, V, C),
+                     dtype=torch.uint8, device="cuda")
+
+    def segmented():
+        state.copy_(h0)
+        for s in range(nseg):
+            sl = slice(s * seg, (s + 1) * seg)
+            kda.kda_chunk_prefill(q[sl], k[sl], v[sl], g[sl], beta[sl], cu_seg, K ** -0.5,
+                                  h0=state, ht=state, chunk=C, o=o[sl], workspace=ws)
+
+    def full():
+        kda.kda_chunk_prefill(q, k, v, g, beta, cu_full, K ** -0.5, h0=h0, ht=state,
+                              chunk=C, o=o, workspace=ws)
+
+    n = max(2, steps // 10)
+    ms_seg = _time(segmented, n, 1)
+    ms_full = _time(full, n, 1)
+    return dict(T=T, ms_segmented=ms_seg, ms_full=ms_full,
+                tokens_per_s_segmented=T / (ms_seg * 1e-3),
+                tokens_per_s_full=T / (ms_full * 1e-3),
+                bytes=prefill_bytes(T, 1, H, K, V))
+
+
+def cpu_baseline(inputs, workload):
+    """The fp64 oracle on the whole prefill workload (gate + prefill), on all
+    host cores, timed by wall clock."""
+    import oracle  # test infrastructure: used only for this reported baseline
+
+    c, _, _ = inputs
+    nthreads = os.cpu_count() or 1
+    t0 = time.time()
+    g, beta = oracle.gate(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    oracle.prefill(c["q"], c["k"], c["v"], g.astype(np.float32), beta.astype(np.float32),
+                   c["cu"], workload["K"] ** -0.5, c["h0"], nthreads=nthreads)
+    dt = time.time() - t0
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(value=c["T"] / dt, unit="tokens/s", cores=nthreads, kind="oracle",
+                sample=f"whole varlen prefill batch ({c['T']} tokens x {workload['H']} heads, "
+                       f"gate + token-serial fp64 recurrence), {dt:.1f} s wall, CPU: {cpu}")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-long", action="store_true", help="skip the 65536-token workload")
+    ap.add_argument("--only", choices=["prefill", "decode", "verify", "long"], default=None,
+                    help="time a single workload (for profiler runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the recurrence shards by head or request with no communication, "
+              "but no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.only == "prefill":
+        p = bench_prefill(args.steps, args.warmup)
+        p.pop("inputs")
+        p.pop("workload")
+        print(json.dumps(p))
+        return
+    if args.only == "decode":
+        print(json.dumps(bench_decode(args.steps, args.warmup)))
+        return
+    if args.only == "verify":
+        print(json.dumps(bench_verify(args.steps, args.warmup)))
+        return
+    if args.only == "long":
+        print(json.dumps(bench_long(args.steps, args.warmup)))
+        return
+
+    p = bench_prefill(args.steps, args.warmup)
+    w = p["workload"]
+    tokens_per_s = p["T"] / (p["ms_step"] * 1e-3)
+    achieved = p["prefill_bytes"] / (p["ms_prefill"] * 1e-3) / 1e9
+    line = {
+        "metric": "KDA prefill tokens/s; decode tokens/s + state HBM GB/s (% of peak), 1 GPU",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": p["ms_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "varlen_prefill_7680: 4 packed sequences {512,1024,2048,4096}, "
+                               "H=32, K=V=128, chunk 64, gate prep + prefill per step",
+                   "global_batch": p["N"], "seq_len": p["T"], "parallelism": "none"},
+        "roofline": {"bound": "hbm", "kernel": "kda_chunk_prefill (plan+intra+state)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "prefill": {"ms": p["ms_prefill"], "ms_gate": p["ms_gate"],
+                    "tokens_per_s": p["T"] / (p["ms_prefill"] * 1e-3),
+                    "algorithmic_bytes": p["prefill_bytes"],
+                    "algorithmic_flops": p["flops"],
+                    "tflops": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12,
+                    "mfma_frac_of_bf16_peak": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12
+                    / BF16_MFMA_PEAK_TFLOPS,
+                    "gate_gbs": p["gate_bytes"] / (p["ms_gate"] * 1e-3) / 1e9},
+    }
+    d = bench_decode(args.steps, args.warmup)
+    line["decode"] = {"workload": "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",
+                      "tokens_per_s": d["tokens_per_s"], "ms": d["ms"],
+                      "state_gbs": d["state_gbs"], "total_gbs": d["gbs"],
+                      "frac_of_hbm_peak": d["gbs"] / HBM_PEAK_GBS}
+    vr = bench_verify(args.steps, args.warmup)
+    line["verify"] = {"workload": "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool",
+                      "tokens_per_s": vr["tokens_per_s"], "ms": vr["ms"],
+                      "total_gbs": vr["gbs"], "frac_of_hbm_peak": vr["gbs"] / HBM_PEAK_GBS}
+    if not args.no_long:
+        lg = bench_long(args.steps, args.warmup)
+        line["long"] = {"workload": "long_prefill_65536: 16 carried 4096-token segments "
+                                    "and one full run",
+                        "tokens_per_s_segmented": lg["tokens_per_s_segmented"],
+                        "tokens_per_s_full": lg["tokens_per_s_full"],
+                        "ms_segmented": lg["ms_segmented"], "ms_full": lg["ms_full"]}
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(p["inputs"], w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

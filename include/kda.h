@@ -1,0 +1,162 @@
+/*
+ * kda.h -- C ABI of libkda: Kimi Delta Attention (KDA) gated delta rule on
+ * AMD Instinct MI355X (gfx950), hand-written HIP kernels.
+ *
+ * The method (sources cited by page title and section):
+ *   "Linear attention" tutorial (zdszero.github.io), section "KDA：逐通道的遗忘门":
+ *     S_t = (I - beta_t k_t^T k_t) Diag(exp g_t) S_{t-1} + beta_t k_t^T v_t,
+ *     row vectors q_t, k_t in R^{1 x K}, v_t in R^{1 x V}, state S in R^{K x V};
+ *     g_t in R^K is a per-key-channel log decay (g <= 0).
+ *   same page, section "实例：Kimi K3": o_t = scale * q_t S_t (scale = K^-1/2
+ *     in the model; here an explicit argument).
+ *   same page, sections "Gated DeltaNet" / "KDA": the gate
+ *     g = -exp(A_log[h]) * softplus(a + dt_bias[h, c]), beta = sigmoid(b);
+ *     the safe gate g = lower_bound * sigmoid(exp(A_log[h]) (a + dt_bias)).
+ *   same page, section "两种计算形态": chunkwise prefill (WY/UT form, one
+ *     64x64 triangular solve per chunk, state carried between chunks) and
+ *     recurrent single-token decode that rewrites the pool state in place.
+ *   "PR #26888 report" ([KDA] target_verify): multi-token verify that records
+ *     the state after every draft token and never updates the pool.
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller, to a
+ *     row-major contiguous array, 16-byte aligned.  The library allocates no
+ *     memory, keeps no global mutable state, never synchronises the stream,
+ *     and may be called from several host threads at once.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it; a return of KDA_OK means "enqueued".
+ *   - States and gates are always fp32.  q, k, v and o share the io dtype.
+ *   - State layout is [.., H, K, V] with V contiguous: row i of a head's
+ *     state belongs to key channel i.
+ *   - q and k are expected to be L2-normalised per (token, head) by the
+ *     caller; the library does not renormalise.
+ *   - Errors are returned, never thrown.  Host-side validation covers null
+ *     pointers, alignment, sizes and supported shapes; on any error nothing
+ *     is enqueued.  Values that live in device memory (cu_seqlens, slot
+ *     indices) are the caller's contract and are not read by the host.
+ *   - Supported head sizes: K, V in {16, 32, 64, 128}.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, misalignment, bad size   */
+  KDA_ERR_UNSUPPORTED = 2,      /* shape or dtype outside the built set   */
+  KDA_ERR_LAUNCH = 3,           /* the HIP runtime refused a launch       */
+  KDA_ERR_WORKSPACE = 4         /* workspace missing or too small         */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype; /* dtype of q, k, v, o */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* kda_status_string(kda_status s);
+
+/*
+ * Gate activation (tutorial, sections "Gated DeltaNet" and "KDA").
+ *   a       [T, H, K] fp32  raw per-channel gate input
+ *   b       [T, H]    fp32  raw write-strength input
+ *   A_log   [H]       fp32  per-head log decay rate
+ *   dt_bias [H, K]    fp32  per-channel bias, or NULL for zero
+ *   lower_bound: 0.f selects g = -exp(A_log) softplus(a + dt_bias) with
+ *     softplus(x) = x for x > 20 (threshold of the ReplaySSM and target-verify
+ *     kernels); a negative value selects the safe gate
+ *     g = lower_bound * sigmoid(exp(A_log) (a + dt_bias)).
+ *   g       [T, H, K] fp32  output log decay (<= 0)
+ *   beta    [T, H]    fp32  output sigmoid(b)
+ * T may be 0 (nothing is enqueued).  K must be a multiple of 4.
+ */
+kda_status kda_gate_prep(const float* a, const float* b, const float* A_log,
+                         const float* dt_bias, int64_t T, int32_t H, int32_t K,
+                         float lower_bound, float* g, float* beta,
+                         void* stream);
+
+/*
+ * Bytes of device workspace kda_chunk_prefill needs for a packed batch of
+ * T tokens in N sequences (an upper bound that holds for every split of T
+ * into N lengths).  Returns 0 for unsupported arguments.
+ */
+size_t kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
+                                        int32_t K, int32_t V, int32_t chunk);
+
+/*
+ * Chunkwise varlen prefill (tutorial, section "两种计算形态"; the WY/UT form
+ * of the unrolled delta rule, section "矩阵（并行）形式").
+ *   q, k    [T, H, K] io dtype;  v [T, H, V] io dtype
+ *   g       [T, H, K] fp32 activated log decay;  beta [T, H] fp32
+ *   cu_seqlens [N + 1] int32 (device): sequence n owns tokens
+ *     cu[n] .. cu[n+1]-1; must satisfy cu[0] = 0 <= cu[1] <= ... <= cu[N] = T.
+ *     Zero-length sequences are allowed (ht[n] = h0[n], or zeros).
+ *   chunk   16, 32 or 64: chunks never cross a sequence boundary; the last
+ *     chunk of a sequence may be short.  The result does not depend on it
+ *     beyond rounding.
+ *   scale   read-out factor (o_t = scale * q_t S_t)
+ *   h0      [N, H, K, V] fp32 initial states, or NULL for zeros
+ *   ht      [N, H, K, V] fp32 final states, or NULL to skip; may alias h0
+ *   o       [T, H, V] io dtype output (fp32 accumulate, round to nearest even)
+ *   workspace / workspace_bytes: caller-owned device scratch of at least
+ *     kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk) bytes, 256-byte
+ *     aligned; its contents on entry are irrelevant.  It must not be reused
+ *     by another call until this call's work on `stream` has finished.
+ * T may be 0 (only ht = h0 is written).
+ */
+kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T,
+                             int32_t H, int32_t K, int32_t V, int32_t chunk,
+                             float scale, const float* h0, float* ht, void* o,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/*
+ * Single-token decode on a slot-indexed state pool, updated in place
+ * (tutorial, section "两种计算形态": the recurrent kernel rewrites the pool
+ * state; ReplaySSM analysis, section 3.6: a negative slot marks a padding row).
+ *   q, k [B, H, K], v [B, H, V] io dtype; g [B, H, K] fp32; beta [B, H] fp32
+ *   state_pool [n_slots, H, K, V] fp32, read and written in place
+ *   slot_idx [B] int32 (device): slot of each request; a negative value
+ *     marks a padding row, whose o is zero and whose state is not touched.
+ *     Live slots must be < n_slots and distinct within one call (two rows on
+ *     one slot race).
+ *   o [B, H, V] io dtype
+ * Per (request, head): S' = Diag(exp g) S; v_hat = k S'; d = beta (v - v_hat);
+ * S = S' + k^T d (written back); o = scale q S.
+ */
+kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g,
+                                const float* beta, float scale,
+                                float* state_pool, int64_t n_slots,
+                                const int32_t* slot_idx, int32_t B, int32_t H,
+                                int32_t K, int32_t V, void* o, void* stream);
+
+/*
+ * Multi-token verify without state update ("PR #26888 report": target_verify
+ * with disable_state_update and an intermediate-state buffer).
+ *   q, k [B, Tv, H, K], v [B, Tv, H, V] io dtype; g [B, Tv, H, K] fp32;
+ *   beta [B, Tv, H] fp32; state_pool [n_slots, H, K, V] fp32, READ ONLY;
+ *   slot_idx [B] int32 (device), negative = padding row (o = 0, inter rows
+ *   left unwritten);
+ *   inter_states [B, Tv, H, K, V] fp32: state after draft token s;
+ *   o [B, Tv, H, V] io dtype.
+ * Row r, step s equals the (s+1)-th of s+1 sequential decode calls started
+ * from pool[slot_idx[r]].
+ */
+kda_status kda_verify(kda_dtype io, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta,
+                      float scale, const float* state_pool, int64_t n_slots,
+                      const int32_t* slot_idx, int32_t B, int32_t Tv,
+                      int32_t H, int32_t K, int32_t V, float* inter_states,
+                      void* o, void* stream);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* KDA_H_ */

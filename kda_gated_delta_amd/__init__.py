@@ -1,0 +1,212 @@
+"""Python binding of libkda (KDA gated delta rule, HIP kernels for gfx950).
+
+Argument marshalling only: each function checks dtypes, shapes, devices and
+contiguity of torch tensors, passes raw device pointers and the current HIP
+stream to the C entry point of the same name (declared in include/kda.h), and
+raises ``KdaError`` on a non-OK status.  Every step of the computation runs
+in the library's kernels; there is no fallback of any kind.  PyTorch provides
+device memory and streams.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+_IO = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libkda.so (built by ``kda_gated_delta_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m kda_gated_delta_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_float, ctypes.c_size_t)
+    L.kda_status_string.argtypes = [ctypes.c_int]
+    L.kda_status_string.restype = ctypes.c_char_p
+    L.kda_gate_prep.argtypes = [vp, vp, vp, vp, i64, i32, i32, f32, vp, vp, vp]
+    L.kda_gate_prep.restype = ctypes.c_int
+    L.kda_chunk_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.kda_chunk_prefill_workspace_size.restype = sz
+    L.kda_chunk_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i64,
+                                    i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
+    L.kda_chunk_prefill.restype = ctypes.c_int
+    L.kda_recurrent_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64,
+                                       vp, i32, i32, i32, i32, vp, vp]
+    L.kda_recurrent_decode.restype = ctypes.c_int
+    L.kda_verify.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, i32,
+                             i32, i32, i32, i32, vp, vp, vp]
+    L.kda_verify.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
+            "kda_chunk_prefill", "kda_recurrent_decode", "kda_verify")
+
+
+def status_string(status: int) -> str:
+    return lib().kda_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise KdaError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape, device) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _IO:
+        raise TypeError(f"io dtype must be float32 or bfloat16, got {t.dtype}")
+    return _IO[t.dtype]
+
+
+def kda_gate_prep(a, b, A_log, dt_bias=None, lower_bound: float = 0.0,
+                  g=None, beta=None):
+    """g [T,H,K], beta [T,H] (fp32) from a [T,H,K], b [T,H], A_log [H],
+    dt_bias [H,K] (or None).  ``lower_bound < 0`` selects the safe gate."""
+    T, H, K = a.shape
+    dev = a.device
+    _need(a, "a", torch.float32, (T, H, K), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (H, K), dev)
+    g = torch.empty_like(a) if g is None else g
+    beta = torch.empty_like(b) if beta is None else beta
+    _need(g, "g", torch.float32, (T, H, K), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    _check("kda_gate_prep", lib().kda_gate_prep(
+        _ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), T, H, K, float(lower_bound),
+        _ptr(g), _ptr(beta), _stream(dev)))
+    return g, beta
+
+
+def kda_chunk_prefill_workspace_size(T: int, N: int, H: int, K: int, V: int,
+                                     chunk: int = 64) -> int:
+    return int(lib().kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk))
+
+
+def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
+                      output_final_state: bool = True, chunk: int = 64, o=None,
+                      ht=None, workspace=None):
+    """Varlen chunkwise prefill.  Returns (o [T,H,V], ht [N,H,K,V] or None).
+
+    ``ht`` may be passed explicitly (it may be ``h0`` itself for an in-place
+    update); ``workspace`` is a uint8 device tensor of at least
+    ``kda_chunk_prefill_workspace_size`` bytes (allocated here if None).
+    """
+    T, H, K = q.shape
+    V = v.shape[2]
+    dev = q.device
+    io = _io_dtype(q)
+    N = cu_seqlens.shape[0] - 1
+    _need(q, "q", q.dtype, (T, H, K), dev)
+    _need(k, "k", q.dtype, (T, H, K), dev)
+    _need(v, "v", q.dtype, (T, H, V), dev)
+    _need(g, "g", torch.float32, (T, H, K), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V), dev)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    if ht is not None:
+        _need(ht, "ht", torch.float32, (N, H, K, V), dev)
+    o = torch.empty((T, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (T, H, V), dev)
+    need = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("kda_chunk_prefill", lib().kda_chunk_prefill(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+        H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace),
+        workspace.numel(), _stream(dev)))
+    return o, ht
+
+
+def kda_recurrent_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx,
+                         o=None):
+    """Single-token decode; ``state_pool`` [n_slots,H,K,V] is updated in place.
+    Returns o [B,H,V]."""
+    B, H, K = q.shape
+    V = v.shape[2]
+    dev = q.device
+    io = _io_dtype(q)
+    n_slots = state_pool.shape[0]
+    _need(k, "k", q.dtype, (B, H, K), dev)
+    _need(v, "v", q.dtype, (B, H, V), dev)
+    _need(g, "g", torch.float32, (B, H, K), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    o = torch.empty((B, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (B, H, V), dev)
+    _check("kda_recurrent_decode", lib().kda_recurrent_decode(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+        _ptr(state_pool), n_slots, _ptr(slot_idx), B, H, K, V, _ptr(o), _stream(dev)))
+    return o
+
+
+def kda_verify(q, k, v, g, beta, scale: float, state_pool, slot_idx,
+               inter_states=None, o=None):
+    """Multi-token verify; the pool is only read.  Returns (o [B,Tv,H,V],
+    inter_states [B,Tv,H,K,V])."""
+    B, Tv, H, K = q.shape
+    V = v.shape[3]
+    dev = q.device
+    io = _io_dtype(q)
+    n_slots = state_pool.shape[0]
+    _need(k, "k", q.dtype, (B, Tv, H, K), dev)
+    _need(v, "v", q.dtype, (B, Tv, H, V), dev)
+    _need(g, "g", torch.float32, (B, Tv, H, K), dev)
+    _need(beta, "beta", torch.float32, (B, Tv, H), dev)
+    _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    if inter_states is None:
+        inter_states = torch.empty((B, Tv, H, K, V), dtype=torch.float32, device=dev)
+    _need(inter_states, "inter_states", torch.float32, (B, Tv, H, K, V), dev)
+    o = torch.empty((B, Tv, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (B, Tv, H, V), dev)
+    _check("kda_verify", lib().kda_verify(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+        _ptr(state_pool), n_slots, _ptr(slot_idx), B, Tv, H, K, V,
+        _ptr(inter_states), _ptr(o), _stream(dev)))
+    return o, inter_states

@@ -1,0 +1,124 @@
+// C ABI of libkda (declared in include/kda.h): argument validation, status
+// codes, and dispatch to the kernel launchers.  Nothing here allocates,
+// synchronises or keeps state; every launch goes to the caller's stream.
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+bool head_dim_ok(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned8(const void* p) { return ((uintptr_t)p & 7u) == 0; }
+
+// io tensors whose rows are read as 4-element groups need 8-byte alignment
+// (bf16) or 16-byte alignment (fp32).
+bool io_aligned(kda_dtype io, const void* p) {
+  return io == KDA_BF16 ? aligned8(p) : aligned16(p);
+}
+
+kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARGUMENT: return "KDA_ERR_INVALID_ARGUMENT";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+kda_status kda_gate_prep(const float* a, const float* b, const float* A_log,
+                         const float* dt_bias, int64_t T, int32_t H, int32_t K,
+                         float lower_bound, float* g, float* beta, void* stream) {
+  if (T < 0 || H < 1 || !(lower_bound <= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K)) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)T * (uint64_t)H >= (1ull << 32)) return KDA_ERR_UNSUPPORTED;
+  if (T == 0) return KDA_OK;
+  if (!a || !b || !A_log || !g || !beta) return KDA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(a) || !aligned16(g) || (dt_bias && !aligned16(dt_bias)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  kda::GateArgs p{a, b, A_log, dt_bias, T, H, K, lower_bound, g, beta};
+  return launch_status(kda::run_gate(p, (hipStream_t)stream));
+}
+
+size_t kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
+                                        int32_t K, int32_t V, int32_t chunk) {
+  if (T < 0 || N < 1 || H < 1 || !head_dim_ok(K) || K != V) return 0;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
+  return kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
+}
+
+kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             const int32_t* cu_seqlens, int32_t N, int64_t T,
+                             int32_t H, int32_t K, int32_t V, int32_t chunk,
+                             float scale, const float* h0, float* ht, void* o,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)T * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!io_aligned(io, q) || !io_aligned(io, k) || !io_aligned(io, v) ||
+                !io_aligned(io, o) || !aligned16(g)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t need = kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return KDA_ERR_WORKSPACE;
+  kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
+                     chunk, scale, h0, ht, o, workspace, workspace_bytes};
+  return launch_status(kda::run_prefill(p, (hipStream_t)stream));
+}
+
+kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g,
+                                const float* beta, float scale,
+                                float* state_pool, int64_t n_slots,
+                                const int32_t* slot_idx, int32_t B, int32_t H,
+                                int32_t K, int32_t V, void* o, void* stream) {
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !state_pool || !slot_idx || !o)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!io_aligned(io, v) || !io_aligned(io, o) || !aligned16(state_pool))
+    return KDA_ERR_INVALID_ARGUMENT;
+  kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
+                    B, 1, H, K, V, nullptr, o};
+  return launch_status(kda::run_decode(p, (hipStream_t)stream));
+}
+
+kda_status kda_verify(kda_dtype io, const void* q, const void* k,
+                      const void* v, const float* g, const float* beta,
+                      float scale, const float* state_pool, int64_t n_slots,
+                      const int32_t* slot_idx, int32_t B, int32_t Tv,
+                      int32_t H, int32_t K, int32_t V, float* inter_states,
+                      void* o, void* stream) {
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (B < 1 || Tv < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !state_pool || !slot_idx || !inter_states || !o)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!io_aligned(io, v) || !io_aligned(io, o) || !aligned16(state_pool) ||
+      !aligned16(inter_states))
+    return KDA_ERR_INVALID_ARGUMENT;
+  kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale,
+                    const_cast<float*>(state_pool), slot_idx, B, Tv, H, K, V,
+                    inter_states, o};
+  return launch_status(kda::run_verify(p, (hipStream_t)stream));
+}
+
+}  // extern "C"

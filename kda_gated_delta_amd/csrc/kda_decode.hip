@@ -1,0 +1,288 @@
+// Recurrent decode and multi-token verify of the KDA gated delta rule.
+//
+// One workgroup per (request, head).  The head's K x V fp32 state is held in
+// registers: thread t owns the float4 column group cg = t % (V/4) of the rows
+// rg, rg + RG, rg + 2 RG, ... (rg = t / (V/4)), so each wave reads and writes
+// whole 512-byte state rows with 128-bit accesses and the state crosses HBM
+// exactly once in each direction.  The reductions over K (k.S', q.S' and
+// q.k) are a butterfly inside the wave plus one LDS exchange across waves.
+//
+// Per token ("Linear attention" tutorial, sections "Gated DeltaNet" and
+// "KDA：逐通道的遗忘门"):  S' = Diag(exp g) S;  v_hat = k S';
+//   d = beta (v - v_hat);  S = S' + k^T d;  o = scale q S = scale (q S' + (q.k) d)
+// The last identity is the decode read-out of the ReplaySSM analysis
+// (section 3.12): it avoids a second pass over the updated state.
+// A negative slot index marks a padding row (ReplaySSM analysis, section 3.6).
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+template <int K, int V>
+struct StepShape {
+  static constexpr int NT = (K * V / 4 < 256) ? K * V / 4 : 256;  // threads
+  static constexpr int CG = V / 4;     // float4 column groups per row
+  static constexpr int RG = NT / CG;   // row groups
+  static constexpr int RPT = K / RG;   // state rows per thread
+  static constexpr int NW = NT / 64;   // waves
+  static_assert(NT % 64 == 0 && RPT >= 1 && RG * RPT == K, "bad shape");
+};
+
+// Partial sums of one thread: k.S' (float4), q.S' (float4), q.k.
+struct Partials {
+  float4 vh, qs;
+  float qk;
+};
+
+// Sums the partials of the threads sharing a column group.  red is an LDS
+// buffer of NW * CG * 9 floats; the caller synchronises before reuse.
+template <int K, int V>
+__device__ __forceinline__ Partials reduce_rows(Partials p, float* red) {
+  typedef StepShape<K, V> Sh;
+  const int t = threadIdx.x;
+  p.vh.x = xor_sum(p.vh.x, Sh::CG);
+  p.vh.y = xor_sum(p.vh.y, Sh::CG);
+  p.vh.z = xor_sum(p.vh.z, Sh::CG);
+  p.vh.w = xor_sum(p.vh.w, Sh::CG);
+  p.qs.x = xor_sum(p.qs.x, Sh::CG);
+  p.qs.y = xor_sum(p.qs.y, Sh::CG);
+  p.qs.z = xor_sum(p.qs.z, Sh::CG);
+  p.qs.w = xor_sum(p.qs.w, Sh::CG);
+  p.qk = xor_sum(p.qk, Sh::CG);
+  if (Sh::NW == 1) return p;
+  const int lane = t & 63, w = t >> 6, cg = t % Sh::CG;
+  if (lane < Sh::CG) {
+    float* dst = red + (w * Sh::CG + lane) * 9;
+    dst[0] = p.vh.x; dst[1] = p.vh.y; dst[2] = p.vh.z; dst[3] = p.vh.w;
+    dst[4] = p.qs.x; dst[5] = p.qs.y; dst[6] = p.qs.z; dst[7] = p.qs.w;
+    dst[8] = p.qk;
+  }
+  __syncthreads();
+  Partials s;
+  s.vh = f4(0.f);
+  s.qs = f4(0.f);
+  s.qk = 0.f;
+#pragma unroll
+  for (int i = 0; i < Sh::NW; ++i) {
+    const float* src = red + (i * Sh::CG + cg) * 9;
+    s.vh = s.vh + make_float4(src[0], src[1], src[2], src[3]);
+    s.qs = s.qs + make_float4(src[4], src[5], src[6], src[7]);
+    s.qk += src[8];
+  }
+  return s;
+}
+
+// Register-resident slice of a head's state owned by one thread.
+template <int RPT>
+struct Rows {
+  float4 s[RPT];
+};
+
+// One token on the register-resident state.  sq/sk/sa hold q, k and exp(g)
+// of the token in LDS; on return s[] holds the updated state and o the
+// (unscaled) read-out q S of this thread's column group.
+template <int K, int V>
+__device__ __forceinline__ float4 token_step(Rows<StepShape<K, V>::RPT>& st,
+                                             const float* sq, const float* sk,
+                                             const float* sa, float4 vv,
+                                             float beta, float* red) {
+  typedef StepShape<K, V> Sh;
+  const int rg = threadIdx.x / Sh::CG;
+  float4* s = st.s;
+  Partials p;
+  p.vh = f4(0.f);
+  p.qs = f4(0.f);
+  p.qk = 0.f;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    const int row = rg + Sh::RG * i;
+    s[i] = sa[row] * s[i];
+    p.vh = fma4(sk[row], s[i], p.vh);
+    p.qs = fma4(sq[row], s[i], p.qs);
+    p.qk = fmaf(sq[row], sk[row], p.qk);
+  }
+  p = reduce_rows<K, V>(p, red);
+  const float4 d = beta * (vv - p.vh);
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = fma4(sk[rg + Sh::RG * i], d, s[i]);
+  return fma4(p.qk, d, p.qs);
+}
+
+template <typename IO, int K, int V>
+__global__ __launch_bounds__((StepShape<K, V>::NT)) void decode_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k,
+    const IO* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale, float* __restrict__ pool,
+    const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o) {
+  typedef StepShape<K, V> Sh;
+  __shared__ float sq[K], sk[K], sa[K];
+  __shared__ float red[Sh::NW * Sh::CG * 9];
+  const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int64_t rh = (int64_t)r * H + h;
+  const int64_t slot = slot_idx[r];
+  if (slot < 0) {
+    if (rg == 0) store4(o + rh * V + 4 * cg, f4(0.f));
+    return;
+  }
+  float* S = pool + (slot * H + h) * (int64_t)(K * V);
+  Rows<Sh::RPT> st;
+  float4* s = st.s;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4(S + (rg + Sh::RG * i) * V + 4 * cg);
+  for (int c = t; c < K; c += Sh::NT) {
+    sq[c] = to_f32(q[rh * K + c]);
+    sk[c] = to_f32(k[rh * K + c]);
+    sa[c] = expf(g[rh * K + c]);
+  }
+  const float4 vv = load4(v + rh * V + 4 * cg);
+  const float b = beta[rh];
+  __syncthreads();
+  const float4 oq = token_step<K, V>(st, sq, sk, sa, vv, b, red);
+  if (rg == 0) store4(o + rh * V + 4 * cg, scale * oq);
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) store4(S + (rg + Sh::RG * i) * V + 4 * cg, s[i]);
+}
+
+// Draft tokens are staged TVB at a time.
+constexpr int TVB = 8;
+
+template <typename IO, int K, int V>
+__global__ __launch_bounds__((StepShape<K, V>::NT)) void verify_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k,
+    const IO* __restrict__ v, const float* __restrict__ g,
+    const float* __restrict__ beta, float scale,
+    const float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
+    int Tv, int H, float* __restrict__ inter, IO* __restrict__ o) {
+  typedef StepShape<K, V> Sh;
+  __shared__ float sq[TVB][K], sk[TVB][K], sa[TVB][K], sb[TVB];
+  __shared__ float red[2][Sh::NW * Sh::CG * 9];
+  const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int64_t slot = slot_idx[r];
+  if (slot < 0) {
+    if (rg == 0)
+      for (int s = 0; s < Tv; ++s)
+        store4(o + (((int64_t)r * Tv + s) * H + h) * V + 4 * cg, f4(0.f));
+    return;
+  }
+  const float* S0 = pool + (slot * H + h) * (int64_t)(K * V);
+  Rows<Sh::RPT> st;
+  float4* s = st.s;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4(S0 + (rg + Sh::RG * i) * V + 4 * cg);
+  int step = 0;
+  for (int s0 = 0; s0 < Tv; s0 += TVB) {
+    const int nb = (Tv - s0 < TVB) ? Tv - s0 : TVB;
+    if (s0 > 0) __syncthreads();  // previous batch fully consumed
+    for (int e = t; e < nb * K; e += Sh::NT) {
+      const int j = e / K, c = e % K;
+      const int64_t src = (((int64_t)r * Tv + s0 + j) * H + h) * K + c;
+      sq[j][c] = to_f32(q[src]);
+      sk[j][c] = to_f32(k[src]);
+      sa[j][c] = expf(g[src]);
+    }
+    if (t < nb) sb[t] = beta[((int64_t)r * Tv + s0 + t) * H + h];
+    float4 vv[TVB];
+#pragma unroll
+    for (int j = 0; j < TVB; ++j)
+      if (j < nb) vv[j] = load4(v + (((int64_t)r * Tv + s0 + j) * H + h) * V + 4 * cg);
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < TVB; ++j) {
+      if (j < nb) {
+        const int64_t rsh = ((int64_t)r * Tv + s0 + j) * H + h;
+        const float4 oq = token_step<K, V>(st, sq[j], sk[j], sa[j], vv[j], sb[j],
+                                           red[step & 1]);
+        ++step;
+        if (rg == 0) store4(o + rsh * V + 4 * cg, scale * oq);
+        float* I = inter + rsh * (int64_t)(K * V);
+#pragma unroll
+        for (int i = 0; i < Sh::RPT; ++i) store4(I + (rg + Sh::RG * i) * V + 4 * cg, s[i]);
+      }
+    }
+  }
+}
+
+template <typename IO, int K, int V>
+hipError_t launch_decode(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float scale,
+                         float* pool, const int32_t* slot_idx, int B, int H,
+                         void* o, hipStream_t stream) {
+  typedef StepShape<K, V> Sh;
+  hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)B * H), dim3(Sh::NT),
+                     0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
+                     scale, pool, slot_idx, H, (IO*)o);
+  return hipGetLastError();
+}
+
+template <typename IO, int K, int V>
+hipError_t launch_verify(const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, float scale,
+                         const float* pool, const int32_t* slot_idx, int B,
+                         int Tv, int H, float* inter, void* o,
+                         hipStream_t stream) {
+  typedef StepShape<K, V> Sh;
+  hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)B * H), dim3(Sh::NT),
+                     0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
+                     scale, pool, slot_idx, Tv, H, inter, (IO*)o);
+  return hipGetLastError();
+}
+
+template <typename IO, int K>
+hipError_t decode_v(const DecodeArgs& a, hipStream_t st) {
+  switch (a.V) {
+    case 16: return launch_decode<IO, K, 16>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
+    case 32: return launch_decode<IO, K, 32>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
+    case 64: return launch_decode<IO, K, 64>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
+    case 128: return launch_decode<IO, K, 128>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t decode_k(const DecodeArgs& a, hipStream_t st) {
+  switch (a.K) {
+    case 16: return decode_v<IO, 16>(a, st);
+    case 32: return decode_v<IO, 32>(a, st);
+    case 64: return decode_v<IO, 64>(a, st);
+    case 128: return decode_v<IO, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO, int K>
+hipError_t verify_v(const DecodeArgs& a, hipStream_t st) {
+  switch (a.V) {
+    case 16: return launch_verify<IO, K, 16>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
+    case 32: return launch_verify<IO, K, 32>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
+    case 64: return launch_verify<IO, K, 64>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
+    case 128: return launch_verify<IO, K, 128>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t verify_k(const DecodeArgs& a, hipStream_t st) {
+  switch (a.K) {
+    case 16: return verify_v<IO, 16>(a, st);
+    case 32: return verify_v<IO, 32>(a, st);
+    case 64: return verify_v<IO, 64>(a, st);
+    case 128: return verify_v<IO, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
+  return a.bf16_io ? decode_k<bf16>(a, stream) : decode_k<float>(a, stream);
+}
+
+hipError_t run_verify(const DecodeArgs& a, hipStream_t stream) {
+  return a.bf16_io ? verify_k<bf16>(a, stream) : verify_k<float>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,53 @@
+// Internal launcher interface between the C ABI (kda_api.hip) and the kernel
+// translation units.  Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct GateArgs {
+  const float *a, *b, *A_log, *dt_bias;
+  int64_t T;
+  int H, K;
+  float lower_bound;
+  float *g, *beta;
+};
+
+struct DecodeArgs {
+  bool bf16_io;
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float scale;
+  float* pool;  // decode: in place; verify: read only
+  const int32_t* slot_idx;
+  int B, Tv, H, K, V;
+  float* inter;  // verify only
+  void* o;
+};
+
+struct PrefillArgs {
+  bool bf16_io;
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const int32_t* cu_seqlens;
+  int N;
+  int64_t T;
+  int H, K, V, C;
+  float scale;
+  const float* h0;
+  float* ht;
+  void* o;
+  void* ws;
+  size_t ws_bytes;
+};
+
+hipError_t run_gate(const GateArgs& a, hipStream_t stream);
+hipError_t run_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t run_verify(const DecodeArgs& a, hipStream_t stream);
+hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream);
+size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C);
+
+}  // namespace kda

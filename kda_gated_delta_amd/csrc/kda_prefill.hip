@@ -1,0 +1,751 @@
+// Chunkwise varlen prefill of the KDA gated delta rule.
+//
+// The recurrence ("Linear attention" tutorial, section "KDA：逐通道的遗忘门")
+//   S_t = (I - b_t k_t^T k_t) Diag(exp g_t) S_{t-1} + b_t k_t^T v_t,  o_t = scale q_t S_t
+// is evaluated a chunk of C tokens at a time (section "两种计算形态": the C
+// rank-1 updates of a chunk merge through the WY/UT representation and one
+// C x C triangular solve; only the state crosses chunk boundaries).
+//
+// Unrolling one chunk (G = inclusive chunk-local cumulative sum of g, S0 the
+// state entering the chunk, B = diag(beta)):
+//   A[t,j]  = sum_c k_t[c] k_j[c] exp(G_t[c] - G_j[c])   (j <  t)
+//   Aq[t,j] = sum_c q_t[c] k_j[c] exp(G_t[c] - G_j[c])   (j <= t)
+//   X = (I + B A)^-1 (unit lower triangular),  M = X B
+//   W = M (K * e^G),  U = M V,  D = U - W S0
+//   O = scale [ (Q * e^G) S0 + Aq D ]
+//   S_C = Diag(e^{G_C}) S0 + (K * e^{G_C - G})^T D
+// Every exponent used is <= 0 (never overflows): inside A and Aq only
+// G_t - G_j with t >= j appears; off-diagonal 16 x 16 blocks factor through
+// the first row r of the row block, exp(G_t - G_r) exp(G_r - G_j), both <= 1.
+//
+// Three kernels:
+//   plan   - one workgroup: chunk table of the packed batch from cu_seqlens
+//            (clamped into [0, T], so a malformed array cannot push an
+//            access out of bounds);
+//   intra  - one workgroup per (chunk, head), fully parallel: everything of a
+//            chunk that does not depend on the carried state (G, A, Aq, the
+//            triangular inverse, W, U, Q*e^G, K*e^{G_C-G}), written to the
+//            workspace already in MFMA fragment order;
+//   state  - one workgroup per (sequence, head, V tile), serial over the
+//            chunks of its sequence: D, O and the state update, with the
+//            state tile resident in MFMA accumulators.
+// Contractions use v_mfma_f32_16x16x32_bf16 with every fp32 operand split
+// into bf16 hi + lo parts (three products, fp32 accumulation): relative error
+// about 2^-16 per product, enough for fp32 inputs; the cumulative sums, the
+// exponentials and the triangular inverse are fp32 on the vector ALUs.
+
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int NTHREADS = 256;  // four waves per workgroup
+
+// -------------------------------------------------------------- fragments
+//
+// v_mfma_f32_16x16x32_bf16, lane l (0..63), g = l / 16, r = l % 16:
+//   A operand (16 x 32, row-major): A[r][8g + j], j = 0..7
+//   B operand (32 x 16):            B[8g + j][r]
+//   accumulator (16 x 16):          C[4g + i][r], i = 0..3
+
+struct Frag {
+  bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ Frag split8(const float (&x)[8]) {
+  Frag f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const bf16 h = (bf16)x[j];
+    f.hi[j] = h;
+    f.lo[j] = (bf16)(x[j] - (float)h);
+  }
+  return f;
+}
+
+// acc += a * b with a, b given as hi + lo (the lo * lo term is dropped).
+__device__ __forceinline__ f32x4 mma3(f32x4 acc, const Frag& a, const Frag& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  return acc;
+}
+
+// A fragment tile stored in the workspace: 64 lanes x 16 B of hi parts, then
+// 64 lanes x 16 B of lo parts (each half one coalesced 1 KB wave access).
+constexpr int FRAG_BYTES = 2048;
+
+__device__ __forceinline__ void store_frag(char* tile, const Frag& f) {
+  const int l = threadIdx.x & 63;
+  *reinterpret_cast<bf16x8*>(tile + l * 16) = f.hi;
+  *reinterpret_cast<bf16x8*>(tile + 1024 + l * 16) = f.lo;
+}
+
+__device__ __forceinline__ Frag load_frag(const char* tile) {
+  const int l = threadIdx.x & 63;
+  Frag f;
+  f.hi = *reinterpret_cast<const bf16x8*>(tile + l * 16);
+  f.lo = *reinterpret_cast<const bf16x8*>(tile + 1024 + l * 16);
+  return f;
+}
+
+// ------------------------------------------------------- workspace layout
+
+struct ChunkEntry {
+  int seq, start, len, pad;
+};
+
+template <int D, int C>
+struct Geom {
+  static constexpr int NB = C / 16;          // 16-row blocks of a chunk
+  static constexpr int KTC = (C + 31) / 32;  // 32-wide k steps over tokens
+  static constexpr int KTD = (D + 31) / 32;  // 32-wide k steps over channels
+  static constexpr int MTD = D / 16;         // 16-row tiles over channels
+  // per (chunk, head) record, in bytes
+  static constexpr size_t W_OFF = 0;                                  // [NB][KTD] A frags
+  static constexpr size_t Q_OFF = W_OFF + (size_t)NB * KTD * FRAG_BYTES;  // [NB][KTD]
+  static constexpr size_t KT_OFF = Q_OFF + (size_t)NB * KTD * FRAG_BYTES;  // [MTD][KTC]
+  static constexpr size_t AQ_OFF = KT_OFF + (size_t)MTD * KTC * FRAG_BYTES;  // [NB][KTC]
+  static constexpr size_t U_OFF = AQ_OFF + (size_t)NB * KTC * FRAG_BYTES;  // [NB][MTD] acc tiles
+  static constexpr size_t GC_OFF = U_OFF + (size_t)NB * MTD * 64 * 16;    // [D] fp32
+  static constexpr size_t REC = ((GC_OFF + D * 4) + 255) / 256 * 256;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Header of the workspace: chunk table [NCB] and per-sequence chunk offsets.
+struct WsLayout {
+  size_t table_off, off_off, rec_off;
+  int64_t ncb;
+};
+
+WsLayout ws_layout(int64_t T, int N, int C) {
+  WsLayout w;
+  w.ncb = (T + C - 1) / C + N;
+  w.table_off = 0;
+  w.off_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
+  w.rec_off = w.off_off + round256((size_t)(N + 1) * sizeof(int));
+  return w;
+}
+
+size_t rec_bytes(int D, int C) {
+#define KDA_REC(d, c) \
+  if (D == d && C == c) return Geom<d, c>::REC;
+  KDA_REC(16, 16) KDA_REC(16, 32) KDA_REC(16, 64)
+  KDA_REC(32, 16) KDA_REC(32, 32) KDA_REC(32, 64)
+  KDA_REC(64, 16) KDA_REC(64, 32) KDA_REC(64, 64)
+  KDA_REC(128, 16) KDA_REC(128, 32) KDA_REC(128, 64)
+#undef KDA_REC
+  return 0;
+}
+
+// ------------------------------------------------------------------- plan
+
+// Chunk table of the packed batch: sequence n owns chunks
+// off[n] .. off[n+1]-1; entries past the last chunk get len = 0.  Sequence
+// bounds are clamped to 0 <= lo <= hi <= T.
+__global__ __launch_bounds__(NTHREADS) void plan_kernel(
+    const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb,
+    ChunkEntry* __restrict__ table, int* __restrict__ off) {
+  __shared__ int scan[NTHREADS];
+  __shared__ int carry;
+  const int t = threadIdx.x;
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < N; base += NTHREADS) {
+    const int n = base + t;
+    int lo = 0, hi = 0, nch = 0;
+    if (n < N) {
+      const int64_t a = cu[n], b = cu[n + 1];
+      lo = (int)(a < 0 ? 0 : (a > T ? T : a));
+      hi = (int)(b < lo ? lo : (b > T ? T : b));
+      nch = (hi - lo + C - 1) / C;
+    }
+    scan[t] = nch;
+    __syncthreads();
+    for (int s = 1; s < NTHREADS; s <<= 1) {  // inclusive Hillis-Steele scan
+      const int x = t >= s ? scan[t - s] : 0;
+      __syncthreads();
+      scan[t] += x;
+      __syncthreads();
+    }
+    const int first = carry + scan[t] - nch;
+    if (n < N) {
+      off[n] = first;
+      for (int j = 0; j < nch && first + j < ncb; ++j) {
+        ChunkEntry e;
+        e.seq = n;
+        e.start = lo + j * C;
+        e.len = (hi - e.start < C) ? hi - e.start : C;
+        e.pad = 0;
+        table[first + j] = e;
+      }
+    }
+    __syncthreads();
+    if (t == NTHREADS - 1) carry += scan[t];
+    __syncthreads();
+  }
+  if (t == 0) off[N] = carry;
+  for (int64_t i = carry + t; i < ncb; i += NTHREADS) {
+    ChunkEntry e;
+    e.seq = 0;
+    e.start = 0;
+    e.len = 0;
+    e.pad = 0;
+    table[i] = e;
+  }
+}
+
+// ------------------------------------------------------------------ intra
+
+template <typename IO, int D, int C>
+struct IntraSmem {
+  static constexpr int DP = D + 4;  // fp32 row stride (16-byte aligned rows)
+  static constexpr int CP = C + 4;
+  static constexpr int DPIO = D + 16 / (int)sizeof(IO);  // io row stride
+  static constexpr size_t G_BYTES = (size_t)C * DP * 4;
+  static constexpr size_t IO_BYTES = (size_t)C * DPIO * sizeof(IO);
+  static constexpr size_t KQ_BYTES = 2 * IO_BYTES > G_BYTES ? 2 * IO_BYTES : G_BYTES;
+  static constexpr size_t CC_BYTES = (size_t)C * CP * 4;
+  static constexpr size_t TOTAL = G_BYTES + KQ_BYTES + 3 * CC_BYTES + C * 4;
+};
+
+template <typename IO, int D, int C>
+__global__ __launch_bounds__(NTHREADS) void intra_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
+    const ChunkEntry* __restrict__ table, char* __restrict__ recs) {
+  typedef Geom<D, C> Gm;
+  typedef IntraSmem<IO, D, C> Sm;
+  constexpr int DP = Sm::DP, CP = Sm::CP, DPIO = Sm::DPIO;
+  constexpr int NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD, MTD = Gm::MTD;
+  __shared__ __align__(16) char smem[Sm::TOTAL];
+  float* sG = reinterpret_cast<float*>(smem);                        // G, then K*e^G, then V
+  IO* sK = reinterpret_cast<IO*>(smem + Sm::G_BYTES);                // k
+  IO* sQ = reinterpret_cast<IO*>(smem + Sm::G_BYTES + Sm::IO_BYTES);  // q
+  float* sW = reinterpret_cast<float*>(smem + Sm::G_BYTES);          // W (over k, q)
+  float* sA = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::KQ_BYTES);
+  float* sAq = sA + C * CP;  // Aq, later scratch of the block inverse
+  float* sX = sAq + C * CP;  // (I + B A)^-1
+  float* sB = sX + C * CP;   // beta
+
+  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+  const ChunkEntry ce = table[chunk];
+  if (ce.len <= 0) return;
+  const int L = ce.len;
+  char* rec = recs + (size_t)blockIdx.x * Gm::REC;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+
+  // ---- 1. load the chunk (rows t >= L are zero), clear A, Aq and X
+  for (int e = tid; e < C * (D / 4); e += NTHREADS) {
+    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
+    float4 gg = f4(0.f), kk = f4(0.f), qq = f4(0.f);
+    if (t < L) {
+      const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
+      gg = load4(g + row);
+      kk = load4(k + row);
+      qq = load4(q + row);
+    }
+    store4(sG + t * DP + c, gg);
+    store4(sK + t * DPIO + c, kk);
+    store4(sQ + t * DPIO + c, qq);
+  }
+  // A, Aq and X start at zero: their blocks above the diagonal are read as
+  // zeros by the 32-wide k steps of the fragment loads below
+  for (int e = tid; e < 3 * C * CP; e += NTHREADS) sA[e] = 0.f;
+  if (tid < C) sB[tid] = tid < L ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
+  __syncthreads();
+
+  // ---- 2. chunk-local inclusive cumulative sum of g, per channel
+  if (tid < D) {
+    float acc = 0.f;
+    for (int t = 0; t < C; ++t) {
+      acc += sG[t * DP + tid];
+      sG[t * DP + tid] = acc;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3a. off-diagonal 16 x 16 blocks of A and Aq on the matrix cores
+  // block (I, J), J < I, factors through reference row r = 16 I.
+  for (int p = w; p < NB * (NB - 1) / 2; p += 4) {
+    int I = 1, J = p;
+    while (J >= I) { J -= I; ++I; }
+    const int r = 16 * I, ta = 16 * I + lr, jb = 16 * J + lr;
+    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KTD; ++kt) {
+      float a8[8], q8[8], b8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = 32 * kt + 8 * lg + j;
+        if (c < D) {
+          const float ea = __expf(sG[ta * DP + c] - sG[r * DP + c]);
+          a8[j] = to_f32(sK[ta * DPIO + c]) * ea;
+          q8[j] = to_f32(sQ[ta * DPIO + c]) * ea;
+          b8[j] = to_f32(sK[jb * DPIO + c]) * __expf(sG[r * DP + c] - sG[jb * DP + c]);
+        } else {
+          a8[j] = q8[j] = b8[j] = 0.f;
+        }
+      }
+      const Frag fa = split8(a8), fq = split8(q8), fb = split8(b8);
+      accA = mma3(accA, fa, fb);
+      accQ = mma3(accQ, fq, fb);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * I + 4 * lg + i, j = 16 * J + lr;
+      sA[t * CP + j] = accA[i];
+      sAq[t * CP + j] = accQ[i];
+    }
+  }
+  // ---- 3b. diagonal 16 x 16 blocks, elementwise exp(G_t - G_j)
+  {
+    constexpr int CPG = D / 16;  // channels per thread
+    const int tl = tid >> 4, cgp = tid & 15;
+    for (int I = 0; I < NB; ++I) {
+      const int t = 16 * I + tl;
+      float kt_[CPG], qt_[CPG], gt_[CPG];
+#pragma unroll
+      for (int c = 0; c < CPG; ++c) {
+        const int cc = cgp * CPG + c;
+        kt_[c] = to_f32(sK[t * DPIO + cc]);
+        qt_[c] = to_f32(sQ[t * DPIO + cc]);
+        gt_[c] = sG[t * DP + cc];
+      }
+      for (int jl = 0; jl < 16; ++jl) {
+        const int j = 16 * I + jl;
+        float pa = 0.f, pq = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) {
+          const int cc = cgp * CPG + c;
+          const float kj = to_f32(sK[j * DPIO + cc]);
+          const float x = gt_[c] - sG[j * DP + cc];
+          const float e = __expf(jl <= tl ? x : 0.f);  // j > t: unused, kept finite
+          pa = fmaf(kt_[c] * kj, e, pa);
+          pq = fmaf(qt_[c] * kj, e, pq);
+        }
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) {
+          pa += __shfl_xor(pa, m, 64);
+          pq += __shfl_xor(pq, m, 64);
+        }
+        if (cgp == 0) {
+          if (jl < tl) sA[t * CP + j] = pa;
+          if (jl <= tl) sAq[t * CP + j] = pq;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 4. state-independent operands of the state pass
+  // (scale Q e^G) as A fragments [NB][KTD]
+  for (int tile = w; tile < NB * KTD; tile += 4) {
+    const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 32 * kt + 8 * lg + j;
+      x[j] = c < D ? scale * to_f32(sQ[t * DPIO + c]) * __expf(sG[t * DP + c]) : 0.f;
+    }
+    store_frag(rec + Gm::Q_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+  }
+  // (K e^{G_C - G})^T as A fragments [MTD][KTC]: rows = channels
+  for (int tile = w; tile < MTD * KTC; tile += 4) {
+    const int mt = tile / KTC, kt = tile % KTC, c = 16 * mt + lr;
+    const float glast = sG[(C - 1) * DP + c];
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int t = 32 * kt + 8 * lg + j;
+      x[j] = t < C ? to_f32(sK[t * DPIO + c]) * __expf(glast - sG[t * DP + c]) : 0.f;
+    }
+    store_frag(rec + Gm::KT_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+  }
+  // scale Aq as A fragments [NB][KTC]
+  for (int tile = w; tile < NB * KTC; tile += 4) {
+    const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int jj = 32 * kt + 8 * lg + j;
+      x[j] = jj < C ? scale * sAq[t * CP + jj] : 0.f;
+    }
+    store_frag(rec + Gm::AQ_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+  }
+  if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[(C - 1) * DP + tid]);
+
+  // ---- 5. X = (I + B A)^-1, B A strictly lower: 16 x 16 diagonal blocks by
+  // forward substitution (one lane per column), then block rows.
+  if (w < NB && lr == l) {  // lanes 0..15 of wave w: block w, column lr
+    const int b0 = 16 * w;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float acc = (r == lr) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) acc = fmaf(-sB[b0 + r] * sA[(b0 + r) * CP + b0 + m], x[m], acc);
+      x[r] = acc;
+      sX[(b0 + r) * CP + b0 + lr] = acc;
+    }
+  }
+  __syncthreads();
+  {
+    const int rr = tid >> 4, cc = tid & 15;
+    float* sY = sAq;  // Aq is in the workspace already
+    for (int I = 1; I < NB; ++I) {
+      for (int J = 0; J < I; ++J) {  // Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ}
+        float acc = 0.f;
+        for (int m = 16 * J; m < 16 * I; ++m)
+          acc = fmaf(sB[16 * I + rr] * sA[(16 * I + rr) * CP + m], sX[m * CP + 16 * J + cc], acc);
+        sY[(16 * J + rr) * 16 + cc] = acc;
+      }
+      __syncthreads();
+      for (int J = 0; J < I; ++J) {  // X_IJ = -X_II Y_J
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+          acc = fmaf(sX[(16 * I + rr) * CP + 16 * I + m], sY[(16 * J + m) * 16 + cc], acc);
+        sX[(16 * I + rr) * CP + 16 * J + cc] = -acc;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 6. K e^G in place of G (G no longer needed)
+  for (int e = tid; e < C * D; e += NTHREADS) {
+    const int t = e / D, c = e % D;
+    sG[t * DP + c] = to_f32(sK[t * DPIO + c]) * __expf(sG[t * DP + c]);
+  }
+  __syncthreads();
+
+  // ---- 7. W = (X B) (K e^G) into LDS (over k and q)
+  for (int tile = w; tile < NB * MTD; tile += 4) {
+    const int mt = tile / MTD, nt = tile % MTD;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KTC; ++kt) {
+      if (32 * kt > 16 * mt + 15) break;  // X is lower triangular
+      float a8[8], b8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = 32 * kt + 8 * lg + j;
+        a8[j] = jj < C ? sX[(16 * mt + lr) * CP + jj] * sB[jj] : 0.f;
+        b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
+      }
+      acc = mma3(acc, split8(a8), split8(b8));
+    }
+    // k and q are dead since step 6, so W may overwrite them
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * DP + 16 * nt + lr] = acc[i];
+  }
+  __syncthreads();
+
+  // ---- 8. W fragments out; V in place of K e^G
+  for (int tile = w; tile < NB * KTD; tile += 4) {
+    const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int c = 32 * kt + 8 * lg + j;
+      x[j] = c < D ? sW[t * DP + c] : 0.f;
+    }
+    store_frag(rec + Gm::W_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+  }
+  for (int e = tid; e < C * (D / 4); e += NTHREADS) {
+    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
+    float4 vv = f4(0.f);
+    if (t < L) vv = load4(v + ((int64_t)(ce.start + t) * H + h) * D + c);
+    store4(sG + t * DP + c, vv);
+  }
+  __syncthreads();
+
+  // ---- 9. U = (X B) V, stored as accumulator tiles [NB][MTD]
+  for (int tile = w; tile < NB * MTD; tile += 4) {
+    const int mt = tile / MTD, nt = tile % MTD;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < KTC; ++kt) {
+      if (32 * kt > 16 * mt + 15) break;
+      float a8[8], b8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = 32 * kt + 8 * lg + j;
+        a8[j] = jj < C ? sX[(16 * mt + lr) * CP + jj] * sB[jj] : 0.f;
+        b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
+      }
+      acc = mma3(acc, split8(a8), split8(b8));
+    }
+    *reinterpret_cast<f32x4*>(rec + Gm::U_OFF + ((size_t)tile * 64 + l) * 16) = acc;
+  }
+}
+
+// ------------------------------------------------------------------ state
+
+template <int D, int C, int VT>
+struct StateSmem {
+  static constexpr int SK = (D < 32 ? 32 : D) + 8;        // S^T row: channels (+pad)
+  static constexpr int DK = Geom<D, C>::KTC * 32 + 8;     // D^T row: tokens (+pad)
+  static constexpr size_t S_BYTES = (size_t)VT * SK * 2;  // one bf16 plane
+  static constexpr size_t D_BYTES = (size_t)VT * DK * 2;
+  static constexpr size_t TOTAL = 2 * S_BYTES + 2 * D_BYTES;
+};
+
+template <typename IO, int D, int C, int VT>
+__global__ __launch_bounds__(NTHREADS) void state_kernel(
+    const ChunkEntry* __restrict__ table, const int* __restrict__ off,
+    const char* __restrict__ recs, int N, int H, const float* __restrict__ h0,
+    float* __restrict__ ht, IO* __restrict__ o) {
+  typedef Geom<D, C> Gm;
+  typedef StateSmem<D, C, VT> Sm;
+  constexpr int NV = D / VT, NTV = VT / 16, NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD;
+  constexpr int MTD = Gm::MTD;
+  constexpr int MS_PER_WAVE = (MTD + 3) / 4;  // state row tiles per wave
+  constexpr int SK = Sm::SK, DK = Sm::DK;
+  __shared__ __align__(16) char smem[Sm::TOTAL];
+  bf16* sSh = reinterpret_cast<bf16*>(smem);
+  bf16* sSl = reinterpret_cast<bf16*>(smem + Sm::S_BYTES);
+  bf16* sDh = reinterpret_cast<bf16*>(smem + 2 * Sm::S_BYTES);
+  bf16* sDl = reinterpret_cast<bf16*>(smem + 2 * Sm::S_BYTES + Sm::D_BYTES);
+
+  // XCD-aware unit mapping: the NV tiles of one (sequence, head) get block
+  // ids congruent mod 8, i.e. the same XCD and L2.
+  const int b = blockIdx.x;
+  const int vt = (b / 8) % NV;
+  const int u = (b / (8 * NV)) * 8 + (b % 8);
+  if (u >= N * H) return;
+  const int n = u / H, h = u % H;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+
+  // zero the LDS padding once (k positions beyond D or C stay zero)
+  for (int e = tid; e < (int)(Sm::TOTAL / 4); e += NTHREADS) reinterpret_cast<int*>(smem)[e] = 0;
+
+  // state tiles owned by this wave: ms = w + 4 i, all NTV column tiles
+  f32x4 S[MS_PER_WAVE][NTV];
+#pragma unroll
+  for (int i = 0; i < MS_PER_WAVE; ++i) {
+    const int ms = w + 4 * i;
+#pragma unroll
+    for (int nt = 0; nt < NTV; ++nt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        float x = 0.f;
+        if (h0 != nullptr && ms < MTD)
+          x = h0[(((int64_t)n * H + h) * D + 16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr];
+        S[i][nt][e] = x;
+      }
+    }
+  }
+  __syncthreads();
+
+  const int c_first = off[n], c_last = off[n + 1];
+  for (int ch = c_first; ch < c_last; ++ch) {
+    const ChunkEntry ce = table[ch];
+    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
+
+    // -- 1. S^T (hi, lo) into LDS
+#pragma unroll
+    for (int i = 0; i < MS_PER_WAVE; ++i) {
+      const int ms = w + 4 * i;
+      if (ms < MTD) {
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) {
+          bf16x4v hi, lo;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16 hh = (bf16)S[i][nt][e];
+            hi[e] = hh;
+            lo[e] = (bf16)(S[i][nt][e] - (float)hh);
+          }
+          const int at = (16 * nt + lr) * SK + 16 * ms + 4 * lg;
+          *reinterpret_cast<bf16x4v*>(sSh + at) = hi;
+          *reinterpret_cast<bf16x4v*>(sSl + at) = lo;
+        }
+      }
+    }
+    __syncthreads();
+
+    // -- 2./3. per 16-token row tile mt = w: P = W S, Qs = (Q e^G) S, D = U - P
+    f32x4 Qs[NTV];
+    const bool has_mt = w < NB;
+    const int mt = w;
+    if (has_mt) {
+      f32x4 P[NTV];
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        P[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Qs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt) {
+        const Frag fw = load_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
+        const Frag fq = load_frag(rec + Gm::Q_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) {
+          Frag fs;
+          const int at = (16 * nt + lr) * SK + 32 * kt + 8 * lg;
+          fs.hi = *reinterpret_cast<const bf16x8*>(sSh + at);
+          fs.lo = *reinterpret_cast<const bf16x8*>(sSl + at);
+          P[nt] = mma3(P[nt], fw, fs);
+          Qs[nt] = mma3(Qs[nt], fq, fs);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        const f32x4 U = *reinterpret_cast<const f32x4*>(
+            rec + Gm::U_OFF + (((size_t)mt * MTD + vt * NTV + nt) * 64 + l) * 16);
+        bf16x4v hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d = U[e] - P[nt][e];
+          const bf16 hh = (bf16)d;
+          hi[e] = hh;
+          lo[e] = (bf16)(d - (float)hh);
+        }
+        const int at = (16 * nt + lr) * DK + 16 * mt + 4 * lg;
+        *reinterpret_cast<bf16x4v*>(sDh + at) = hi;
+        *reinterpret_cast<bf16x4v*>(sDl + at) = lo;
+      }
+    }
+    __syncthreads();
+
+    // -- 4. O = Qs + (scale Aq) D for row tile mt, written to o
+    if (has_mt) {
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt) {
+        if (32 * kt > 16 * mt + 15) break;  // Aq is lower triangular
+        const Frag fa = load_frag(rec + Gm::AQ_OFF + (size_t)(mt * KTC + kt) * FRAG_BYTES);
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) {
+          Frag fd;
+          const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
+          fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
+          fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
+          Qs[nt] = mma3(Qs[nt], fa, fd);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = 16 * mt + 4 * lg + e;
+          if (t < ce.len)
+            o[((int64_t)(ce.start + t) * H + h) * D + vt * VT + 16 * nt + lr] =
+                from_f32<IO>(Qs[nt][e]);
+        }
+      }
+    }
+
+    // -- 5. S = Diag(e^{G_C}) S + (K e^{G_C - G})^T D
+    const float* gC = reinterpret_cast<const float*>(rec + Gm::GC_OFF);
+#pragma unroll
+    for (int i = 0; i < MS_PER_WAVE; ++i) {
+      const int ms = w + 4 * i;
+      if (ms < MTD) {
+        const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ms + 4 * lg);
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[i][nt][e] *= gc[e];
+#pragma unroll
+        for (int kt = 0; kt < KTC; ++kt) {
+          const Frag fk = load_frag(rec + Gm::KT_OFF + (size_t)(ms * KTC + kt) * FRAG_BYTES);
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt) {
+            Frag fd;
+            const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
+            fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
+            fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
+            S[i][nt] = mma3(S[i][nt], fk, fd);
+          }
+        }
+      }
+    }
+  }
+
+  if (ht != nullptr) {
+#pragma unroll
+    for (int i = 0; i < MS_PER_WAVE; ++i) {
+      const int ms = w + 4 * i;
+      if (ms < MTD) {
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            ht[(((int64_t)n * H + h) * D + 16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr] =
+                S[i][nt][e];
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- launch
+
+template <int D>
+constexpr int state_vt() { return D >= 32 ? 32 : 16; }
+
+template <typename IO, int D, int C>
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  typedef Geom<D, C> Gm;
+  constexpr int VT = state_vt<D>();
+  constexpr int NV = D / VT;
+  const WsLayout ws = ws_layout(a.T, a.N, C);
+  char* base = reinterpret_cast<char*>(a.ws);
+  ChunkEntry* table = reinterpret_cast<ChunkEntry*>(base + ws.table_off);
+  int* off = reinterpret_cast<int*>(base + ws.off_off);
+  char* recs = base + ws.rec_off;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
+                     C, ws.ncb, table, off);
+  if (a.T > 0)
+    hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
+                       dim3(NTHREADS), 0, st, (const IO*)a.q, (const IO*)a.k,
+                       (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs);
+  const int units = a.N * a.H;
+  const int groups = (units + 7) / 8;
+  hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
+                     dim3(NTHREADS), 0, st, table, off, recs, a.N, a.H, a.h0, a.ht,
+                     (IO*)a.o);
+  (void)sizeof(Gm);
+  return hipGetLastError();
+}
+
+template <typename IO, int D>
+hipError_t prefill_c(const PrefillArgs& a, hipStream_t st) {
+  switch (a.C) {
+    case 16: return launch_prefill<IO, D, 16>(a, st);
+    case 32: return launch_prefill<IO, D, 32>(a, st);
+    case 64: return launch_prefill<IO, D, 64>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t prefill_d(const PrefillArgs& a, hipStream_t st) {
+  switch (a.K) {
+    case 16: return prefill_c<IO, 16>(a, st);
+    case 32: return prefill_c<IO, 32>(a, st);
+    case 64: return prefill_c<IO, 64>(a, st);
+    case 128: return prefill_c<IO, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C) {
+  (void)V;
+  const WsLayout ws = ws_layout(T, N, C);
+  return ws.rec_off + (size_t)ws.ncb * H * rec_bytes(K, C);
+}
+
+hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream) {
+  return a.bf16_io ? prefill_d<bf16>(a, stream) : prefill_d<float>(a, stream);
+}
+
+}  // namespace kda

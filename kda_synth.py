@@ -115,3 +115,25 @@ def orthonormal_keys(n: int, K: int, seed: int) -> np.ndarray:
     assert n <= K
     qm, _ = np.linalg.qr(rng(seed).standard_normal((K, K)))
     return np.ascontiguousarray(qm[:, :n].T)
+
+
+# Named workloads (shapes and draw parameters); the seed of workload i is i.
+WORKLOADS = {
+    # B=1, T=64, H=2, K=V=16, fp32, chunk 16, dt_bias = 0, zero initial state
+    "tiny_f32_prefill": dict(kind="prefill", seqlens=[64], H=2, K=16, V=16, io="f32",
+                             chunk=16, dt_bias_std=0.0, h0_std=None, seed=0),
+    # 4 sequences {512, 1024, 2048, 4096} packed, H=32, K=V=128, bf16, chunk 64
+    "varlen_prefill_7680": dict(kind="prefill", seqlens=[512, 1024, 2048, 4096], H=32,
+                                K=128, V=128, io="bf16", chunk=64, dt_bias_std=0.5,
+                                h0_std=0.02, seed=1),
+    # 256 single-token requests on a 512-slot fp32 pool, H=32, K=V=128, bf16
+    "decode_256": dict(kind="decode", B=256, H=32, K=128, V=128, n_slots=512,
+                       io="bf16", dt_bias_std=0.5, state_std=0.02, seed=2),
+    # one 65536-token sequence, H=32, K=V=128, bf16, run as 16 x 4096 carried
+    "long_prefill_65536": dict(kind="prefill", seqlens=[65536], H=32, K=128, V=128,
+                               io="bf16", chunk=64, dt_bias_std=0.5, h0_std=0.02,
+                               seed=3, segments=16),
+    # 64 requests x 8 draft tokens on a 128-slot pool, H=32, K=V=128, bf16
+    "verify_64x8": dict(kind="verify", B=64, Tv=8, H=32, K=128, V=128, n_slots=128,
+                        io="bf16", dt_bias_std=0.5, state_std=0.02, seed=4),
+}

@@ -1,0 +1,117 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every entry point that include/kda.h
+declares, and argument validation must turn every bad call into a status code
+before anything reaches the HIP runtime.  Only calls that fail validation (or
+that have nothing to enqueue) are made here.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kda_gated_delta_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, LAUNCH, WORKSPACE = 0, 1, 2, 3, 4
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert set(declared) == set(kda.EXPORTED), declared
+    L = kda.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    assert kda.status_string(OK) == "KDA_OK"
+    assert kda.status_string(INVALID) == "KDA_ERR_INVALID_ARGUMENT"
+    assert kda.status_string(UNSUPPORTED) == "KDA_ERR_UNSUPPORTED"
+    assert kda.status_string(LAUNCH) == "KDA_ERR_LAUNCH"
+    assert kda.status_string(WORKSPACE) == "KDA_ERR_WORKSPACE"
+    assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
+
+
+P = ctypes.c_void_p(4096)  # aligned, never dereferenced: calls below fail validation
+P_MIS = ctypes.c_void_p(4096 + 4)
+
+
+def test_gate_prep_validation():
+    L = kda.lib()
+    # T = 0: nothing to enqueue
+    assert L.kda_gate_prep(None, None, None, None, 0, 2, 16, 0.0, None, None, None) == OK
+    assert L.kda_gate_prep(P, P, P, None, 4, 2, 16, 0.0, None, P, None) == INVALID
+    assert L.kda_gate_prep(P, P, P, None, 4, 2, 24, 0.0, P, P, None) == UNSUPPORTED
+    assert L.kda_gate_prep(P, P, P, None, -1, 2, 16, 0.0, P, P, None) == INVALID
+    assert L.kda_gate_prep(P, P, P, None, 4, 0, 16, 0.0, P, P, None) == INVALID
+    assert L.kda_gate_prep(P, P, P, None, 4, 2, 16, 0.5, P, P, None) == INVALID
+    assert L.kda_gate_prep(P_MIS, P, P, None, 4, 2, 16, 0.0, P, P, None) == INVALID
+
+
+def test_decode_validation():
+    L = kda.lib()
+    args = lambda **kw: [kw.get("io", 1), P, P, P, P, P, 1.0, kw.get("pool", P),
+                         kw.get("n_slots", 8), P, kw.get("B", 2), 4, kw.get("K", 128),
+                         kw.get("V", 128), kw.get("o", P), None]
+    assert L.kda_recurrent_decode(*args(io=7)) == UNSUPPORTED
+    assert L.kda_recurrent_decode(*args(B=0)) == INVALID
+    assert L.kda_recurrent_decode(*args(n_slots=0)) == INVALID
+    assert L.kda_recurrent_decode(*args(K=48)) == UNSUPPORTED
+    assert L.kda_recurrent_decode(*args(V=256)) == UNSUPPORTED
+    assert L.kda_recurrent_decode(*args(o=None)) == INVALID
+    assert L.kda_recurrent_decode(*args(pool=P_MIS)) == INVALID
+
+
+def test_verify_validation():
+    L = kda.lib()
+    args = lambda **kw: [kw.get("io", 1), P, P, P, P, P, 1.0, P, 8, P, 2,
+                         kw.get("Tv", 4), 4, 128, 128, kw.get("inter", P), P, None]
+    assert L.kda_verify(*args(Tv=0)) == INVALID
+    assert L.kda_verify(*args(inter=None)) == INVALID
+    assert L.kda_verify(*args(inter=P_MIS)) == INVALID
+    assert L.kda_verify(*args(io=2)) == UNSUPPORTED
+
+
+def test_prefill_validation_and_workspace():
+    L = kda.lib()
+    ws = kda.kda_chunk_prefill_workspace_size(7680, 4, 32, 128, 128, 64)
+    assert ws > 0 and ws % 256 == 0
+    # monotone in T and N
+    assert kda.kda_chunk_prefill_workspace_size(7681, 4, 32, 128, 128, 64) >= ws
+    assert kda.kda_chunk_prefill_workspace_size(7680, 5, 32, 128, 128, 64) >= ws
+    assert kda.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 16, 48) == 0
+    assert kda.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 32, 16) == 0
+
+    def call(**kw):
+        return L.kda_chunk_prefill(
+            kw.get("io", 1), P, P, P, P, P, kw.get("cu", P), kw.get("N", 4),
+            kw.get("T", 7680), 32, kw.get("K", 128), kw.get("V", 128),
+            kw.get("chunk", 64), 1.0, None, P, P, kw.get("ws", P),
+            kw.get("ws_bytes", ws), None)
+    assert call(chunk=48) == UNSUPPORTED
+    assert call(K=64, V=128) == UNSUPPORTED
+    assert call(N=0) == INVALID
+    assert call(cu=None) == INVALID
+    assert call(ws=None) == WORKSPACE
+    assert call(ws_bytes=ws - 1) == WORKSPACE
+    assert call(ws=ctypes.c_void_p(4096 + 64)) == WORKSPACE  # not 256-aligned
+
+
+def test_binding_rejects_cpu_and_wrong_dtypes():
+    import torch
+    q = torch.zeros(2, 4, 16)
+    with pytest.raises(TypeError):
+        kda.kda_recurrent_decode(q.to(torch.float16), q, q, q, q[..., 0], 1.0,
+                                 torch.zeros(4, 4, 16, 16), torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError):
+        kda.kda_gate_prep(torch.zeros(3, 2, 16), torch.zeros(3, 3), torch.zeros(2))

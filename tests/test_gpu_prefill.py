@@ -1,0 +1,202 @@
+"""GPU parity of the chunkwise varlen prefill against the fp64 oracle.
+
+The HIP path runs through the C ABI (thin binding); the oracle runs the
+token-by-token recurrence on the same seeded inputs and on the same fp32
+gates.  Besides the workloads' own gate distribution every shape is also run
+in a slow-decay regime (A_log = 0, dt_bias = -8): with the workloads' gates
+the state carried between chunks and the initial state decay below e^-38
+within one chunk, so only slow decay makes those paths visible.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_gated_delta_amd as kda
+import kda_synth
+import oracle
+from kda_testutil import TOL, TORCH_IO, assert_io_output, dev, gates_f32, host, rel_err_blocks
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(c, g=None, beta=None):
+    if g is None:
+        g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    io = TORCH_IO[c["io"]]
+    t = dict(q=dev(c["q"], io), k=dev(c["k"], io), v=dev(c["v"], io), g=dev(g),
+             beta=dev(beta), cu=dev(c["cu"], torch.int32),
+             h0=None if c["h0"] is None else dev(c["h0"]))
+    return t, g, beta
+
+
+def _check(c, chunk, heads=None, g=None, beta=None, scale=None):
+    """Runs prefill on the GPU and compares o and ht with the oracle (all
+    heads, or the listed ones)."""
+    t, g, beta = _inputs(c, g, beta)
+    K = c["K"]
+    scale = K ** -0.5 if scale is None else scale
+    o, ht = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                  scale, h0=t["h0"], chunk=chunk)
+    torch.cuda.synchronize()
+    o, ht = host(o), host(ht)
+    hs = slice(None) if heads is None else heads
+    sub = lambda x: None if x is None else np.ascontiguousarray(x[:, hs])
+    o_ref, ht_ref = oracle.prefill(sub(c["q"]), sub(c["k"]), sub(c["v"]), sub(g),
+                                   sub(beta), c["cu"], scale, sub(c["h0"]))
+    assert_io_output(o[:, hs], o_ref, c["io"], 1)
+    err_ht = rel_err_blocks(ht[:, hs], ht_ref, 2)
+    assert err_ht <= TOL[c["io"]], err_ht
+    return o, ht
+
+
+# ------------------------------------------------------------ workloads
+
+def test_tiny_f32_workload():
+    w = kda_synth.WORKLOADS["tiny_f32_prefill"]
+    for regime in ("config", "long"):
+        c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"],
+                                   seed=w["seed"], regime=regime,
+                                   dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+        _check(c, w["chunk"])
+
+
+def test_tiny_f32_zero_gate():
+    """g = 0 (no decay) everywhere: the longest memory the recurrence has."""
+    w = kda_synth.WORKLOADS["tiny_f32_prefill"]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"], seed=5,
+                               h0_std=0.5)
+    _, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    _check(c, w["chunk"], g=np.zeros_like(c["a"]), beta=beta)
+
+
+@pytest.mark.parametrize("regime", ["config", "long"])
+def test_varlen_workload(regime):
+    w = kda_synth.WORKLOADS["varlen_prefill_7680"]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"],
+                               seed=w["seed"], regime=regime,
+                               dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+    _check(c, w["chunk"])
+
+
+def test_long_workload_segments_vs_full_vs_oracle():
+    """65536 tokens: 16 carried segments of 4096 equal one full run, and
+    both equal the oracle (sampled heads)."""
+    w = kda_synth.WORKLOADS["long_prefill_65536"]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"],
+                               seed=w["seed"], regime="long",
+                               dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+    t, g, beta = _inputs(c)
+    T, scale = c["T"], w["K"] ** -0.5
+    o_full, ht_full = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                            t["cu"], scale, h0=t["h0"], chunk=w["chunk"])
+    seg = T // w["segments"]
+    state = t["h0"].clone()
+    o_seg = torch.empty_like(o_full)
+    cu1 = torch.tensor([0, seg], dtype=torch.int32, device="cuda")
+    for s in range(w["segments"]):
+        sl = slice(s * seg, (s + 1) * seg)
+        o_s, _ = kda.kda_chunk_prefill(t["q"][sl], t["k"][sl], t["v"][sl], t["g"][sl],
+                                       t["beta"][sl], cu1, scale, h0=state, ht=state,
+                                       chunk=w["chunk"])  # in place: ht aliases h0
+        o_seg[sl] = o_s
+    torch.cuda.synchronize()
+    # the segment boundaries coincide with chunk boundaries: identical arithmetic
+    assert torch.equal(o_seg, o_full)
+    assert torch.equal(state, ht_full)
+    heads = [0, 13, 31]
+    sub = lambda x: np.ascontiguousarray(x[:, heads])
+    o_ref, ht_ref = oracle.prefill(sub(c["q"]), sub(c["k"]), sub(c["v"]), sub(g),
+                                   sub(beta), c["cu"], scale, sub(c["h0"]))
+    assert_io_output(host(o_full)[:, heads], o_ref, "bf16", 1)
+    assert rel_err_blocks(host(ht_full)[:, heads], ht_ref, 2) <= TOL["bf16"]
+
+
+# ---------------------------------------------------------- shapes, edges
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("D", [16, 32, 64, 128])
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_head_dims_and_chunk_sizes(io, D, chunk):
+    c = kda_synth.prefill_case([5, 17, 1, 41, 100], 3, D, D, io, seed=D + chunk,
+                               regime="long")
+    _check(c, chunk)
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 65, 128, 1024])
+def test_single_sequence_lengths(T):
+    for io in ("f32", "bf16"):
+        c = kda_synth.prefill_case([T], 2, 128, 128, io, seed=T, regime="long")
+        _check(c, 64)
+
+
+@pytest.mark.parametrize("seqlens", [[32, 32, 32, 32], [5, 17, 1, 41], [128],
+                                     [0, 70, 0, 3, 0]])
+def test_varlen_edges_with_and_without_h0(seqlens):
+    for h0_std in (None, 0.3):
+        c = kda_synth.prefill_case(seqlens, 4, 64, 64, "bf16", seed=len(seqlens),
+                                   regime="long", h0_std=h0_std)
+        _, ht = _check(c, 32)
+        for n, L in enumerate(seqlens):
+            if L == 0:  # an empty sequence hands its initial state through
+                exp = np.zeros_like(ht[n]) if c["h0"] is None else c["h0"][n]
+                np.testing.assert_array_equal(ht[n], exp)
+
+
+def test_result_does_not_depend_on_chunk_size():
+    c = kda_synth.prefill_case([300, 77], 2, 128, 128, "f32", seed=9, regime="long")
+    t, g, beta = _inputs(c)
+    outs = [kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                  0.1, h0=t["h0"], chunk=C) for C in (16, 32, 64)]
+    torch.cuda.synchronize()
+    for o, ht in outs[1:]:
+        assert rel_err_blocks(host(o), host(outs[0][0]), 1) <= 5e-5
+        assert rel_err_blocks(host(ht), host(outs[0][1]), 2) <= 5e-5
+
+
+def test_no_final_state_and_empty_batch():
+    c = kda_synth.prefill_case([40, 9], 2, 32, 32, "bf16", seed=3)
+    t, g, beta = _inputs(c)
+    o, ht = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                  0.2, h0=t["h0"], output_final_state=False, chunk=16)
+    assert ht is None
+    o_ref, _ = oracle.prefill(c["q"], c["k"], c["v"], g, beta, c["cu"], 0.2, c["h0"])
+    torch.cuda.synchronize()
+    assert_io_output(host(o), o_ref, "bf16", 1)
+    # T = 0: only ht = h0 is written
+    z = lambda *s: torch.zeros(*s, device="cuda")
+    cu0 = torch.zeros(3, dtype=torch.int32, device="cuda")
+    h0 = torch.randn(2, 2, 32, 32, device="cuda")
+    o0, ht0 = kda.kda_chunk_prefill(z(0, 2, 32).bfloat16(), z(0, 2, 32).bfloat16(),
+                                    z(0, 2, 32).bfloat16(), z(0, 2, 32), z(0, 2), cu0,
+                                    0.2, h0=h0, chunk=16)
+    torch.cuda.synchronize()
+    assert o0.shape == (0, 2, 32) and torch.equal(ht0, h0)
+
+
+def test_prefill_then_decodes_equals_longer_prefill():
+    """prefill(seq[:T]) vs prefill(seq[:T-8]) followed by 8 decode steps."""
+    c = kda_synth.prefill_case([200], 4, 128, 128, "bf16", seed=12, regime="long")
+    t, g, beta = _inputs(c)
+    T, kk, scale = 200, 8, 128 ** -0.5
+    o_full, ht_full = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                            t["cu"], scale, h0=t["h0"])
+    cu = torch.tensor([0, T - kk], dtype=torch.int32, device="cuda")
+    pre = slice(0, T - kk)
+    o_pre, ht_pre = kda.kda_chunk_prefill(t["q"][pre], t["k"][pre], t["v"][pre],
+                                          t["g"][pre], t["beta"][pre], cu, scale,
+                                          h0=t["h0"])
+    pool = torch.cat([torch.zeros_like(ht_pre), ht_pre])  # slot 1
+    idx = torch.ones(1, dtype=torch.int32, device="cuda")
+    o_dec = []
+    for i in range(T - kk, T):
+        o_dec.append(kda.kda_recurrent_decode(t["q"][i:i + 1], t["k"][i:i + 1],
+                                              t["v"][i:i + 1], t["g"][i:i + 1],
+                                              t["beta"][i:i + 1], scale, pool, idx))
+    torch.cuda.synchronize()
+    o_dec = host(torch.cat(o_dec))
+    # both routes are checked against the oracle, and against each other
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, c["cu"], scale, c["h0"])
+    assert_io_output(o_dec, o_ref[T - kk:], "bf16", 1)
+    assert rel_err_blocks(host(pool[1:]), ht_ref, 2) <= TOL["bf16"]
+    assert rel_err_blocks(host(pool[1:]), host(ht_full), 2) <= TOL["bf16"]
+    np.testing.assert_array_equal(host(o_pre), host(o_full[pre]))
