@@ -215,13 +215,16 @@ struct IntraSmem {
   static constexpr size_t TOTAL = G_BYTES + KQ_BYTES + 3 * CC_BYTES + C * 4;
 };
 
+constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
+
 template <typename IO, int D, int C>
-__global__ __launch_bounds__(NTHREADS) void intra_kernel(
+__global__ __launch_bounds__(NT_INTRA) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
     const ChunkEntry* __restrict__ table, char* __restrict__ recs) {
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
+  constexpr int NT = NT_INTRA, NW = NT / 64;
   constexpr int DP = Sm::DP, CP = Sm::CP, DPIO = Sm::DPIO;
   constexpr int NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD, MTD = Gm::MTD;
   __shared__ __align__(16) char smem[Sm::TOTAL];
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
 
   // ---- 1. load the chunk (rows t >= L are zero), clear A, Aq and X
-  for (int e = tid; e < C * (D / 4); e += NTHREADS) {
+  for (int e = tid; e < C * (D / 4); e += NT) {
     const int t = e / (D / 4), c = (e % (D / 4)) * 4;
     float4 gg = f4(0.f), kk = f4(0.f), qq = f4(0.f);
     if (t < L) {
@@ -257,23 +260,39 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
   }
   // A, Aq and X start at zero: their blocks above the diagonal are read as
   // zeros by the 32-wide k steps of the fragment loads below
-  for (int e = tid; e < 3 * C * CP; e += NTHREADS) sA[e] = 0.f;
+  for (int e = tid; e < 3 * C * CP; e += NT) sA[e] = 0.f;
   if (tid < C) sB[tid] = tid < L ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
   __syncthreads();
 
-  // ---- 2. chunk-local inclusive cumulative sum of g, per channel
-  if (tid < D) {
-    float acc = 0.f;
-    for (int t = 0; t < C; ++t) {
-      acc += sG[t * DP + tid];
-      sG[t * DP + tid] = acc;
+  // ---- 2. chunk-local inclusive cumulative sum of g, per channel, in NSEG
+  // row segments scanned in parallel and then offset
+  {
+    constexpr int NSEG = (NT / D < C / 4) ? NT / D : C / 4;
+    constexpr int RPS = C / NSEG;
+    const int c = tid % D, seg = tid / D;
+    if (seg < NSEG) {
+      float acc = 0.f;
+#pragma unroll
+      for (int r = 0; r < RPS; ++r) {
+        acc += sG[(seg * RPS + r) * DP + c];
+        sG[(seg * RPS + r) * DP + c] = acc;
+      }
+    }
+    __syncthreads();
+    float offs = 0.f;
+    if (seg < NSEG)
+      for (int s2 = 0; s2 < seg; ++s2) offs += sG[(s2 * RPS + RPS - 1) * DP + c];
+    __syncthreads();
+    if (seg < NSEG && seg > 0) {
+#pragma unroll
+      for (int r = 0; r < RPS; ++r) sG[(seg * RPS + r) * DP + c] += offs;
     }
   }
   __syncthreads();
 
   // ---- 3a. off-diagonal 16 x 16 blocks of A and Aq on the matrix cores
   // block (I, J), J < I, factors through reference row r = 16 I.
-  for (int p = w; p < NB * (NB - 1) / 2; p += 4) {
+  for (int p = w; p < NB * (NB - 1) / 2; p += NW) {
     int I = 1, J = p;
     while (J >= I) { J -= I; ++I; }
     const int r = 16 * I, ta = 16 * I + lr, jb = 16 * J + lr;
@@ -285,10 +304,11 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
       for (int j = 0; j < 8; ++j) {
         const int c = 32 * kt + 8 * lg + j;
         if (c < D) {
-          const float ea = __expf(sG[ta * DP + c] - sG[r * DP + c]);
+          const float gr = sG[r * DP + c];
+          const float ea = __expf(sG[ta * DP + c] - gr);
           a8[j] = to_f32(sK[ta * DPIO + c]) * ea;
           q8[j] = to_f32(sQ[ta * DPIO + c]) * ea;
-          b8[j] = to_f32(sK[jb * DPIO + c]) * __expf(sG[r * DP + c] - sG[jb * DP + c]);
+          b8[j] = to_f32(sK[jb * DPIO + c]) * __expf(gr - sG[jb * DP + c]);
         } else {
           a8[j] = q8[j] = b8[j] = 0.f;
         }
@@ -304,26 +324,28 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
       sAq[t * CP + j] = accQ[i];
     }
   }
-  // ---- 3b. diagonal 16 x 16 blocks, elementwise exp(G_t - G_j)
+  // ---- 3b. diagonal 16 x 16 blocks, elementwise exp(G_t - G_j) for j <= t;
+  // two blocks at a time, 16 lanes per row with interleaved channels
   {
     constexpr int CPG = D / 16;  // channels per thread
-    const int tl = tid >> 4, cgp = tid & 15;
-    for (int I = 0; I < NB; ++I) {
+    const int blk = tid >> 8, lt = tid & 255, tl = lt >> 4, cgp = lt & 15;
+    const int tl_max = 4 * ((lt >> 6) & 3) + 3;  // last row of this wave
+    for (int I = blk; I < NB; I += 2) {
       const int t = 16 * I + tl;
       float kt_[CPG], qt_[CPG], gt_[CPG];
 #pragma unroll
       for (int c = 0; c < CPG; ++c) {
-        const int cc = cgp * CPG + c;
+        const int cc = c * 16 + cgp;
         kt_[c] = to_f32(sK[t * DPIO + cc]);
         qt_[c] = to_f32(sQ[t * DPIO + cc]);
         gt_[c] = sG[t * DP + cc];
       }
-      for (int jl = 0; jl < 16; ++jl) {
+      for (int jl = 0; jl <= tl_max; ++jl) {
         const int j = 16 * I + jl;
         float pa = 0.f, pq = 0.f;
 #pragma unroll
         for (int c = 0; c < CPG; ++c) {
-          const int cc = cgp * CPG + c;
+          const int cc = c * 16 + cgp;
           const float kj = to_f32(sK[j * DPIO + cc]);
           const float x = gt_[c] - sG[j * DP + cc];
           const float e = __expf(jl <= tl ? x : 0.f);  // j > t: unused, kept finite
@@ -346,7 +368,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
 
   // ---- 4. state-independent operands of the state pass
   // (scale Q e^G) as A fragments [NB][KTD]
-  for (int tile = w; tile < NB * KTD; tile += 4) {
+  for (int tile = w; tile < NB * KTD; tile += NW) {
     const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
     store_frag(rec + Gm::Q_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
   // (K e^{G_C - G})^T as A fragments [MTD][KTC]: rows = channels
-  for (int tile = w; tile < MTD * KTC; tile += 4) {
+  for (int tile = w; tile < MTD * KTC; tile += NW) {
     const int mt = tile / KTC, kt = tile % KTC, c = 16 * mt + lr;
     const float glast = sG[(C - 1) * DP + c];
     float x[8];
@@ -369,7 +391,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
     store_frag(rec + Gm::KT_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
   // scale Aq as A fragments [NB][KTC]
-  for (int tile = w; tile < NB * KTC; tile += 4) {
+  for (int tile = w; tile < NB * KTC; tile += NW) {
     const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
@@ -383,50 +405,61 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
 
   // ---- 5. X = (I + B A)^-1, B A strictly lower: 16 x 16 diagonal blocks by
   // forward substitution (one lane per column), then block rows.
-  if (w < NB && lr == l) {  // lanes 0..15 of wave w: block w, column lr
+  if (w < NB && l < 16) {  // lanes 0..15 of wave w: block w, column l
     const int b0 = 16 * w;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float acc = (r == lr) ? 1.f : 0.f;
+      float acc = (r == l) ? 1.f : 0.f;
+      const float br = sB[b0 + r];
 #pragma unroll
-      for (int m = 0; m < r; ++m) acc = fmaf(-sB[b0 + r] * sA[(b0 + r) * CP + b0 + m], x[m], acc);
+      for (int m = 0; m < r; ++m) acc = fmaf(-br * sA[(b0 + r) * CP + b0 + m], x[m], acc);
       x[r] = acc;
-      sX[(b0 + r) * CP + b0 + lr] = acc;
     }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[(b0 + r) * CP + b0 + l] = x[r];
   }
   __syncthreads();
   {
-    const int rr = tid >> 4, cc = tid & 15;
+    const int rr = (tid >> 4) & 15, cc = tid & 15, half = tid >> 8;
     float* sY = sAq;  // Aq is in the workspace already
+#pragma unroll
     for (int I = 1; I < NB; ++I) {
+#pragma unroll
       for (int J = 0; J < I; ++J) {  // Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ}
-        float acc = 0.f;
-        for (int m = 16 * J; m < 16 * I; ++m)
-          acc = fmaf(sB[16 * I + rr] * sA[(16 * I + rr) * CP + m], sX[m * CP + 16 * J + cc], acc);
-        sY[(16 * J + rr) * 16 + cc] = acc;
+        if ((J & 1) == half) {
+          const float br = sB[16 * I + rr];
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 16 * J; m < 16 * I; ++m)
+            acc = fmaf(sA[(16 * I + rr) * CP + m], sX[m * CP + 16 * J + cc], acc);
+          sY[(16 * J + rr) * 16 + cc] = br * acc;
+        }
       }
       __syncthreads();
-      for (int J = 0; J < I; ++J) {  // X_IJ = -X_II Y_J
-        float acc = 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m)
-          acc = fmaf(sX[(16 * I + rr) * CP + 16 * I + m], sY[(16 * J + m) * 16 + cc], acc);
-        sX[(16 * I + rr) * CP + 16 * J + cc] = -acc;
+      for (int J = 0; J < I; ++J) {  // X_IJ = -X_II Y_J
+        if ((J & 1) == half) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < 16; ++m)
+            acc = fmaf(sX[(16 * I + rr) * CP + 16 * I + m], sY[(16 * J + m) * 16 + cc], acc);
+          sX[(16 * I + rr) * CP + 16 * J + cc] = -acc;
+        }
       }
       __syncthreads();
     }
   }
 
   // ---- 6. K e^G in place of G (G no longer needed)
-  for (int e = tid; e < C * D; e += NTHREADS) {
+  for (int e = tid; e < C * D; e += NT) {
     const int t = e / D, c = e % D;
     sG[t * DP + c] = to_f32(sK[t * DPIO + c]) * __expf(sG[t * DP + c]);
   }
   __syncthreads();
 
-  // ---- 7. W = (X B) (K e^G) into LDS (over k and q)
-  for (int tile = w; tile < NB * MTD; tile += 4) {
+  // ---- 7. W = (X B) (K e^G) into LDS (over k and q, dead since step 6)
+  for (int tile = w; tile < NB * MTD; tile += NW) {
     const int mt = tile / MTD, nt = tile % MTD;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -441,14 +474,13 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
       }
       acc = mma3(acc, split8(a8), split8(b8));
     }
-    // k and q are dead since step 6, so W may overwrite them
 #pragma unroll
     for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * DP + 16 * nt + lr] = acc[i];
   }
   __syncthreads();
 
   // ---- 8. W fragments out; V in place of K e^G
-  for (int tile = w; tile < NB * KTD; tile += 4) {
+  for (int tile = w; tile < NB * KTD; tile += NW) {
     const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
@@ -458,7 +490,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
     }
     store_frag(rec + Gm::W_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
-  for (int e = tid; e < C * (D / 4); e += NTHREADS) {
+  for (int e = tid; e < C * (D / 4); e += NT) {
     const int t = e / (D / 4), c = (e % (D / 4)) * 4;
     float4 vv = f4(0.f);
     if (t < L) vv = load4(v + ((int64_t)(ce.start + t) * H + h) * D + c);
@@ -467,7 +499,7 @@ __global__ __launch_bounds__(NTHREADS) void intra_kernel(
   __syncthreads();
 
   // ---- 9. U = (X B) V, stored as accumulator tiles [NB][MTD]
-  for (int tile = w; tile < NB * MTD; tile += 4) {
+  for (int tile = w; tile < NB * MTD; tile += NW) {
     const int mt = tile / MTD, nt = tile % MTD;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -497,6 +529,22 @@ struct StateSmem {
   static constexpr size_t TOTAL = 2 * S_BYTES + 2 * D_BYTES;
 };
 
+// Per-wave operands of one chunk that the state pass reads from the workspace.
+// They are fetched a phase ahead of their use: W and Q e^G of chunk i+1
+// while chunk i finishes its output and state update; U, Aq, K e^{G_C-G} and
+// e^{G_C} of chunk i while its W S products run.
+template <int D, int C, int VT>
+struct StateOps {
+  typedef Geom<D, C> Gm;
+  static constexpr int NTV = VT / 16, KTC = Gm::KTC, KTD = Gm::KTD;
+  static constexpr int MS = (Gm::MTD + 3) / 4;  // state row tiles per wave
+  Frag w[KTD], q[KTD];     // row tile mt = wave of W and scale Q e^G
+  f32x4 u[NTV];            // U tiles of this V tile
+  Frag aq[KTC];            // scale Aq, row tile mt
+  Frag kt[MS][KTC];        // (K e^{G_C-G})^T, row tiles ms = wave + 4 i
+  f32x4 gc[MS];            // e^{G_C} of the rows of those tiles
+};
+
 template <typename IO, int D, int C, int VT>
 __global__ __launch_bounds__(NTHREADS) void state_kernel(
     const ChunkEntry* __restrict__ table, const int* __restrict__ off,
@@ -504,9 +552,9 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
     float* __restrict__ ht, IO* __restrict__ o) {
   typedef Geom<D, C> Gm;
   typedef StateSmem<D, C, VT> Sm;
+  typedef StateOps<D, C, VT> Ops;
   constexpr int NV = D / VT, NTV = VT / 16, NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD;
-  constexpr int MTD = Gm::MTD;
-  constexpr int MS_PER_WAVE = (MTD + 3) / 4;  // state row tiles per wave
+  constexpr int MTD = Gm::MTD, MS = Ops::MS;
   constexpr int SK = Sm::SK, DK = Sm::DK;
   __shared__ __align__(16) char smem[Sm::TOTAL];
   bf16* sSh = reinterpret_cast<bf16*>(smem);
@@ -522,14 +570,16 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
   if (u >= N * H) return;
   const int n = u / H, h = u % H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+  const bool has_mt = w < NB;
+  const int mt = w;
 
   // zero the LDS padding once (k positions beyond D or C stay zero)
   for (int e = tid; e < (int)(Sm::TOTAL / 4); e += NTHREADS) reinterpret_cast<int*>(smem)[e] = 0;
 
   // state tiles owned by this wave: ms = w + 4 i, all NTV column tiles
-  f32x4 S[MS_PER_WAVE][NTV];
+  f32x4 S[MS][NTV];
 #pragma unroll
-  for (int i = 0; i < MS_PER_WAVE; ++i) {
+  for (int i = 0; i < MS; ++i) {
     const int ms = w + 4 * i;
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) {
@@ -542,16 +592,53 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
       }
     }
   }
-  __syncthreads();
 
   const int c_first = off[n], c_last = off[n + 1];
+  Ops ops;
+  auto load_wq = [&](int ch) {
+    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
+    if (has_mt) {
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt) {
+        ops.w[kt] = load_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
+        ops.q[kt] = load_frag(rec + Gm::Q_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
+      }
+    }
+  };
+  auto load_rest = [&](int ch) {
+    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
+    if (has_mt) {
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt)
+        ops.u[nt] = *reinterpret_cast<const f32x4*>(
+            rec + Gm::U_OFF + (((size_t)mt * MTD + vt * NTV + nt) * 64 + l) * 16);
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt)
+        if (32 * kt <= 16 * mt + 15)
+          ops.aq[kt] = load_frag(rec + Gm::AQ_OFF + (size_t)(mt * KTC + kt) * FRAG_BYTES);
+    }
+    const float* gC = reinterpret_cast<const float*>(rec + Gm::GC_OFF);
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int ms = w + 4 * i;
+      if (ms < MTD) {
+        ops.gc[i] = *reinterpret_cast<const f32x4*>(gC + 16 * ms + 4 * lg);
+#pragma unroll
+        for (int kt = 0; kt < KTC; ++kt)
+          ops.kt[i][kt] = load_frag(rec + Gm::KT_OFF + (size_t)(ms * KTC + kt) * FRAG_BYTES);
+      }
+    }
+  };
+  if (c_first < c_last) load_wq(c_first);
+  __syncthreads();
+
   for (int ch = c_first; ch < c_last; ++ch) {
     const ChunkEntry ce = table[ch];
-    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
+    load_rest(ch);
 
     // -- 1. S^T (hi, lo) into LDS
 #pragma unroll
-    for (int i = 0; i < MS_PER_WAVE; ++i) {
+    for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
       if (ms < MTD) {
 #pragma unroll
@@ -571,10 +658,8 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
     }
     __syncthreads();
 
-    // -- 2./3. per 16-token row tile mt = w: P = W S, Qs = (Q e^G) S, D = U - P
+    // -- 2./3. row tile mt = w: P = W S, Qs = (Q e^G) S, D = U - P
     f32x4 Qs[NTV];
-    const bool has_mt = w < NB;
-    const int mt = w;
     if (has_mt) {
       f32x4 P[NTV];
 #pragma unroll
@@ -584,26 +669,22 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
       }
 #pragma unroll
       for (int kt = 0; kt < KTD; ++kt) {
-        const Frag fw = load_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
-        const Frag fq = load_frag(rec + Gm::Q_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           Frag fs;
           const int at = (16 * nt + lr) * SK + 32 * kt + 8 * lg;
           fs.hi = *reinterpret_cast<const bf16x8*>(sSh + at);
           fs.lo = *reinterpret_cast<const bf16x8*>(sSl + at);
-          P[nt] = mma3(P[nt], fw, fs);
-          Qs[nt] = mma3(Qs[nt], fq, fs);
+          P[nt] = mma3(P[nt], ops.w[kt], fs);
+          Qs[nt] = mma3(Qs[nt], ops.q[kt], fs);
         }
       }
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) {
-        const f32x4 U = *reinterpret_cast<const f32x4*>(
-            rec + Gm::U_OFF + (((size_t)mt * MTD + vt * NTV + nt) * 64 + l) * 16);
         bf16x4v hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float d = U[e] - P[nt][e];
+          const float d = ops.u[nt][e] - P[nt][e];
           const bf16 hh = (bf16)d;
           hi[e] = hh;
           lo[e] = (bf16)(d - (float)hh);
@@ -613,6 +694,8 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
         *reinterpret_cast<bf16x4v*>(sDl + at) = lo;
       }
     }
+    // W and Q e^G of this chunk are consumed: fetch the next chunk's
+    if (ch + 1 < c_last) load_wq(ch + 1);
     __syncthreads();
 
     // -- 4. O = Qs + (scale Aq) D for row tile mt, written to o
@@ -620,14 +703,13 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
 #pragma unroll
       for (int kt = 0; kt < KTC; ++kt) {
         if (32 * kt > 16 * mt + 15) break;  // Aq is lower triangular
-        const Frag fa = load_frag(rec + Gm::AQ_OFF + (size_t)(mt * KTC + kt) * FRAG_BYTES);
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           Frag fd;
           const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
           fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
           fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
-          Qs[nt] = mma3(Qs[nt], fa, fd);
+          Qs[nt] = mma3(Qs[nt], ops.aq[kt], fd);
         }
       }
 #pragma unroll
@@ -643,26 +725,23 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
     }
 
     // -- 5. S = Diag(e^{G_C}) S + (K e^{G_C - G})^T D
-    const float* gC = reinterpret_cast<const float*>(rec + Gm::GC_OFF);
 #pragma unroll
-    for (int i = 0; i < MS_PER_WAVE; ++i) {
+    for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
       if (ms < MTD) {
-        const f32x4 gc = *reinterpret_cast<const f32x4*>(gC + 16 * ms + 4 * lg);
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) S[i][nt][e] *= gc[e];
+          for (int e = 0; e < 4; ++e) S[i][nt][e] *= ops.gc[i][e];
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt) {
-          const Frag fk = load_frag(rec + Gm::KT_OFF + (size_t)(ms * KTC + kt) * FRAG_BYTES);
 #pragma unroll
           for (int nt = 0; nt < NTV; ++nt) {
             Frag fd;
             const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
             fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
             fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
-            S[i][nt] = mma3(S[i][nt], fk, fd);
+            S[i][nt] = mma3(S[i][nt], ops.kt[i][kt], fd);
           }
         }
       }
@@ -671,7 +750,7 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
 
   if (ht != nullptr) {
 #pragma unroll
-    for (int i = 0; i < MS_PER_WAVE; ++i) {
+    for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
       if (ms < MTD) {
 #pragma unroll
@@ -704,7 +783,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                      C, ws.ncb, table, off);
   if (a.T > 0)
     hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
-                       dim3(NTHREADS), 0, st, (const IO*)a.q, (const IO*)a.k,
+                       dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
                        (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs);
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
