@@ -94,6 +94,19 @@ __device__ __forceinline__ Frag load_frag(const char* tile) {
   return f;
 }
 
+// Eight consecutive values (16-byte aligned) from LDS as fp32.
+__device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void lds8(const bf16* p, float (&x)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+}
+
 // ------------------------------------------------------- workspace layout
 
 struct ChunkEntry {
@@ -208,17 +221,29 @@ struct IntraSmem {
   static constexpr int DP = D + 4;  // fp32 row stride (16-byte aligned rows)
   static constexpr int CP = C + 4;
   static constexpr int DPIO = D + 16 / (int)sizeof(IO);  // io row stride
-  static constexpr size_t G_BYTES = (size_t)C * DP * 4;
-  static constexpr size_t IO_BYTES = (size_t)C * DPIO * sizeof(IO);
-  static constexpr size_t KQ_BYTES = 2 * IO_BYTES > G_BYTES ? 2 * IO_BYTES : G_BYTES;
-  static constexpr size_t CC_BYTES = (size_t)C * CP * 4;
-  static constexpr size_t TOTAL = G_BYTES + KQ_BYTES + 3 * CC_BYTES + C * 4;
+  static constexpr int NB = C / 16, KTC = (C + 31) / 32;
+  static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
+  static constexpr size_t G_BYTES = (size_t)C * DP * 4;                 // G / K e^G / V
+  static constexpr size_t K_BYTES = cmax(cmax((size_t)C * DPIO * sizeof(IO),  // k, then
+                                              (size_t)NB * KTC * FRAG_BYTES),  // M frags,
+                                         (size_t)3 * 256 * 4);                 // solve scratch
+  static constexpr size_t AA_BYTES = cmax((size_t)C * CP * 4,      // A^T | Aq, then X
+                                          (size_t)32 * DP * 4);    // W staging (32 rows)
+  static constexpr size_t TOTAL = G_BYTES + K_BYTES + AA_BYTES + C * 4;
 };
 
 constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
 
+// LDS use (bf16 io, C = 64, D = 128: 68.9 KB, two workgroups per CU):
+//   sG  [C][D+4] fp32   G (cumsum of g), then K e^G, then V
+//   sK  [C][D+8] io     k; then the block-inverse scratch; then the split
+//                       fragments of M = X diag(beta)
+//   sAA [C][C+4] fp32   A transposed in the strict upper triangle and Aq in
+//                       the lower one; Aq's triangle is then reused for X;
+//                       finally 32-row staging of W
+// q is not staged: its rows are read from global memory in fragment form.
 template <typename IO, int D, int C>
-__global__ __launch_bounds__(NT_INTRA) void intra_kernel(
+__global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
     const ChunkEntry* __restrict__ table, char* __restrict__ recs) {
@@ -228,14 +253,13 @@ __global__ __launch_bounds__(NT_INTRA) void intra_kernel(
   constexpr int DP = Sm::DP, CP = Sm::CP, DPIO = Sm::DPIO;
   constexpr int NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD, MTD = Gm::MTD;
   __shared__ __align__(16) char smem[Sm::TOTAL];
-  float* sG = reinterpret_cast<float*>(smem);                        // G, then K*e^G, then V
-  IO* sK = reinterpret_cast<IO*>(smem + Sm::G_BYTES);                // k
-  IO* sQ = reinterpret_cast<IO*>(smem + Sm::G_BYTES + Sm::IO_BYTES);  // q
-  float* sW = reinterpret_cast<float*>(smem + Sm::G_BYTES);          // W (over k, q)
-  float* sA = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::KQ_BYTES);
-  float* sAq = sA + C * CP;  // Aq, later scratch of the block inverse
-  float* sX = sAq + C * CP;  // (I + B A)^-1
-  float* sB = sX + C * CP;   // beta
+  float* sG = reinterpret_cast<float*>(smem);
+  IO* sK = reinterpret_cast<IO*>(smem + Sm::G_BYTES);
+  float* sY = reinterpret_cast<float*>(smem + Sm::G_BYTES);     // over k (solve)
+  bf16x8* sMf = reinterpret_cast<bf16x8*>(smem + Sm::G_BYTES);  // over k (W, U)
+  float* sAA = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES);
+  float* sW = sAA;  // W staging, over A / Aq / X
+  float* sB = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES + Sm::AA_BYTES);
 
   const int chunk = blockIdx.x / H, h = blockIdx.x % H;
   const ChunkEntry ce = table[chunk];
@@ -243,24 +267,42 @@ __global__ __launch_bounds__(NT_INTRA) void intra_kernel(
   const int L = ce.len;
   char* rec = recs + (size_t)blockIdx.x * Gm::REC;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+  // row t of q (8 io elements from channel c) straight from global memory
+  auto qrow8 = [&](int t, int c, float (&x)[8]) {
+    if (t < L && c < D) {
+      const IO* src = q + ((int64_t)(ce.start + t) * H + h) * D + c;
+      const float4 lo4 = load4(src), hi4 = load4(src + 4);
+      x[0] = lo4.x; x[1] = lo4.y; x[2] = lo4.z; x[3] = lo4.w;
+      x[4] = hi4.x; x[5] = hi4.y; x[6] = hi4.z; x[7] = hi4.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+  };
 
-  // ---- 1. load the chunk (rows t >= L are zero), clear A, Aq and X
+  // v is only needed in step 9: fetch it now into registers
+  constexpr int VPT = (C * (D / 4) + NT - 1) / NT;  // float4 groups per thread
+  float4 vreg[VPT];
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+    vreg[i] = (e < C * (D / 4) && t < L) ? load4(v + ((int64_t)(ce.start + t) * H + h) * D + c)
+                                          : f4(0.f);
+  }
+
+  // ---- 1. load g and k (rows t >= L are zero); clear A / Aq
   for (int e = tid; e < C * (D / 4); e += NT) {
     const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-    float4 gg = f4(0.f), kk = f4(0.f), qq = f4(0.f);
+    float4 gg = f4(0.f), kk = f4(0.f);
     if (t < L) {
       const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
       gg = load4(g + row);
       kk = load4(k + row);
-      qq = load4(q + row);
     }
     store4(sG + t * DP + c, gg);
     store4(sK + t * DPIO + c, kk);
-    store4(sQ + t * DPIO + c, qq);
   }
-  // A, Aq and X start at zero: their blocks above the diagonal are read as
-  // zeros by the 32-wide k steps of the fragment loads below
-  for (int e = tid; e < 3 * C * CP; e += NT) sA[e] = 0.f;
+  for (int e = tid; e < C * CP; e += NT) sAA[e] = 0.f;
   if (tid < C) sB[tid] = tid < L ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
   __syncthreads();
 
@@ -290,77 +332,159 @@ __global__ __launch_bounds__(NT_INTRA) void intra_kernel(
   }
   __syncthreads();
 
-  // ---- 3a. off-diagonal 16 x 16 blocks of A and Aq on the matrix cores
-  // block (I, J), J < I, factors through reference row r = 16 I.
-  for (int p = w; p < NB * (NB - 1) / 2; p += NW) {
-    int I = 1, J = p;
-    while (J >= I) { J -= I; ++I; }
-    const int r = 16 * I, ta = 16 * I + lr, jb = 16 * J + lr;
-    f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+  // ---- 3. A (strictly lower, from k; stored transposed) and Aq (lower, from
+  // q) on the matrix cores, as work units (product P: 0 = A, 1 = Aq; row
+  // block I; column block J <= I).  For row t of block I:
+  //  - J < I: exp(G_t - G_j) = exp(G_t - G_r) exp(G_r - G_j) through the
+  //    block's first row r, both factors <= 1;
+  //  - J = I: pairs in different 4-token sub-blocks factor through the first
+  //    token r' of t's sub-block.  That is three products (rows of sub-block
+  //    s = 1..3 against columns before r') accumulated into one tile; rows of
+  //    other sub-blocks and columns at or past r' contribute zero.
+  // Pairs inside one 4-token sub-block (and the diagonal of Aq) follow
+  // elementwise.  Wave w takes the diagonal unit (P, I) = (w / 4, w % 4) and
+  // off-diagonal units w, w + 8, ...
+  {
+    Frag zero;
 #pragma unroll
-    for (int kt = 0; kt < KTD; ++kt) {
-      float a8[8], q8[8], b8[8];
+    for (int j = 0; j < 8; ++j) zero.hi[j] = zero.lo[j] = (bf16)0.f;
+    // row operand x_t[c] exp(G_t[c] - G_ref[c]) for the 8 channels of lane lg
+    auto row8 = [&](int P, int t, int kt, int ref, float (&o8)[8]) {
+      const int c0 = 32 * kt + 8 * lg;
+      if (c0 < D) {
+        float x8[8], gt[8], gr[8];
+        if (P == 0) lds8(sK + t * DPIO + c0, x8); else qrow8(t, c0, x8);
+        lds8(sG + t * DP + c0, gt);
+        lds8(sG + ref * DP + c0, gr);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int c = 32 * kt + 8 * lg + j;
-        if (c < D) {
-          const float gr = sG[r * DP + c];
-          const float ea = __expf(sG[ta * DP + c] - gr);
-          a8[j] = to_f32(sK[ta * DPIO + c]) * ea;
-          q8[j] = to_f32(sQ[ta * DPIO + c]) * ea;
-          b8[j] = to_f32(sK[jb * DPIO + c]) * __expf(gr - sG[jb * DP + c]);
-        } else {
-          a8[j] = q8[j] = b8[j] = 0.f;
-        }
+        for (int j = 0; j < 8; ++j) o8[j] = x8[j] * __expf(gt[j] - gr[j]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o8[j] = 0.f;
       }
-      const Frag fa = split8(a8), fq = split8(q8), fb = split8(b8);
-      accA = mma3(accA, fa, fb);
-      accQ = mma3(accQ, fq, fb);
-    }
+    };
+    // column operand k_j[c] exp(G_ref[c] - G_j[c]) (zero when !on)
+    auto col8 = [&](int j, int kt, int ref, bool on, float (&o8)[8]) {
+      const int c0 = 32 * kt + 8 * lg;
+      if (c0 < D && on) {
+        float k8[8], gj[8], gr[8];
+        lds8(sK + j * DPIO + c0, k8);
+        lds8(sG + j * DP + c0, gj);
+        lds8(sG + ref * DP + c0, gr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = 16 * I + 4 * lg + i, j = 16 * J + lr;
-      sA[t * CP + j] = accA[i];
-      sAq[t * CP + j] = accQ[i];
+        for (int i = 0; i < 8; ++i) o8[i] = k8[i] * __expf(gr[i] - gj[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o8[i] = 0.f;
+      }
+    };
+    auto store_tile = [&](int P, int I, int J, const f32x4& acc, bool diag) {
+      if (diag && !(lg > (lr >> 2))) return;  // keep rows of a later sub-block only
+      if (P == 0)  // A[t][j] -> sAA[j][t]
+        *reinterpret_cast<f32x4*>(sAA + (16 * J + lr) * CP + 16 * I + 4 * lg) = acc;
+      else
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAA[(16 * I + 4 * lg + i) * CP + 16 * J + lr] = acc[i];
+    };
+    // diagonal unit
+    {
+      const int P = w >> 2, I = w & 3;
+      if (I < NB) {
+        const int t = 16 * I + lr, sub = lr >> 2, rs = 16 * I + 4 * sub, jr = 16 * I + lr;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KTD; ++kt) {
+          float ad[8];
+          row8(P, t, kt, rs, ad);
+          const Frag fad = split8(ad);
+#pragma unroll
+          for (int sb = 1; sb < 4; ++sb) {
+            float b8[8];
+            col8(jr, kt, 16 * I + 4 * sb, sub < sb, b8);
+            acc = mma3(acc, sub == sb ? fad : zero, split8(b8));
+          }
+        }
+        store_tile(P, I, I, acc, true);
+      }
+    }
+    // off-diagonal units: u -> (P, I, J), J < I
+    constexpr int NOFF = NB * (NB - 1) / 2;
+    for (int u = w; u < 2 * NOFF; u += NW) {
+      const int P = u / (NOFF > 0 ? NOFF : 1);
+      int I = 1, J = u % (NOFF > 0 ? NOFF : 1);
+      while (J >= I) { J -= I; ++I; }
+      const int t = 16 * I + lr, r = 16 * I, jr = 16 * J + lr;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt) {
+        float ao[8], b8[8];
+        row8(P, t, kt, r, ao);
+        col8(jr, kt, r, true, b8);
+        acc = mma3(acc, split8(ao), split8(b8));
+      }
+      store_tile(P, I, J, acc, false);
     }
   }
-  // ---- 3b. diagonal 16 x 16 blocks, elementwise exp(G_t - G_j) for j <= t;
-  // two blocks at a time, 16 lanes per row with interleaved channels
+  // ---- 3b. pairs inside one 4-token sub-block, elementwise; CG lanes per
+  // sub-block, channels interleaved across them
   {
-    constexpr int CPG = D / 16;  // channels per thread
-    const int blk = tid >> 8, lt = tid & 255, tl = lt >> 4, cgp = lt & 15;
-    const int tl_max = 4 * ((lt >> 6) & 3) + 3;  // last row of this wave
-    for (int I = blk; I < NB; I += 2) {
-      const int t = 16 * I + tl;
-      float kt_[CPG], qt_[CPG], gt_[CPG];
+    constexpr int CG = D < 32 ? D : 32, CPG = D / CG, NSB = C / 4;
+    if (tid < NSB * CG) {
+      const int sb = tid / CG, cg = tid % CG, t0 = 4 * sb;
+      float kk[4][CPG], qq[4][CPG], gg[4][CPG];
 #pragma unroll
-      for (int c = 0; c < CPG; ++c) {
-        const int cc = c * 16 + cgp;
-        kt_[c] = to_f32(sK[t * DPIO + cc]);
-        qt_[c] = to_f32(sQ[t * DPIO + cc]);
-        gt_[c] = sG[t * DP + cc];
+      for (int a2 = 0; a2 < 4; ++a2)
+#pragma unroll
+        for (int i = 0; i < CPG; ++i) {
+          const int c = i * CG + cg, t = t0 + a2;
+          kk[a2][i] = to_f32(sK[t * DPIO + c]);
+          qq[a2][i] = t < L ? to_f32(q[((int64_t)(ce.start + t) * H + h) * D + c]) : 0.f;
+          gg[a2][i] = sG[t * DP + c];
+        }
+      float pa[6], pq[6], pd[4];
+      int n = 0;
+#pragma unroll
+      for (int a2 = 1; a2 < 4; ++a2)
+#pragma unroll
+        for (int b2 = 0; b2 < a2; ++b2, ++n) {
+          float sa = 0.f, sq2 = 0.f;
+#pragma unroll
+          for (int i = 0; i < CPG; ++i) {
+            const float e = __expf(gg[a2][i] - gg[b2][i]) * kk[b2][i];
+            sa = fmaf(kk[a2][i], e, sa);
+            sq2 = fmaf(qq[a2][i], e, sq2);
+          }
+          pa[n] = sa;
+          pq[n] = sq2;
+        }
+#pragma unroll
+      for (int a2 = 0; a2 < 4; ++a2) {
+        float sd = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPG; ++i) sd = fmaf(qq[a2][i], kk[a2][i], sd);
+        pd[a2] = sd;
       }
-      for (int jl = 0; jl <= tl_max; ++jl) {
-        const int j = 16 * I + jl;
-        float pa = 0.f, pq = 0.f;
 #pragma unroll
-        for (int c = 0; c < CPG; ++c) {
-          const int cc = c * 16 + cgp;
-          const float kj = to_f32(sK[j * DPIO + cc]);
-          const float x = gt_[c] - sG[j * DP + cc];
-          const float e = __expf(jl <= tl ? x : 0.f);  // j > t: unused, kept finite
-          pa = fmaf(kt_[c] * kj, e, pa);
-          pq = fmaf(qt_[c] * kj, e, pq);
+      for (int m = 1; m < CG; m <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+          pa[i] += __shfl_xor(pa[i], m, 64);
+          pq[i] += __shfl_xor(pq[i], m, 64);
         }
 #pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-          pa += __shfl_xor(pa, m, 64);
-          pq += __shfl_xor(pq, m, 64);
-        }
-        if (cgp == 0) {
-          if (jl < tl) sA[t * CP + j] = pa;
-          if (jl <= tl) sAq[t * CP + j] = pq;
-        }
+        for (int i = 0; i < 4; ++i) pd[i] += __shfl_xor(pd[i], m, 64);
+      }
+      if (cg == 0) {
+        n = 0;
+#pragma unroll
+        for (int a2 = 1; a2 < 4; ++a2)
+#pragma unroll
+          for (int b2 = 0; b2 < a2; ++b2, ++n) {
+            sAA[(t0 + b2) * CP + t0 + a2] = pa[n];  // A transposed
+            sAA[(t0 + a2) * CP + t0 + b2] = pq[n];
+          }
+#pragma unroll
+        for (int a2 = 0; a2 < 4; ++a2) sAA[(t0 + a2) * CP + t0 + a2] = pd[a2];
       }
     }
   }
@@ -371,10 +495,11 @@ __global__ __launch_bounds__(NT_INTRA) void intra_kernel(
   for (int tile = w; tile < NB * KTD; tile += NW) {
     const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
     float x[8];
+    qrow8(t, 32 * kt + 8 * lg, x);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int c = 32 * kt + 8 * lg + j;
-      x[j] = c < D ? scale * to_f32(sQ[t * DPIO + c]) * __expf(sG[t * DP + c]) : 0.f;
+      x[j] = c < D ? scale * x[j] * __expf(sG[t * DP + c]) : 0.f;
     }
     store_frag(rec + Gm::Q_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
@@ -390,131 +515,199 @@ __global__ __launch_bounds__(NT_INTRA) void intra_kernel(
     }
     store_frag(rec + Gm::KT_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
-  // scale Aq as A fragments [NB][KTC]
+  // scale Aq as A fragments [NB][KTC] (lower triangle of sAA)
   for (int tile = w; tile < NB * KTC; tile += NW) {
     const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = 32 * kt + 8 * lg + j;
-      x[j] = jj < C ? scale * sAq[t * CP + jj] : 0.f;
+      x[j] = (jj < C && jj <= t) ? scale * sAA[t * CP + jj] : 0.f;
     }
     store_frag(rec + Gm::AQ_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
   if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[(C - 1) * DP + tid]);
+  __syncthreads();
 
-  // ---- 5. X = (I + B A)^-1, B A strictly lower: 16 x 16 diagonal blocks by
-  // forward substitution (one lane per column), then block rows.
-  if (w < NB && l < 16) {  // lanes 0..15 of wave w: block w, column l
-    const int b0 = 16 * w;
-    float x[16];
+  // ---- 5. K e^G in place of G (G no longer needed)
+  for (int e = tid; e < C * D; e += NT) {
+    const int t = e / D, c = e % D;
+    sG[t * DP + c] = to_f32(sK[t * DPIO + c]) * __expf(sG[t * DP + c]);
+  }
+
+  // ---- 6. X = (I + B A)^-1, B A strictly lower (A read transposed from the
+  // upper triangle of sAA, X written to the lower one): 16 x 16 diagonal
+  // blocks by forward substitution (one lane per column), then block rows.
+  if (w < NB) {
+    // Wave w inverts diagonal block w.  Lane (column cl = l % 16, quarter
+    // p = l / 16) holds x_r of column cl for the rows r = p + 4 i.
+    // Right-looking: once x_m is final it is broadcast from its lane, and
+    // x_r -= (B A)[r][m] x_m for r > m; A[r][m] is read from sAA[m][r].
+    const int b0 = 16 * w, cl = l & 15, p = l >> 4;
+    float x[4], bb[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float acc = (r == l) ? 1.f : 0.f;
-      const float br = sB[b0 + r];
-#pragma unroll
-      for (int m = 0; m < r; ++m) acc = fmaf(-br * sA[(b0 + r) * CP + b0 + m], x[m], acc);
-      x[r] = acc;
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (p + 4 * i == cl) ? 1.f : 0.f;
+      bb[i] = sB[b0 + p + 4 * i];
     }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sX[(b0 + r) * CP + b0 + l] = x[r];
+    for (int m = 0; m < 15; ++m) {
+      const float xm = __shfl(x[m >> 2], cl + 16 * (m & 3), 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = p + 4 * i;
+        if (r > m) x[i] = fmaf(-bb[i] * sAA[(b0 + m) * CP + b0 + r], xm, x[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = p + 4 * i;
+      if (r >= cl) sAA[(b0 + r) * CP + b0 + cl] = x[i];
+    }
   }
-  __syncthreads();
+  __syncthreads();  // also: k (step 5) is dead, its space becomes scratch
   {
     const int rr = (tid >> 4) & 15, cc = tid & 15, half = tid >> 8;
-    float* sY = sAq;  // Aq is in the workspace already
 #pragma unroll
     for (int I = 1; I < NB; ++I) {
 #pragma unroll
       for (int J = 0; J < I; ++J) {  // Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ}
         if ((J & 1) == half) {
           const float br = sB[16 * I + rr];
-          float acc = 0.f;
+          float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 16 * J; m < 16 * I; ++m)
-            acc = fmaf(sA[(16 * I + rr) * CP + m], sX[m * CP + 16 * J + cc], acc);
-          sY[(16 * J + rr) * 16 + cc] = br * acc;
+          for (int m = 16 * J; m < 16 * I; ++m) {
+            const float xm = (m >= 16 * J + cc) ? sAA[m * CP + 16 * J + cc] : 0.f;
+            acc[m & 3] = fmaf(sAA[m * CP + 16 * I + rr], xm, acc[m & 3]);
+            if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+          sY[(16 * J + rr) * 16 + cc] = br * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
       }
       __syncthreads();
 #pragma unroll
       for (int J = 0; J < I; ++J) {  // X_IJ = -X_II Y_J
         if ((J & 1) == half) {
-          float acc = 0.f;
+          float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < 16; ++m)
-            acc = fmaf(sX[(16 * I + rr) * CP + 16 * I + m], sY[(16 * J + m) * 16 + cc], acc);
-          sX[(16 * I + rr) * CP + 16 * J + cc] = -acc;
+          for (int m = 0; m < 16; ++m) {
+            const float xm = (m <= rr) ? sAA[(16 * I + rr) * CP + 16 * I + m] : 0.f;
+            acc[m & 3] = fmaf(xm, sY[(16 * J + m) * 16 + cc], acc[m & 3]);
+            if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+          }
+          sAA[(16 * I + rr) * CP + 16 * J + cc] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
       }
       __syncthreads();
     }
   }
 
-  // ---- 6. K e^G in place of G (G no longer needed)
-  for (int e = tid; e < C * D; e += NT) {
-    const int t = e / D, c = e % D;
-    sG[t * DP + c] = to_f32(sK[t * DPIO + c]) * __expf(sG[t * DP + c]);
-  }
-  __syncthreads();
-
-  // ---- 7. W = (X B) (K e^G) into LDS (over k and q, dead since step 6)
-  for (int tile = w; tile < NB * MTD; tile += NW) {
-    const int mt = tile / MTD, nt = tile % MTD;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kt = 0; kt < KTC; ++kt) {
-      if (32 * kt > 16 * mt + 15) break;  // X is lower triangular
-      float a8[8], b8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int jj = 32 * kt + 8 * lg + j;
-        a8[j] = jj < C ? sX[(16 * mt + lr) * CP + jj] * sB[jj] : 0.f;
-        b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
-      }
-      acc = mma3(acc, split8(a8), split8(b8));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sW[(16 * mt + 4 * lg + i) * DP + 16 * nt + lr] = acc[i];
-  }
-  __syncthreads();
-
-  // ---- 8. W fragments out; V in place of K e^G
-  for (int tile = w; tile < NB * KTD; tile += NW) {
-    const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
+  // ---- 7. M = X diag(beta) as split A fragments [NB][KTC] (over k), shared
+  // by all waves
+  for (int tile = w; tile < NB * KTC; tile += NW) {
+    const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int c = 32 * kt + 8 * lg + j;
-      x[j] = c < D ? sW[t * DP + c] : 0.f;
+      const int jj = 32 * kt + 8 * lg + j;
+      x[j] = (jj < C && jj <= t) ? sAA[t * CP + jj] * sB[jj] : 0.f;
     }
-    store_frag(rec + Gm::W_OFF + (size_t)tile * FRAG_BYTES, split8(x));
-  }
-  for (int e = tid; e < C * (D / 4); e += NT) {
-    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-    float4 vv = f4(0.f);
-    if (t < L) vv = load4(v + ((int64_t)(ce.start + t) * H + h) * D + c);
-    store4(sG + t * DP + c, vv);
+    const Frag f = split8(x);
+    sMf[tile * 128 + l] = f.hi;
+    sMf[tile * 128 + 64 + l] = f.lo;
   }
   __syncthreads();
 
-  // ---- 9. U = (X B) V, stored as accumulator tiles [NB][MTD]
-  for (int tile = w; tile < NB * MTD; tile += NW) {
-    const int mt = tile / MTD, nt = tile % MTD;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // ---- 8. W = M (K e^G), 32 rows at a time staged in LDS (over sAA) and
+  // written out as A fragments; a wave owns a 16-channel column tile and
+  // splits its B fragments once
+  for (int half = 0; half < (NB + 1) / 2; ++half) {
+    for (int nt = w; nt < MTD; nt += NW) {
+      Frag fb[KTC];
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt) {
+        float b8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int jj = 32 * kt + 8 * lg + j;
+          b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
+        }
+        fb[kt] = split8(b8);
+      }
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2) {
+        const int mt = 2 * half + m2;
+        if (mt < NB) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kt = 0; kt < KTC; ++kt) {
+            if (32 * kt > 16 * mt + 15) break;  // X is lower triangular
+            Frag fa;
+            fa.hi = sMf[(mt * KTC + kt) * 128 + l];
+            fa.lo = sMf[(mt * KTC + kt) * 128 + 64 + l];
+            acc = mma3(acc, fa, fb[kt]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sW[(16 * m2 + 4 * lg + i) * DP + 16 * nt + lr] = acc[i];
+        }
+      }
+    }
+    __syncthreads();
+    for (int tile = w; tile < 2 * KTD; tile += NW) {
+      const int m2 = tile / KTD, kt = tile % KTD, mt = 2 * half + m2;
+      if (mt < NB) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = 32 * kt + 8 * lg + j;
+          x[j] = c < D ? sW[(16 * m2 + lr) * DP + c] : 0.f;
+        }
+        store_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES, split8(x));
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- 9. V (fetched at the start) in place of K e^G
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+    if (e < C * (D / 4)) store4(sG + t * DP + c, vreg[i]);
+  }
+  __syncthreads();
+
+  // ---- 10. U = M V, stored as accumulator tiles [NB][MTD].  A bf16 V is
+  // exact in bf16, so its lo part is zero and that product is skipped.
+  for (int nt = w; nt < MTD; nt += NW) {
+    Frag fb[KTC];
 #pragma unroll
     for (int kt = 0; kt < KTC; ++kt) {
-      if (32 * kt > 16 * mt + 15) break;
-      float a8[8], b8[8];
+      float b8[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int jj = 32 * kt + 8 * lg + j;
-        a8[j] = jj < C ? sX[(16 * mt + lr) * CP + jj] * sB[jj] : 0.f;
         b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
       }
-      acc = mma3(acc, split8(a8), split8(b8));
+      fb[kt] = split8(b8);
     }
-    *reinterpret_cast<f32x4*>(rec + Gm::U_OFF + ((size_t)tile * 64 + l) * 16) = acc;
+#pragma unroll
+    for (int mt = 0; mt < NB; ++mt) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt) {
+        if (32 * kt > 16 * mt + 15) break;
+        Frag fa;
+        fa.hi = sMf[(mt * KTC + kt) * 128 + l];
+        fa.lo = sMf[(mt * KTC + kt) * 128 + 64 + l];
+        if (sizeof(IO) == 2) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.lo, fb[kt].hi, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa.hi, fb[kt].hi, acc, 0, 0, 0);
+        } else {
+          acc = mma3(acc, fa, fb[kt]);
+        }
+      }
+      *reinterpret_cast<f32x4*>(rec + Gm::U_OFF + (((size_t)mt * MTD + nt) * 64 + l) * 16) = acc;
+    }
   }
 }
 
