@@ -133,7 +133,7 @@ size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Header of the workspace: chunk table [NCB] and per-sequence chunk offsets.
 struct WsLayout {
-  size_t table_off, off_off, rec_off;
+  size_t table_off, off_off, order_off, rec_off;
   int64_t ncb;
 };
 
@@ -142,7 +142,8 @@ WsLayout ws_layout(int64_t T, int N, int C) {
   w.ncb = (T + C - 1) / C + N;
   w.table_off = 0;
   w.off_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
-  w.rec_off = w.off_off + round256((size_t)(N + 1) * sizeof(int));
+  w.order_off = w.off_off + round256((size_t)(N + 1) * sizeof(int));
+  w.rec_off = w.order_off + round256((size_t)N * sizeof(int));
   return w;
 }
 
@@ -164,9 +165,10 @@ size_t rec_bytes(int D, int C) {
 // bounds are clamped to 0 <= lo <= hi <= T.
 __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb,
-    ChunkEntry* __restrict__ table, int* __restrict__ off) {
+    ChunkEntry* __restrict__ table, int* __restrict__ off, int* __restrict__ order) {
   __shared__ int scan[NTHREADS];
   __shared__ int carry;
+  __shared__ int bcount[33], bbase[33];
   const int t = threadIdx.x;
   if (t == 0) carry = 0;
   __syncthreads();
@@ -204,6 +206,29 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     __syncthreads();
   }
   if (t == 0) off[N] = carry;
+  // Longest sequences first: order[] lists the sequences by descending
+  // power-of-two bucket of their chunk count, so the state pass starts the
+  // longest serial chains first.
+  if (t < 33) bcount[t] = 0;
+  __syncthreads();
+  auto bucket = [&](int n) {  // chunk count from the clamped bounds, as above
+    const int64_t a = cu[n], b = cu[n + 1];
+    const int lo = (int)(a < 0 ? 0 : (a > T ? T : a));
+    const int hi = (int)(b < lo ? lo : (b > T ? T : b));
+    const int nch = (hi - lo + C - 1) / C;
+    return nch <= 0 ? 0 : 32 - __clz(nch);
+  };
+  for (int n = t; n < N; n += NTHREADS) atomicAdd(&bcount[bucket(n)], 1);
+  __syncthreads();
+  if (t == 0) {
+    int acc = 0;
+    for (int b = 32; b >= 0; --b) {
+      bbase[b] = acc;
+      acc += bcount[b];
+    }
+  }
+  __syncthreads();
+  for (int n = t; n < N; n += NTHREADS) order[atomicAdd(&bbase[bucket(n)], 1)] = n;
   for (int64_t i = carry + t; i < ncb; i += NTHREADS) {
     ChunkEntry e;
     e.seq = 0;
@@ -723,9 +748,6 @@ struct StateSmem {
 };
 
 // Per-wave operands of one chunk that the state pass reads from the workspace.
-// They are fetched a phase ahead of their use: W and Q e^G of chunk i+1
-// while chunk i finishes its output and state update; U, Aq, K e^{G_C-G} and
-// e^{G_C} of chunk i while its W S products run.
 template <int D, int C, int VT>
 struct StateOps {
   typedef Geom<D, C> Gm;
@@ -736,13 +758,14 @@ struct StateOps {
   Frag aq[KTC];            // scale Aq, row tile mt
   Frag kt[MS][KTC];        // (K e^{G_C-G})^T, row tiles ms = wave + 4 i
   f32x4 gc[MS];            // e^{G_C} of the rows of those tiles
+  ChunkEntry ce;           // token range of the chunk
 };
 
 template <typename IO, int D, int C, int VT>
-__global__ __launch_bounds__(NTHREADS) void state_kernel(
+__global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     const ChunkEntry* __restrict__ table, const int* __restrict__ off,
-    const char* __restrict__ recs, int N, int H, const float* __restrict__ h0,
-    float* __restrict__ ht, IO* __restrict__ o) {
+    const int* __restrict__ order, const char* __restrict__ recs, int N, int H,
+    const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o) {
   typedef Geom<D, C> Gm;
   typedef StateSmem<D, C, VT> Sm;
   typedef StateOps<D, C, VT> Ops;
@@ -756,12 +779,13 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
   bf16* sDl = reinterpret_cast<bf16*>(smem + 2 * Sm::S_BYTES + Sm::D_BYTES);
 
   // XCD-aware unit mapping: the NV tiles of one (sequence, head) get block
-  // ids congruent mod 8, i.e. the same XCD and L2.
+  // ids congruent mod 8, i.e. the same XCD and L2.  Units are taken in the
+  // plan's longest-sequence-first order.
   const int b = blockIdx.x;
   const int vt = (b / 8) % NV;
   const int u = (b / (8 * NV)) * 8 + (b % 8);
   if (u >= N * H) return;
-  const int n = u / H, h = u % H;
+  const int n = order[u / H], h = u % H;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
   const bool has_mt = w < NB;
   const int mt = w;
@@ -787,20 +811,15 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
   }
 
   const int c_first = off[n], c_last = off[n + 1];
-  Ops ops;
-  auto load_wq = [&](int ch) {
+  auto load = [&](Ops& ops, int ch) {
     const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
+    ops.ce = table[ch];
     if (has_mt) {
 #pragma unroll
       for (int kt = 0; kt < KTD; ++kt) {
         ops.w[kt] = load_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
         ops.q[kt] = load_frag(rec + Gm::Q_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
       }
-    }
-  };
-  auto load_rest = [&](int ch) {
-    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
-    if (has_mt) {
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt)
         ops.u[nt] = *reinterpret_cast<const f32x4*>(
@@ -822,13 +841,8 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
       }
     }
   };
-  if (c_first < c_last) load_wq(c_first);
-  __syncthreads();
 
-  for (int ch = c_first; ch < c_last; ++ch) {
-    const ChunkEntry ce = table[ch];
-    load_rest(ch);
-
+  auto process = [&](const Ops& ops) {
     // -- 1. S^T (hi, lo) into LDS
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
@@ -887,8 +901,6 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
         *reinterpret_cast<bf16x4v*>(sDl + at) = lo;
       }
     }
-    // W and Q e^G of this chunk are consumed: fetch the next chunk's
-    if (ch + 1 < c_last) load_wq(ch + 1);
     __syncthreads();
 
     // -- 4. O = Qs + (scale Aq) D for row tile mt, written to o
@@ -910,8 +922,8 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int t = 16 * mt + 4 * lg + e;
-          if (t < ce.len)
-            o[((int64_t)(ce.start + t) * H + h) * D + vt * VT + 16 * nt + lr] =
+          if (t < ops.ce.len)
+            o[((int64_t)(ops.ce.start + t) * H + h) * D + vt * VT + 16 * nt + lr] =
                 from_f32<IO>(Qs[nt][e]);
         }
       }
@@ -939,6 +951,19 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
         }
       }
     }
+  };
+
+  // Two operand sets in registers: chunk i+1's set is fetched while chunk i
+  // is computed.
+  Ops opsA, opsB;
+  if (c_first < c_last) load(opsA, c_first);
+  __syncthreads();
+  for (int ch = c_first; ch < c_last; ch += 2) {
+    if (ch + 1 < c_last) load(opsB, ch + 1);
+    process(opsA);
+    if (ch + 1 >= c_last) break;
+    if (ch + 2 < c_last) load(opsA, ch + 2);
+    process(opsB);
   }
 
   if (ht != nullptr) {
@@ -959,8 +984,11 @@ __global__ __launch_bounds__(NTHREADS) void state_kernel(
 
 // ----------------------------------------------------------------- launch
 
+// V tile of the state pass: every tile's workgroup loads the chunk's full
+// W, Q e^G, K e^{G_C-G} and Aq, so wider tiles cut the replicated operand
+// traffic (per-CU load bandwidth) at the cost of fewer, busier workgroups.
 template <int D>
-constexpr int state_vt() { return D >= 32 ? 32 : 16; }
+constexpr int state_vt() { return D >= 32 ? 32 : D; }
 
 template <typename IO, int D, int C>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
@@ -971,9 +999,10 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   char* base = reinterpret_cast<char*>(a.ws);
   ChunkEntry* table = reinterpret_cast<ChunkEntry*>(base + ws.table_off);
   int* off = reinterpret_cast<int*>(base + ws.off_off);
+  int* order = reinterpret_cast<int*>(base + ws.order_off);
   char* recs = base + ws.rec_off;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
-                     C, ws.ncb, table, off);
+                     C, ws.ncb, table, off, order);
   if (a.T > 0)
     hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
@@ -981,7 +1010,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
-                     dim3(NTHREADS), 0, st, table, off, recs, a.N, a.H, a.h0, a.ht,
+                     dim3(NTHREADS), 0, st, table, off, order, recs, a.N, a.H, a.h0, a.ht,
                      (IO*)a.o);
   (void)sizeof(Gm);
   return hipGetLastError();
