@@ -63,6 +63,33 @@ def prefill_bytes(T, N, H, K, V, io_bytes=2):
     return T * H * per_tok_head + 2 * N * H * K * V * 4
 
 
+def intra_bytes(T, H, K, V, io_bytes=2):
+    """Algorithmic bytes the intra-chunk kernel must move: it is the only
+    reader of q, k, v, g and beta."""
+    return T * H * ((2 * K + V) * io_bytes + 4 * K + 4)
+
+
+def state_bytes(T, N, H, K, V, io_bytes=2):
+    """Algorithmic bytes the state kernel must move: o written, h0 read and
+    ht written.  intra_bytes + state_bytes = prefill_bytes."""
+    return T * H * V * io_bytes + 2 * N * H * K * V * 4
+
+
+def intra_flops(T, H, K, V, C):
+    """Algorithmic flops of the intra-chunk kernel per token-head: the
+    strictly lower decayed K K^T ((C-1)/2 pairs per token), the lower decayed
+    Q K^T with diagonal ((C+1)/2), and the two triangular products W = M (K e^G)
+    and U = M V; 2 flops per multiply-add."""
+    return T * H * ((C - 1) * K + (C + 1) * K + (C + 1) * K + (C + 1) * V)
+
+
+def state_flops(T, H, K, V, C):
+    """Algorithmic flops of the state kernel per token-head: W S, (Q e^G) S
+    and (K e^{G_C - G})^T D (K V multiply-adds each) and the lower-triangular
+    Aq D ((C+1)/2 V)."""
+    return T * H * (6 * K * V + (C + 1) * V)
+
+
 def gate_bytes(T, H, K):
     """a read, g written (fp32, per channel); b read, beta written."""
     return T * H * (8 * K + 8)
@@ -108,6 +135,13 @@ def bench_prefill(steps, warmup):
     ws = torch.empty(kda.kda_chunk_prefill_workspace_size(T, N, H, K, V, C),
                      dtype=torch.uint8, device="cuda")
 
+    # A plain elementwise copy (negation) of known size, 256 MiB read and
+    # 256 MiB written, outside every timed region: the reference point that scales rocprofv3's FETCH_SIZE and
+    # WRITE_SIZE counters to bytes.
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    torch.neg(src, out=torch.empty_like(src))
+    del src
+
     def gate():
         kda.kda_gate_prep(t["a"], t["b"], t["A_log"], t["dt_bias"], g=g, beta=beta)
 
@@ -122,11 +156,30 @@ def bench_prefill(steps, warmup):
     ms_step = _time(step, steps, warmup)
     ms_gate = _time(gate, steps, warmup)
     ms_prefill = _time(prefill, steps, warmup)
+    kernels = kernel_times(t, g, beta, o, ht, ws, scale, C, steps)
     pb = prefill_bytes(T, N, H, K, V)
     gb = gate_bytes(T, H, K)
     return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_gate=ms_gate,
                 ms_prefill=ms_prefill, prefill_bytes=pb, gate_bytes=gb,
-                flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
+                intra_bytes=intra_bytes(T, H, K, V), state_bytes=state_bytes(T, N, H, K, V),
+                kernels=kernels, flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
+
+
+def kernel_times(t, g, beta, o, ht, ws, scale, C, steps):
+    """Average duration (ms) of each of the prefill's three kernels, from HIP
+    events that kda_chunk_prefill_marked records between them on the launch
+    stream.  Before every call a 512 MiB buffer is overwritten (outside the
+    marks) so that no input is served from the 256 MB last-level cache."""
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for m in marks:
+        flush.zero_()
+        kda.kda_chunk_prefill_marked(m, t["q"], t["k"], t["v"], g, beta, t["cu"], scale,
+                                     h0=t["h0"], chunk=C, o=o, ht=ht, workspace=ws)
+    torch.cuda.synchronize()
+    names = ("plan", "intra", "state")
+    return {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / steps
+            for i, n in enumerate(names)}
 
 
 def bench_decode(steps, warmup):
@@ -204,6 +257,51 @@ def bench_long(steps, warmup):
                 tokens_per_s_segmented=T / (ms_seg * 1e-3),
                 tokens_per_s_full=T / (ms_full * 1e-3),
                 bytes=prefill_bytes(T, 1, H, K, V))
+
+
+KERNEL_SYMBOL = {"intra": "intra_kernel", "state": "state_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_varlen_7680_traffic.md")
+PREFILL_SOURCE = os.path.join(ROOT, "kda_gated_delta_amd", "csrc", "kda_prefill.hip")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size),
+    or None when there is none or the kernel source has changed since."""
+    import hashlib
+
+    try:
+        lines = open(TRAFFIC_FILE).read().splitlines()
+        sha = hashlib.sha256(open(PREFILL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    for ln in lines:
+        if ln.startswith('{"traffic"'):
+            rec = json.loads(ln)["traffic"].get(kernel)
+            if rec and rec.get("source_sha256") == sha:
+                return rec["bytes_per_launch"]
+    return None
+
+
+def roofline(p):
+    """Roofline of the prefill's dominant kernel (the longer of the intra-chunk
+    and state kernels by live HIP-event timing).  Its bound is the larger of
+    algorithmic bytes / HBM peak and algorithmic flops / bf16 MFMA peak."""
+    w, T, N = p["workload"], p["T"], p["N"]
+    H, K, V, C = w["H"], w["K"], w["V"], w["chunk"]
+    kern = max(("intra", "state"), key=lambda n: p["kernels"][n])
+    nbytes = p["intra_bytes"] if kern == "intra" else p["state_bytes"]
+    flops = (intra_flops if kern == "intra" else state_flops)(T, H, K, V, C)
+    sec = p["kernels"][kern] * 1e-3
+    if nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (BF16_MFMA_PEAK_TFLOPS * 1e12):
+        bound, achieved, peak, unit = "hbm", nbytes / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "mfma", flops / sec / 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "kernel": KERNEL_SYMBOL[kern], "achieved": achieved,
+            "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": measured_traffic(KERNEL_SYMBOL[kern]),
+            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "avg_ms": p["kernels"][kern]}
 
 
 def cpu_baseline(inputs, workload):
@@ -285,12 +383,12 @@ def main():
         "config": {"workload": "varlen_prefill_7680: 4 packed sequences {512,1024,2048,4096}, "
                                "H=32, K=V=128, chunk 64, gate prep + prefill per step",
                    "global_batch": p["N"], "seq_len": p["T"], "parallelism": "none"},
-        "roofline": {"bound": "hbm", "kernel": "kda_chunk_prefill (plan+intra+state)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "roofline": roofline(p),
         "prefill": {"ms": p["ms_prefill"], "ms_gate": p["ms_gate"],
+                    "kernel_ms": p["kernels"],
                     "tokens_per_s": p["T"] / (p["ms_prefill"] * 1e-3),
                     "algorithmic_bytes": p["prefill_bytes"],
+                    "gbs": achieved, "frac_of_hbm_peak": achieved / HBM_PEAK_GBS,
                     "algorithmic_flops": p["flops"],
                     "tflops": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12,
                     "mfma_frac_of_bf16_peak": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12

@@ -71,7 +71,7 @@ const char* kda_status_string(kda_status s);
  *     g = lower_bound * sigmoid(exp(A_log) (a + dt_bias)).
  *   g       [T, H, K] fp32  output log decay (<= 0)
  *   beta    [T, H]    fp32  output sigmoid(b)
- * T may be 0 (nothing is enqueued).  K must be a multiple of 4.
+ * T may be 0 (nothing is enqueued).  K in {16, 32, 64, 128}.
  */
 kda_status kda_gate_prep(const float* a, const float* b, const float* A_log,
                          const float* dt_bias, int64_t T, int32_t H, int32_t K,
@@ -114,6 +114,27 @@ kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
                              float scale, const float* h0, float* ht, void* o,
                              void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/*
+ * kda_chunk_prefill with kernel timing marks, for benchmarks and profilers.
+ * Same arguments, work and results as kda_chunk_prefill; in addition it
+ * records four caller-created HIP events (hipEvent_t passed as void*) on
+ * `stream`: marks[0] before the chunk-table kernel, marks[1] before the
+ * intra-chunk kernel, marks[2] before the inter-chunk state kernel and
+ * marks[3] after it, so that the elapsed time between consecutive marks is
+ * one kernel's duration.  A NULL `marks` or a NULL entry returns
+ * KDA_ERR_INVALID_ARGUMENT with nothing enqueued; a failed event record
+ * returns KDA_ERR_LAUNCH.
+ */
+kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
+                                    const void* v, const float* g,
+                                    const float* beta,
+                                    const int32_t* cu_seqlens, int32_t N,
+                                    int64_t T, int32_t H, int32_t K, int32_t V,
+                                    int32_t chunk, float scale, const float* h0,
+                                    float* ht, void* o, void* workspace,
+                                    size_t workspace_bytes, void* stream,
+                                    void* const* marks);
 
 /*
  * Single-token decode on a slot-indexed state pool, updated in place

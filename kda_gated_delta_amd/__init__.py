@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i64,
                                     i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.kda_chunk_prefill.restype = ctypes.c_int
+    L.kda_chunk_prefill_marked.argtypes = L.kda_chunk_prefill.argtypes + [vp]
+    L.kda_chunk_prefill_marked.restype = ctypes.c_int
     L.kda_recurrent_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64,
                                        vp, i32, i32, i32, i32, vp, vp]
     L.kda_recurrent_decode.restype = ctypes.c_int
@@ -61,7 +63,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
-            "kda_chunk_prefill", "kda_recurrent_decode", "kda_verify")
+            "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_recurrent_decode",
+            "kda_verify")
 
 
 def status_string(status: int) -> str:
@@ -133,6 +136,27 @@ def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
     update); ``workspace`` is a uint8 device tensor of at least
     ``kda_chunk_prefill_workspace_size`` bytes (allocated here if None).
     """
+    return _prefill("kda_chunk_prefill", None, q, k, v, g, beta, cu_seqlens, scale, h0,
+                    output_final_state, chunk, o, ht, workspace)
+
+
+def kda_chunk_prefill_marked(marks, q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
+                             output_final_state: bool = True, chunk: int = 64, o=None,
+                             ht=None, workspace=None):
+    """kda_chunk_prefill that also records the four ``torch.cuda.Event``s in
+    ``marks`` around its three kernels (chunk table, intra-chunk, state pass):
+    ``marks[i].elapsed_time(marks[i + 1])`` is kernel i's duration."""
+    if len(marks) != 4:
+        raise ValueError("marks: expected 4 events")
+    for m in marks:
+        if not m.cuda_event:  # events are created lazily by their first record
+            m.record()
+    return _prefill("kda_chunk_prefill_marked", marks, q, k, v, g, beta, cu_seqlens,
+                    scale, h0, output_final_state, chunk, o, ht, workspace)
+
+
+def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_state,
+             chunk, o, ht, workspace):
     T, H, K = q.shape
     V = v.shape[2]
     dev = q.device
@@ -155,10 +179,14 @@ def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
     need = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    _check("kda_chunk_prefill", lib().kda_chunk_prefill(
-        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
-        H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace),
-        workspace.numel(), _stream(dev)))
+    args = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
+            H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace),
+            workspace.numel(), _stream(dev)]
+    if marks is None:
+        _check(fn, lib().kda_chunk_prefill(*args))
+    else:
+        arr = (ctypes.c_void_p * 4)(*[m.cuda_event for m in marks])
+        _check(fn, lib().kda_chunk_prefill_marked(*args, arr))
     return o, ht
 
 

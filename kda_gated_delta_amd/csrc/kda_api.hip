@@ -19,6 +19,31 @@ bool io_aligned(kda_dtype io, const void* p) {
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
 
+kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const int32_t* cu_seqlens,
+                           int32_t N, int64_t T, int32_t H, int32_t K, int32_t V,
+                           int32_t chunk, float scale, const float* h0, float* ht, void* o,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* marks) {
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)T * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
+  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
+  if (T > 0 && (!io_aligned(io, q) || !io_aligned(io, k) || !io_aligned(io, v) ||
+                !io_aligned(io, o) || !aligned16(g)))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return KDA_ERR_INVALID_ARGUMENT;
+  const size_t need = kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
+    return KDA_ERR_WORKSPACE;
+  kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
+                     chunk, scale, h0, ht, o, workspace, workspace_bytes, marks};
+  return launch_status(kda::run_prefill(p, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,23 +87,21 @@ kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
                              float scale, const float* h0, float* ht, void* o,
                              void* workspace, size_t workspace_bytes,
                              void* stream) {
-  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-  if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
-  if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
-  if ((uint64_t)T * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
-  if (!cu_seqlens) return KDA_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!q || !k || !v || !g || !beta || !o)) return KDA_ERR_INVALID_ARGUMENT;
-  if (T > 0 && (!io_aligned(io, q) || !io_aligned(io, k) || !io_aligned(io, v) ||
-                !io_aligned(io, o) || !aligned16(g)))
+  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale,
+                         h0, ht, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
+                                    const void* v, const float* g, const float* beta,
+                                    const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                    int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                    float scale, const float* h0, float* ht, void* o,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* marks) {
+  if (!marks || !marks[0] || !marks[1] || !marks[2] || !marks[3])
     return KDA_ERR_INVALID_ARGUMENT;
-  if ((h0 && !aligned16(h0)) || (ht && !aligned16(ht))) return KDA_ERR_INVALID_ARGUMENT;
-  const size_t need = kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
-  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
-    return KDA_ERR_WORKSPACE;
-  kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
-                     chunk, scale, h0, ht, o, workspace, workspace_bytes};
-  return launch_status(kda::run_prefill(p, (hipStream_t)stream));
+  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale,
+                         h0, ht, o, workspace, workspace_bytes, stream, marks);
 }
 
 kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,

@@ -42,6 +42,9 @@ struct PrefillArgs {
   void* o;
   void* ws;
   size_t ws_bytes;
+  // Optional timing marks (hipEvent_t): recorded before the plan, intra and
+  // state kernels and after the state kernel; nullptr for none.
+  void* const* marks;
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

@@ -1001,17 +1001,25 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   int* off = reinterpret_cast<int*>(base + ws.off_off);
   int* order = reinterpret_cast<int*>(base + ws.order_off);
   char* recs = base + ws.rec_off;
+  auto mark = [&](int i) -> hipError_t {
+    return a.marks ? hipEventRecord((hipEvent_t)a.marks[i], st) : hipSuccess;
+  };
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
                      C, ws.ncb, table, off, order);
+  if ((e = mark(1)) != hipSuccess) return e;
   if (a.T > 0)
     hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
                        (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs);
+  if ((e = mark(2)) != hipSuccess) return e;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
                      dim3(NTHREADS), 0, st, table, off, order, recs, a.N, a.H, a.h0, a.ht,
                      (IO*)a.o);
+  if ((e = mark(3)) != hipSuccess) return e;
   (void)sizeof(Gm);
   return hipGetLastError();
 }

@@ -200,3 +200,19 @@ def test_prefill_then_decodes_equals_longer_prefill():
     assert rel_err_blocks(host(pool[1:]), ht_ref, 2) <= TOL["bf16"]
     assert rel_err_blocks(host(pool[1:]), host(ht_full), 2) <= TOL["bf16"]
     np.testing.assert_array_equal(host(o_pre), host(o_full[pre]))
+
+
+def test_marked_prefill_equals_unmarked():
+    """The timing-mark variant does the same work: bit-identical results, and
+    each mark pair brackets a kernel of positive duration."""
+    c = kda_synth.prefill_case([300, 77, 640], 4, 128, 128, "bf16", seed=21, regime="long")
+    t, g, beta = _inputs(c)
+    o1, ht1 = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
+                                    0.1, h0=t["h0"])
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    o2, ht2 = kda.kda_chunk_prefill_marked(marks, t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                           t["cu"], 0.1, h0=t["h0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    for i in range(3):
+        assert marks[i].elapsed_time(marks[i + 1]) > 0
