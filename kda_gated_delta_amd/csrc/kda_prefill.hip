@@ -94,6 +94,44 @@ __device__ __forceinline__ Frag load_frag(const char* tile) {
   return f;
 }
 
+// Buffer-resource loads: the base and every tile offset stay in scalar
+// registers, the only per-lane address is the lane's 16-byte slot.  Word 3 of
+// the descriptor selects 32-bit raw data (the gfx9 value).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// A fragment tile at byte `tile` of the resource (hi plane, then lo plane).
+__device__ __forceinline__ Frag buffer_frag(__amdgpu_buffer_rsrc_t r, uint32_t lane16,
+                                            uint32_t tile) {
+  Frag f;
+  f.hi = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane16, tile, 0));
+  f.lo = __builtin_bit_cast(bf16x8,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, lane16, tile + 1024, 0));
+  return f;
+}
+
+__device__ __forceinline__ f32x4 buffer_f32x4(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Scheduling hint for the block it sits in: spread `loads` vector-memory
+// reads evenly over the first `mfmas` MFMAs, so that a burst of loads does
+// not stall the wave on a full memory queue.
+template <int MFMAS, int LOADS>
+__device__ __forceinline__ void interleave_loads() {
+  constexpr int PER = MFMAS / LOADS > 0 ? MFMAS / LOADS : 1;
+#pragma unroll
+  for (int i = 0; i < LOADS; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, PER, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);    // VMEM read
+  }
+}
+
 // Eight consecutive values (16-byte aligned) from LDS as fp32.
 __device__ __forceinline__ void lds8(const float* p, float (&x)[8]) {
   const float4 a = *reinterpret_cast<const float4*>(p);
@@ -290,7 +328,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   const ChunkEntry ce = table[chunk];
   if (ce.len <= 0) return;
   const int L = ce.len;
-  char* rec = recs + (size_t)blockIdx.x * Gm::REC;
+  // records are head-major, so that one head's chain of chunks is contiguous
+  const int ncb = gridDim.x / H;
+  char* rec = recs + ((size_t)h * ncb + chunk) * Gm::REC;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
   // row t of q (8 io elements from channel c) straight from global memory
   auto qrow8 = [&](int t, int c, float (&x)[8]) {
@@ -738,13 +778,17 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 
 // ------------------------------------------------------------------ state
 
-template <int D, int C, int VT>
+template <typename IO, int D, int C, int VT>
 struct StateSmem {
   static constexpr int SK = (D < 32 ? 32 : D) + 8;        // S^T row: channels (+pad)
   static constexpr int DK = Geom<D, C>::KTC * 32 + 8;     // D^T row: tokens (+pad)
   static constexpr size_t S_BYTES = (size_t)VT * SK * 2;  // one bf16 plane
   static constexpr size_t D_BYTES = (size_t)VT * DK * 2;
-  static constexpr size_t TOTAL = 2 * S_BYTES + 2 * D_BYTES;
+  static constexpr size_t O_BYTES = (size_t)16 * VT * sizeof(IO);  // one wave's O tile
+  static constexpr size_t S_OFF = 0;                       // [hi, lo]
+  static constexpr size_t D_OFF = 2 * S_BYTES;             // [hi, lo]
+  static constexpr size_t O_OFF = D_OFF + 2 * D_BYTES;     // [4 waves]
+  static constexpr size_t TOTAL = O_OFF + 4 * O_BYTES;
 };
 
 // Per-wave operands of one chunk that the state pass reads from the workspace.
@@ -758,25 +802,22 @@ struct StateOps {
   Frag aq[KTC];            // scale Aq, row tile mt
   Frag kt[MS][KTC];        // (K e^{G_C-G})^T, row tiles ms = wave + 4 i
   f32x4 gc[MS];            // e^{G_C} of the rows of those tiles
-  ChunkEntry ce;           // token range of the chunk
 };
 
 template <typename IO, int D, int C, int VT>
 __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     const ChunkEntry* __restrict__ table, const int* __restrict__ off,
-    const int* __restrict__ order, const char* __restrict__ recs, int N, int H,
+    const int* __restrict__ order, const char* __restrict__ recs, int ncb, int N, int H,
     const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o) {
   typedef Geom<D, C> Gm;
-  typedef StateSmem<D, C, VT> Sm;
+  typedef StateSmem<IO, D, C, VT> Sm;
   typedef StateOps<D, C, VT> Ops;
   constexpr int NV = D / VT, NTV = VT / 16, NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD;
   constexpr int MTD = Gm::MTD, MS = Ops::MS;
   constexpr int SK = Sm::SK, DK = Sm::DK;
   __shared__ __align__(16) char smem[Sm::TOTAL];
-  bf16* sSh = reinterpret_cast<bf16*>(smem);
-  bf16* sSl = reinterpret_cast<bf16*>(smem + Sm::S_BYTES);
-  bf16* sDh = reinterpret_cast<bf16*>(smem + 2 * Sm::S_BYTES);
-  bf16* sDl = reinterpret_cast<bf16*>(smem + 2 * Sm::S_BYTES + Sm::D_BYTES);
+  bf16* sDh = reinterpret_cast<bf16*>(smem + Sm::D_OFF);
+  bf16* sDl = reinterpret_cast<bf16*>(smem + Sm::D_OFF + Sm::D_BYTES);
 
   // XCD-aware unit mapping: the NV tiles of one (sequence, head) get block
   // ids congruent mod 8, i.e. the same XCD and L2.  Units are taken in the
@@ -785,10 +826,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
   const int vt = (b / 8) % NV;
   const int u = (b / (8 * NV)) * 8 + (b % 8);
   if (u >= N * H) return;
-  const int n = order[u / H], h = u % H;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
-  const bool has_mt = w < NB;
+  // workgroup-uniform values as scalars, so that every branch on them is
+  // uniform and the chunk table is read through scalar loads
+  const int n = __builtin_amdgcn_readfirstlane(order[u / H]), h = u % H;
+  const int tid = threadIdx.x, l = tid & 63, lg = l >> 4, lr = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // When every wave owns a chunk row tile and the same number of state row
+  // tiles (the usual D and C), these tests are compile-time true: no branch
+  // then separates the operand loads, and the wait counts the compiler places
+  // for them stay exact, so the next chunk's loads are never waited for.
+  constexpr bool ALL_MT = NB >= 4, ALL_MS = MTD % 4 == 0;
+  const bool has_mt = ALL_MT || w < NB;
   const int mt = w;
+  IO* sO = reinterpret_cast<IO*>(smem + Sm::O_OFF + w * Sm::O_BYTES);
 
   // zero the LDS padding once (k positions beyond D or C stay zero)
   for (int e = tid; e < (int)(Sm::TOTAL / 4); e += NTHREADS) reinterpret_cast<int*>(smem)[e] = 0;
@@ -803,51 +853,111 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float x = 0.f;
-        if (h0 != nullptr && ms < MTD)
+        if (h0 != nullptr && (ALL_MS || ms < MTD))
           x = h0[(((int64_t)n * H + h) * D + 16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr];
         S[i][nt][e] = x;
       }
     }
   }
 
-  const int c_first = off[n], c_last = off[n + 1];
-  auto load = [&](Ops& ops, int ch) {
-    const char* rec = recs + ((size_t)ch * H + h) * Gm::REC;
-    ops.ce = table[ch];
+  const int c_first = __builtin_amdgcn_readfirstlane(off[n]);
+  const int c_last = __builtin_amdgcn_readfirstlane(off[n + 1]);
+  // token range of the sequence; chunk c covers tokens from seq_start +
+  // (c - c_first) C, at most C of them, up to seq_end
+  int seq_start = 0, seq_end = 0;
+  if (c_first < c_last) {
+    seq_start = __builtin_amdgcn_readfirstlane(table[c_first].start);
+    seq_end = __builtin_amdgcn_readfirstlane(table[c_last - 1].start + table[c_last - 1].len);
+  }
+  // Every operand of a chunk is loaded unconditionally (including Aq tiles
+  // above the diagonal, which are never multiplied), so the loads form one
+  // straight block.
+  const uint32_t lane16 = (uint32_t)l * 16u;
+  auto rsrc_of = [&](int ch) {
+    return buffer_rsrc(recs + ((size_t)h * ncb + ch) * Gm::REC, (uint32_t)Gm::REC);
+  };
+  // The operand set of a chunk is fetched in four parts, so that the fetch
+  // of chunk i+1 can be spread over the phases of chunk i.
+  auto load_w = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
     if (has_mt) {
 #pragma unroll
-      for (int kt = 0; kt < KTD; ++kt) {
-        ops.w[kt] = load_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
-        ops.q[kt] = load_frag(rec + Gm::Q_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES);
-      }
+      for (int kt = 0; kt < KTD; ++kt)
+        ops.w[kt] = buffer_frag(r, lane16, Gm::W_OFF + (mt * KTD + kt) * FRAG_BYTES);
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt)
-        ops.u[nt] = *reinterpret_cast<const f32x4*>(
-            rec + Gm::U_OFF + (((size_t)mt * MTD + vt * NTV + nt) * 64 + l) * 16);
-#pragma unroll
-      for (int kt = 0; kt < KTC; ++kt)
-        if (32 * kt <= 16 * mt + 15)
-          ops.aq[kt] = load_frag(rec + Gm::AQ_OFF + (size_t)(mt * KTC + kt) * FRAG_BYTES);
+        ops.u[nt] = buffer_f32x4(r, lane16, Gm::U_OFF + ((mt * MTD + vt * NTV + nt) * 64) * 16);
     }
-    const float* gC = reinterpret_cast<const float*>(rec + Gm::GC_OFF);
+  };
+  auto load_kt = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
-      if (ms < MTD) {
-        ops.gc[i] = *reinterpret_cast<const f32x4*>(gC + 16 * ms + 4 * lg);
+      if (ALL_MS || ms < MTD) {
+        ops.gc[i] = buffer_f32x4(r, (uint32_t)lg * 16u, Gm::GC_OFF + 64 * ms);
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt)
-          ops.kt[i][kt] = load_frag(rec + Gm::KT_OFF + (size_t)(ms * KTC + kt) * FRAG_BYTES);
+          ops.kt[i][kt] = buffer_frag(r, lane16, Gm::KT_OFF + (ms * KTC + kt) * FRAG_BYTES);
       }
     }
   };
+  auto load_q = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
+    if (has_mt) {
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt)
+        ops.q[kt] = buffer_frag(r, lane16, Gm::Q_OFF + (mt * KTD + kt) * FRAG_BYTES);
+    }
+  };
+  auto load_aq = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
+    if (has_mt) {
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt)
+        ops.aq[kt] = buffer_frag(r, lane16, Gm::AQ_OFF + (mt * KTC + kt) * FRAG_BYTES);
+    }
+  };
+  auto load = [&](Ops& ops, int ch) {
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(ch);
+    load_w(ops, r);
+    load_kt(ops, r);
+    load_q(ops, r);
+    load_aq(ops, r);
+  };
 
-  auto process = [&](const Ops& ops) {
+  // One chunk.  The carried chain is S -> P = W S -> D = U - P -> S update;
+  // the read-out O = (Q e^G) S + Aq D follows the update.  Each phase first
+  // reads all of its LDS fragments, then issues its MFMAs back to back; the
+  // entering S and D fragments stay in registers for the read-out.
+  bf16* sSh = reinterpret_cast<bf16*>(smem + Sm::S_OFF);
+  bf16* sSl = reinterpret_cast<bf16*>(smem + Sm::S_OFF + Sm::S_BYTES);
+  // L2 prefetch two chunks ahead: the NV workgroups of a (sequence, head)
+  // each touch one word in every NV-th 128-byte line of the record, so the
+  // operand loads of that chunk, issued one chunk later, hit L2.  The words
+  // are read into registers that are consumed one chunk after that, when the
+  // loads have long completed.
+  constexpr int LINES = (int)(Gm::REC / 128);
+  constexpr int NPF = (LINES + NV * NTHREADS - 1) / (NV * NTHREADS);
+  int pf[NPF];
+#pragma unroll
+  for (int i = 0; i < NPF; ++i) pf[i] = 0;
+  auto prefetch = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) asm volatile("" ::"v"(pf[i]));
+    const __amdgpu_buffer_rsrc_t r = rsrc_of(min(ch + 2, c_last - 1));
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) {
+      const int line = vt + NV * (tid + NTHREADS * i);
+      // out-of-range offsets read as zero (the buffer bound is the record)
+      pf[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)line * 128u, 0, 0);
+    }
+  };
+
+  auto process = [&](Ops& ops, int ch) {
+    const __amdgpu_buffer_rsrc_t rn = rsrc_of(min(ch + 1, c_last - 1));
+    prefetch(ch);
     // -- 1. S^T (hi, lo) into LDS
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
-      if (ms < MTD) {
+      if (ALL_MS || ms < MTD) {
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           bf16x4v hi, lo;
@@ -865,27 +975,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     }
     __syncthreads();
 
-    // -- 2./3. row tile mt = w: P = W S, Qs = (Q e^G) S, D = U - P
-    f32x4 Qs[NTV];
+    // -- 2. row tile mt = w: P = W S, D = U - P into LDS
+    Frag fs[KTD][NTV];
     if (has_mt) {
-      f32x4 P[NTV];
 #pragma unroll
-      for (int nt = 0; nt < NTV; ++nt) {
-        P[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Qs[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int kt = 0; kt < KTD; ++kt) {
+      for (int kt = 0; kt < KTD; ++kt)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
-          Frag fs;
           const int at = (16 * nt + lr) * SK + 32 * kt + 8 * lg;
-          fs.hi = *reinterpret_cast<const bf16x8*>(sSh + at);
-          fs.lo = *reinterpret_cast<const bf16x8*>(sSl + at);
-          P[nt] = mma3(P[nt], ops.w[kt], fs);
-          Qs[nt] = mma3(Qs[nt], ops.q[kt], fs);
+          fs[kt][nt].hi = *reinterpret_cast<const bf16x8*>(sSh + at);
+          fs[kt][nt].lo = *reinterpret_cast<const bf16x8*>(sSl + at);
         }
-      }
+      f32x4 P[NTV];
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) P[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) P[nt] = mma3(P[nt], ops.w[kt], fs[kt][nt]);
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) {
         bf16x4v hi, lo;
@@ -903,74 +1010,91 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     }
     __syncthreads();
 
-    // -- 4. O = Qs + (scale Aq) D for row tile mt, written to o
-    if (has_mt) {
+    // -- 3. S = Diag(e^{G_C}) S + (K e^{G_C - G})^T D
+    Frag fd[KTC][NTV];
 #pragma unroll
-      for (int kt = 0; kt < KTC; ++kt) {
-        if (32 * kt > 16 * mt + 15) break;  // Aq is lower triangular
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) {
-          Frag fd;
-          const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
-          fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
-          fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
-          Qs[nt] = mma3(Qs[nt], ops.aq[kt], fd);
-        }
-      }
+    for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * lg + e;
-          if (t < ops.ce.len)
-            o[((int64_t)(ops.ce.start + t) * H + h) * D + vt * VT + 16 * nt + lr] =
-                from_f32<IO>(Qs[nt][e]);
-        }
+        const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
+        fd[kt][nt].hi = *reinterpret_cast<const bf16x8*>(sDh + at);
+        fd[kt][nt].lo = *reinterpret_cast<const bf16x8*>(sDl + at);
       }
-    }
-
-    // -- 5. S = Diag(e^{G_C}) S + (K e^{G_C - G})^T D
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
-      if (ms < MTD) {
+      if (ALL_MS || ms < MTD) {
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[i][nt][e] *= ops.gc[i][e];
 #pragma unroll
-        for (int kt = 0; kt < KTC; ++kt) {
+        for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-          for (int nt = 0; nt < NTV; ++nt) {
-            Frag fd;
-            const int at = (16 * nt + lr) * DK + 32 * kt + 8 * lg;
-            fd.hi = *reinterpret_cast<const bf16x8*>(sDh + at);
-            fd.lo = *reinterpret_cast<const bf16x8*>(sDl + at);
-            S[i][nt] = mma3(S[i][nt], ops.kt[i][kt], fd);
-          }
-        }
+          for (int nt = 0; nt < NTV; ++nt) S[i][nt] = mma3(S[i][nt], ops.kt[i][kt], fd[kt][nt]);
+      }
+    }
+    // W and U of this chunk are dead: fetch the next ones between the MFMAs
+    load_w(ops, rn);
+    interleave_loads<3 * MS * KTC * NTV, 2 * KTD + NTV>();
+
+    // -- 4. O = (scale Q e^G) S + (scale Aq) D for row tile mt
+    // (K e^{G_C-G} and e^{G_C} of this chunk are dead: every wave that owns
+    // state rows fetches the next ones, spread between the MFMAs below)
+    load_kt(ops, rn);
+    if (has_mt) {
+      f32x4 O[NTV];
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kt = 0; kt < KTD; ++kt)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) O[nt] = mma3(O[nt], ops.q[kt], fs[kt][nt]);
+      interleave_loads<3 * KTD * NTV, MS * (2 * KTC + 1)>();
+#pragma unroll
+      for (int kt = 0; kt < KTC; ++kt) {
+        if (32 * kt > 16 * mt + 15) break;  // Aq is lower triangular (uniform)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) O[nt] = mma3(O[nt], ops.aq[kt], fd[kt][nt]);
+      }
+      load_q(ops, rn);
+      load_aq(ops, rn);
+      // stage the 16 x VT tile in this wave's LDS slot, then 16-byte stores
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sO[(4 * lg + e) * VT + 16 * nt + lr] = from_f32<IO>(O[nt][e]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int c_start = seq_start + (ch - c_first) * C;
+      const int c_len = min(C, seq_end - c_start);
+      constexpr int ROW16 = VT * (int)sizeof(IO) / 16;  // 16-byte pieces per row
+#pragma unroll
+      for (int p = l; p < 16 * ROW16; p += 64) {
+        const int r = p / ROW16, c16 = p % ROW16;
+        const int t = 16 * mt + r;
+        const uint4 val = *reinterpret_cast<const uint4*>(sO + r * VT + c16 * (16 / sizeof(IO)));
+        if (t < c_len)
+          *reinterpret_cast<uint4*>(o + ((int64_t)(c_start + t) * H + h) * D + vt * VT +
+                                    c16 * (16 / sizeof(IO))) = val;
       }
     }
   };
 
-  // Two operand sets in registers: chunk i+1's set is fetched while chunk i
-  // is computed.
-  Ops opsA, opsB;
-  if (c_first < c_last) load(opsA, c_first);
+  // One operand set in registers: each part is refetched for chunk i+1 as
+  // soon as chunk i has used it, so every fetch has about one chunk period
+  // to arrive (the last fetch repeats the last chunk and goes unused).
+  Ops ops;
+  if (c_first < c_last) load(ops, c_first);
   __syncthreads();
-  for (int ch = c_first; ch < c_last; ch += 2) {
-    if (ch + 1 < c_last) load(opsB, ch + 1);
-    process(opsA);
-    if (ch + 1 >= c_last) break;
-    if (ch + 2 < c_last) load(opsA, ch + 2);
-    process(opsB);
-  }
+  for (int ch = c_first; ch < c_last; ++ch) process(ops, ch);
 
   if (ht != nullptr) {
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
-      if (ms < MTD) {
+      if (ALL_MS || ms < MTD) {
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
@@ -1017,7 +1141,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
-                     dim3(NTHREADS), 0, st, table, off, order, recs, a.N, a.H, a.h0, a.ht,
+                     dim3(NTHREADS), 0, st, table, off, order, recs, (int)ws.ncb, a.N, a.H,
+                     a.h0, a.ht,
                      (IO*)a.o);
   if ((e = mark(3)) != hipSuccess) return e;
   (void)sizeof(Gm);
