@@ -6,8 +6,8 @@
 // softplus(x) = x above the threshold 20, as in the kernels analysed on the
 // ReplaySSM page (section 3.8) and the target-verify PR report.
 //
-// Purely elementwise and HBM-bound: 128-bit loads and stores, a grid-stride
-// loop over float4 groups of the [T*H, K] row-major gate tensor.
+// Purely elementwise and HBM-bound: 128-bit loads and stores over float4
+// groups of the [T*H, K] row-major gate tensor.
 
 #include "kda_common.h"
 #include "kda_internal.h"
@@ -15,12 +15,56 @@
 namespace kda {
 namespace {
 
+// e^y on the hardware base-2 exponential.  y log2(e) is formed with its
+// rounding error carried separately (Cody and Waite's argument splitting:
+// log2(e) = L2E_HI + L2E_LO, the product error recovered by an fma), so the
+// result stays within a few ulp for large |y| instead of losing |y| 2^-24
+// relative to the rounding of the product.  Overflows to +inf above ~88.7,
+// underflows to 0 below ~-87.3 (denormal results are flushed).
+__device__ __forceinline__ float exp_split(float y) {
+  constexpr float L2E_HI = 1.4426950216293335f;  // log2(e) rounded to fp32
+  constexpr float L2E_LO = 1.925963033500011e-08f;  // log2(e) - L2E_HI
+  constexpr float LN2 = 0.6931471824645996f;
+  const float p = y * L2E_HI;
+  const float pl = fmaf(y, L2E_HI, -p) + y * L2E_LO;
+  return __builtin_amdgcn_exp2f(p) * fmaf(pl, LN2, 1.f);
+}
+
+// log(1 + u) for u in [0, 1].  Below 2^-8 the series u - u^2/2 + u^3/3
+// (truncation below u^3/4 relative); above, Goldberg's correction of a
+// rounded log: with w = 1 + u rounded, log(w) * u / (w - 1) (w - 1 is exact
+// since w lies in [1, 2]).
+__device__ __forceinline__ float log1p_unit(float u) {
+  constexpr float LN2 = 0.6931471824645996f;
+  const float series = u * fmaf(u, fmaf(u, 0.3333333432674408f, -0.5f), 1.f);
+  const float w = 1.f + u;
+  const float corrected = __builtin_amdgcn_logf(w) * LN2 * (u * __builtin_amdgcn_rcpf(w - 1.f));
+  return u < 0x1p-8f ? series : corrected;
+}
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), and x itself
+// above the threshold 20.
+__device__ __forceinline__ float softplus20(float x) {
+  const float sp = fmaxf(x, 0.f) + log1p_unit(exp_split(-fabsf(x)));
+  return x > 20.f ? x : sp;
+}
+
+// sigmoid(z) = 1 / (1 + e^-z); e^-z overflowing to +inf gives 0.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.f + exp_split(-z));
+}
+
 template <bool SAFE>
 __device__ __forceinline__ float gate1(float x, float rate, float lb) {
-  if (SAFE) return lb / (1.f + expf(-rate * x));
-  const float sp = x > 20.f ? x : log1pf(expf(x));
-  return -rate * sp;
+  if (SAFE) return lb * sigmoid_fast(rate * x);
+  return -rate * softplus20(x);
 }
+
+// Each thread takes UNROLL float4 groups, a block-stride apart, and issues
+// all of their loads before any arithmetic (several 16-byte loads in flight
+// per thread); a block covers UNROLL * 256 / (K / 4) whole (token, head)
+// rows, whose beta its first threads compute.
+constexpr int GATE_UNROLL = 4;
 
 template <int K, bool SAFE>
 __global__ __launch_bounds__(256) void gate_kernel(
@@ -29,29 +73,43 @@ __global__ __launch_bounds__(256) void gate_kernel(
     int64_t TH, int H, float lb, float* __restrict__ g,
     float* __restrict__ beta) {
   constexpr int Q = K / 4;  // float4 groups per (token, head) row
+  constexpr int ROWS = GATE_UNROLL * 256 / Q;
   const int64_t n4 = TH * Q;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4; i += stride) {
-    const uint32_t row = (uint32_t)(i / Q);
-    const int c = (int)(i % Q) * 4;
-    const int h = (int)(row % (uint32_t)H);
-    const float rate = expf(A_log[h]);
-    float4 x = load4(a + i * 4);
-    if (dt_bias) x = x + load4(dt_bias + h * K + c);
-    store4(g + i * 4, make_float4(gate1<SAFE>(x.x, rate, lb), gate1<SAFE>(x.y, rate, lb),
-                                  gate1<SAFE>(x.z, rate, lb), gate1<SAFE>(x.w, rate, lb)));
+  const int64_t base = (int64_t)blockIdx.x * (GATE_UNROLL * 256) + threadIdx.x;
+  float4 x[GATE_UNROLL];
+#pragma unroll
+  for (int u = 0; u < GATE_UNROLL; ++u) {
+    const int64_t i = base + u * 256;
+    x[u] = i < n4 ? load4(a + i * 4) : f4(0.f);
   }
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < TH; i += stride)
-    beta[i] = 1.f / (1.f + expf(-b[i]));
+  // b of this block's rows
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+  const bool has_b = threadIdx.x < ROWS && row0 + threadIdx.x < TH;
+  const float bb = has_b ? b[row0 + threadIdx.x] : 0.f;
+#pragma unroll
+  for (int u = 0; u < GATE_UNROLL; ++u) {
+    const int64_t i = base + u * 256;
+    if (i < n4) {
+      const int c = (int)(i % Q) * 4;
+      const int h = (int)((uint64_t)(i / Q) % (uint32_t)H);
+      const float rate = exp_split(A_log[h]);
+      float4 y = x[u];
+      if (dt_bias) y = y + load4(dt_bias + h * K + c);
+      store4(g + i * 4, make_float4(gate1<SAFE>(y.x, rate, lb), gate1<SAFE>(y.y, rate, lb),
+                                    gate1<SAFE>(y.z, rate, lb), gate1<SAFE>(y.w, rate, lb)));
+    }
+  }
+  if (has_b) beta[row0 + threadIdx.x] = sigmoid_fast(bb);
 }
 
 template <int K>
 hipError_t launch_gate(const GateArgs& p, hipStream_t st) {
   const int64_t TH = p.T * p.H;
   const int64_t n4 = TH * (K / 4);
-  int64_t blocks = (n4 + 255) / 256;
-  if (blocks > 256 * 64) blocks = 256 * 64;  // grid-stride beyond 64 blocks per CU
-  if (blocks < 1) blocks = 1;
+  const int64_t per_block = GATE_UNROLL * 256;
+  const int64_t blocks = (n4 + per_block - 1) / per_block;
+  if (blocks < 1) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (p.lower_bound != 0.f)
     hipLaunchKernelGGL((gate_kernel<K, true>), dim3((unsigned)blocks), dim3(256), 0, st,
                        p.a, p.b, p.A_log, p.dt_bias, TH, p.H, p.lower_bound, p.g, p.beta);
