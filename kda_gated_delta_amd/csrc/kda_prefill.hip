@@ -279,32 +279,75 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
 
 // ------------------------------------------------------------------ intra
 
+// Swizzled LDS layouts (no padding).  A row of N elements is cut into groups
+// of GR elements; group i of row r is stored at group position i ^ (r mod
+// N/GR).  Lanes that read the same columns of different rows then hit
+// different banks, and a group stays contiguous.
+template <int N, int GR>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int NG = N / GR;
+  static_assert((NG & (NG - 1)) == 0 && (GR & (GR - 1)) == 0, "powers of two");
+  return r * N + ((((unsigned)c / GR) ^ (unsigned)r) & (NG - 1)) * GR + ((unsigned)c % GR);
+}
+
 template <typename IO, int D, int C>
 struct IntraSmem {
-  static constexpr int DP = D + 4;  // fp32 row stride (16-byte aligned rows)
-  static constexpr int CP = C + 4;
-  static constexpr int DPIO = D + 16 / (int)sizeof(IO);  // io row stride
   static constexpr int NB = C / 16, KTC = (C + 31) / 32;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-  static constexpr size_t G_BYTES = (size_t)C * DP * 4;                 // G / K e^G / V
-  static constexpr size_t K_BYTES = cmax(cmax((size_t)C * DPIO * sizeof(IO),  // k, then
-                                              (size_t)NB * KTC * FRAG_BYTES),  // M frags,
-                                         (size_t)3 * 256 * 4);                 // solve scratch
-  static constexpr size_t AA_BYTES = cmax((size_t)C * CP * 4,      // A^T | Aq, then X
-                                          (size_t)32 * DP * 4);    // W staging (32 rows)
-  static constexpr size_t TOTAL = G_BYTES + K_BYTES + AA_BYTES + C * 4;
+  // sG [C][D] fp32 (groups of 8): G, then K e^G, then V
+  static constexpr size_t G_BYTES = (size_t)C * D * 4;
+  // sK [C][D] io (groups of 8): k; then the block-inverse scratch; then the
+  // split fragments of M = X diag(beta)
+  static constexpr size_t K_BYTES = cmax(cmax((size_t)C * D * sizeof(IO),
+                                              (size_t)NB * KTC * FRAG_BYTES),
+                                         (size_t)3 * 256 * 4);
+  // sQ [C][D] io (groups of 8): q; then beta
+  static constexpr size_t Q_BYTES = cmax((size_t)C * D * sizeof(IO), (size_t)C * 4);
+  // sAA [C][C] fp32 (groups of 4): A transposed in the strict upper triangle
+  // and Aq in the lower one, Aq's triangle then reused for X; finally the
+  // 32-row staging of W ([32][D] fp32, groups of 8)
+  static constexpr size_t AA_BYTES = cmax((size_t)C * C * 4, (size_t)32 * D * 4);
+  static constexpr size_t TOTAL = G_BYTES + K_BYTES + Q_BYTES + AA_BYTES;
 };
 
 constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
 
-// LDS use (bf16 io, C = 64, D = 128: 68.9 KB, two workgroups per CU):
-//   sG  [C][D+4] fp32   G (cumsum of g), then K e^G, then V
-//   sK  [C][D+8] io     k; then the block-inverse scratch; then the split
-//                       fragments of M = X diag(beta)
-//   sAA [C][C+4] fp32   A transposed in the strict upper triangle and Aq in
-//                       the lower one; Aq's triangle is then reused for X;
-//                       finally 32-row staging of W
-// q is not staged: its rows are read from global memory in fragment form.
+// Off-diagonal work of A and Aq: wave NB + idx takes row block I and the
+// column blocks J0 .. J0 + nJ - 1 (at most two, sharing the row operand);
+// row blocks are dealt from the last one.
+template <int NB>
+__device__ __forceinline__ void offdiag_group(int idx, int& I, int& J0, int& nJ) {
+  int k = 0;
+  I = 0;
+  J0 = 0;
+  nJ = 0;
+#pragma unroll
+  for (int i = NB - 1; i >= 1; --i)
+#pragma unroll
+    for (int j = 0; j < i; j += 2) {
+      if (k == idx) {
+        I = i;
+        J0 = j;
+        nJ = (i - j) < 2 ? (i - j) : 2;
+      }
+      ++k;
+    }
+}
+
+// Lane-broadcast helpers (DPP, no LDS): row_newbcast:n gives every lane of a
+// 16-lane row the value of lane n of that row; quad_perm[0,0,0,0] gives every
+// lane of a 4-lane quad the value of the quad's first lane.
+template <int N>
+__device__ __forceinline__ float bcast_row(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float bcast_quad0(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x00, 0xf, 0xf, false));
+}
+
+// LDS use (bf16 io, C = 64, D = 128: 80 KB, two workgroups per CU): see
+// IntraSmem.  Every input is staged once; the work units read their rows
+// from LDS into registers and take reference rows by lane broadcast.
 template <typename IO, int D, int C>
 __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
@@ -313,16 +356,22 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
   constexpr int NT = NT_INTRA, NW = NT / 64;
-  constexpr int DP = Sm::DP, CP = Sm::CP, DPIO = Sm::DPIO;
   constexpr int NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD, MTD = Gm::MTD;
+  constexpr int IOV = 16 / (int)sizeof(IO);  // io elements per 16 bytes
   __shared__ __align__(16) char smem[Sm::TOTAL];
   float* sG = reinterpret_cast<float*>(smem);
   IO* sK = reinterpret_cast<IO*>(smem + Sm::G_BYTES);
   float* sY = reinterpret_cast<float*>(smem + Sm::G_BYTES);     // over k (solve)
   bf16x8* sMf = reinterpret_cast<bf16x8*>(smem + Sm::G_BYTES);  // over k (W, U)
-  float* sAA = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES);
+  IO* sQ = reinterpret_cast<IO*>(smem + Sm::G_BYTES + Sm::K_BYTES);
+  float* sB = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES);  // over q
+  float* sAA = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES + Sm::Q_BYTES);
   float* sW = sAA;  // W staging, over A / Aq / X
-  float* sB = reinterpret_cast<float*>(smem + Sm::G_BYTES + Sm::K_BYTES + Sm::AA_BYTES);
+
+  // layouts
+  auto iG = [](int t, int c) { return swz<D, 8>(t, c); };    // sG, sK, sQ
+  auto iA = [](int r, int c) { return swz<C, 4>(r, c); };    // sAA
+  auto iW = [](int r, int c) { return swz<D, 8>(r, c); };    // sW
 
   const int chunk = blockIdx.x / H, h = blockIdx.x % H;
   const ChunkEntry ce = table[chunk];
@@ -331,21 +380,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   // records are head-major, so that one head's chain of chunks is contiguous
   const int ncb = gridDim.x / H;
   char* rec = recs + ((size_t)h * ncb + chunk) * Gm::REC;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
-  // row t of q (8 io elements from channel c) straight from global memory
-  auto qrow8 = [&](int t, int c, float (&x)[8]) {
-    if (t < L && c < D) {
-      const IO* src = q + ((int64_t)(ce.start + t) * H + h) * D + c;
-      const float4 lo4 = load4(src), hi4 = load4(src + 4);
-      x[0] = lo4.x; x[1] = lo4.y; x[2] = lo4.z; x[3] = lo4.w;
-      x[4] = hi4.x; x[5] = hi4.y; x[6] = hi4.z; x[7] = hi4.w;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = 0.f;
-    }
-  };
+  const int tid = threadIdx.x, l = tid & 63, lg = l >> 4, lr = l & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // v is only needed in step 9: fetch it now into registers
+  // v is only needed in step 9 and beta from step 6: fetch them now
   constexpr int VPT = (C * (D / 4) + NT - 1) / NT;  // float4 groups per thread
   float4 vreg[VPT];
 #pragma unroll
@@ -354,21 +392,44 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     vreg[i] = (e < C * (D / 4) && t < L) ? load4(v + ((int64_t)(ce.start + t) * H + h) * D + c)
                                           : f4(0.f);
   }
+  const float breg = (tid < C && tid < L) ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
 
-  // ---- 1. load g and k (rows t >= L are zero); clear A / Aq
-  for (int e = tid; e < C * (D / 4); e += NT) {
-    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-    float4 gg = f4(0.f), kk = f4(0.f);
-    if (t < L) {
-      const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
-      gg = load4(g + row);
-      kk = load4(k + row);
+  // ---- 1. stage g, k, q (rows t >= L are zero); clear A / Aq.  All loads
+  // of a thread are issued before its LDS stores.
+  {
+    constexpr int G4 = (C * (D / 4) + NT - 1) / NT;     // float4 groups of g
+    constexpr int K16 = (C * (D / IOV) + NT - 1) / NT;  // 16-byte groups of k, q
+    float4 gg[G4];
+    uint4 kk[K16], qq[K16];
+#pragma unroll
+    for (int i = 0; i < G4; ++i) {
+      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      gg[i] = (e < C * (D / 4) && t < L) ? load4(g + ((int64_t)(ce.start + t) * H + h) * D + c)
+                                          : f4(0.f);
     }
-    store4(sG + t * DP + c, gg);
-    store4(sK + t * DPIO + c, kk);
+#pragma unroll
+    for (int i = 0; i < K16; ++i) {
+      const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
+      const bool in = e < C * (D / IOV) && t < L;
+      const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
+      kk[i] = in ? *reinterpret_cast<const uint4*>(k + row) : make_uint4(0, 0, 0, 0);
+      qq[i] = in ? *reinterpret_cast<const uint4*>(q + row) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < G4; ++i) {
+      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iG(t, c)) = gg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < K16; ++i) {
+      const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
+      if (e < C * (D / IOV)) {
+        *reinterpret_cast<uint4*>(sK + iG(t, c)) = kk[i];
+        *reinterpret_cast<uint4*>(sQ + iG(t, c)) = qq[i];
+      }
+    }
+    for (int e = tid; e < C * C / 4; e += NT) reinterpret_cast<float4*>(sAA)[e] = f4(0.f);
   }
-  for (int e = tid; e < C * CP; e += NT) sAA[e] = 0.f;
-  if (tid < C) sB[tid] = tid < L ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
   __syncthreads();
 
   // ---- 2. chunk-local inclusive cumulative sum of g, per channel, in NSEG
@@ -381,113 +442,152 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       float acc = 0.f;
 #pragma unroll
       for (int r = 0; r < RPS; ++r) {
-        acc += sG[(seg * RPS + r) * DP + c];
-        sG[(seg * RPS + r) * DP + c] = acc;
+        acc += sG[iG(seg * RPS + r, c)];
+        sG[iG(seg * RPS + r, c)] = acc;
       }
     }
     __syncthreads();
     float offs = 0.f;
     if (seg < NSEG)
-      for (int s2 = 0; s2 < seg; ++s2) offs += sG[(s2 * RPS + RPS - 1) * DP + c];
+      for (int s2 = 0; s2 < seg; ++s2) offs += sG[iG(s2 * RPS + RPS - 1, c)];
     __syncthreads();
     if (seg < NSEG && seg > 0) {
 #pragma unroll
-      for (int r = 0; r < RPS; ++r) sG[(seg * RPS + r) * DP + c] += offs;
+      for (int r = 0; r < RPS; ++r) sG[iG(seg * RPS + r, c)] += offs;
     }
   }
   __syncthreads();
 
+  // Eight channels c0 .. c0 + 7 of row t, as fp32 (zero past D).
+  auto row_io8 = [&](const IO* base, int t, int c0, float (&x)[8]) {
+    if (c0 < D) {
+      if (sizeof(IO) == 2) {
+        lds8(reinterpret_cast<const bf16*>(base) + iG(t, c0), x);
+      } else {
+        const float4 a = *reinterpret_cast<const float4*>(base + iG(t, c0));
+        const float4 b = *reinterpret_cast<const float4*>(base + iG(t, c0) + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+  };
+  auto row_g8 = [&](int t, int c0, float (&x)[8]) {
+    if (c0 < D) {
+      lds8(sG + iG(t, c0), x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+  };
+
   // ---- 3. A (strictly lower, from k; stored transposed) and Aq (lower, from
-  // q) on the matrix cores, as work units (product P: 0 = A, 1 = Aq; row
-  // block I; column block J <= I).  For row t of block I:
-  //  - J < I: exp(G_t - G_j) = exp(G_t - G_r) exp(G_r - G_j) through the
-  //    block's first row r, both factors <= 1;
-  //  - J = I: pairs in different 4-token sub-blocks factor through the first
-  //    token r' of t's sub-block.  That is three products (rows of sub-block
-  //    s = 1..3 against columns before r') accumulated into one tile; rows of
-  //    other sub-blocks and columns at or past r' contribute zero.
-  // Pairs inside one 4-token sub-block (and the diagonal of Aq) follow
-  // elementwise.  Wave w takes the diagonal unit (P, I) = (w / 4, w % 4) and
-  // off-diagonal units w, w + 8, ...
+  // q) on the matrix cores.  Lane (lg, lr) of a unit owns row t = 16 I + lr
+  // and channels 32 kt + 8 lg + j.  Both products share every exponential.
+  //  - Off-diagonal blocks (J < I): exp(G_t - G_j) = exp(G_t - G_r)
+  //    exp(G_r - G_j) through the block's first row r = 16 I, both <= 1.
+  //  - Diagonal block: pairs in different 4-token sub-blocks factor through
+  //    the first token r' of t's sub-block: three products (rows of
+  //    sub-block s = 1..3 against the columns before r') accumulate into one
+  //    tile.  Pairs inside one sub-block (and Aq's diagonal) follow in 3b.
   {
+    auto store_tile = [&](int I, int J, const f32x4& accA, const f32x4& accQ, bool diag) {
+      // keep, on the diagonal, rows of a later sub-block than the column only
+      const bool keep = !diag || (lg > (lr >> 2));
+      if (keep) {
+        // A[t][j] -> sAA[j][t] (t = 16 I + 4 lg + i, j = 16 J + lr)
+        *reinterpret_cast<f32x4*>(sAA + iA(16 * J + lr, 16 * I + 4 * lg)) = accA;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sAA[iA(16 * I + 4 * lg + i, 16 * J + lr)] = accQ[i];
+      }
+    };
     Frag zero;
 #pragma unroll
     for (int j = 0; j < 8; ++j) zero.hi[j] = zero.lo[j] = (bf16)0.f;
-    // row operand x_t[c] exp(G_t[c] - G_ref[c]) for the 8 channels of lane lg
-    auto row8 = [&](int P, int t, int kt, int ref, float (&o8)[8]) {
-      const int c0 = 32 * kt + 8 * lg;
-      if (c0 < D) {
-        float x8[8], gt[8], gr[8];
-        if (P == 0) lds8(sK + t * DPIO + c0, x8); else qrow8(t, c0, x8);
-        lds8(sG + t * DP + c0, gt);
-        lds8(sG + ref * DP + c0, gr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] = x8[j] * __expf(gt[j] - gr[j]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-      }
-    };
-    // column operand k_j[c] exp(G_ref[c] - G_j[c]) (zero when !on)
-    auto col8 = [&](int j, int kt, int ref, bool on, float (&o8)[8]) {
-      const int c0 = 32 * kt + 8 * lg;
-      if (c0 < D && on) {
-        float k8[8], gj[8], gr[8];
-        lds8(sK + j * DPIO + c0, k8);
-        lds8(sG + j * DP + c0, gj);
-        lds8(sG + ref * DP + c0, gr);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o8[i] = k8[i] * __expf(gr[i] - gj[i]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o8[i] = 0.f;
-      }
-    };
-    auto store_tile = [&](int P, int I, int J, const f32x4& acc, bool diag) {
-      if (diag && !(lg > (lr >> 2))) return;  // keep rows of a later sub-block only
-      if (P == 0)  // A[t][j] -> sAA[j][t]
-        *reinterpret_cast<f32x4*>(sAA + (16 * J + lr) * CP + 16 * I + 4 * lg) = acc;
-      else
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sAA[(16 * I + 4 * lg + i) * CP + 16 * J + lr] = acc[i];
-    };
-    // diagonal unit
-    {
-      const int P = w >> 2, I = w & 3;
-      if (I < NB) {
-        const int t = 16 * I + lr, sub = lr >> 2, rs = 16 * I + 4 * sub, jr = 16 * I + lr;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kt = 0; kt < KTD; ++kt) {
-          float ad[8];
-          row8(P, t, kt, rs, ad);
-          const Frag fad = split8(ad);
-#pragma unroll
-          for (int sb = 1; sb < 4; ++sb) {
-            float b8[8];
-            col8(jr, kt, 16 * I + 4 * sb, sub < sb, b8);
-            acc = mma3(acc, sub == sb ? fad : zero, split8(b8));
-          }
-        }
-        store_tile(P, I, I, acc, true);
-      }
-    }
-    // off-diagonal units: u -> (P, I, J), J < I
-    constexpr int NOFF = NB * (NB - 1) / 2;
-    for (int u = w; u < 2 * NOFF; u += NW) {
-      const int P = u / (NOFF > 0 ? NOFF : 1);
-      int I = 1, J = u % (NOFF > 0 ? NOFF : 1);
-      while (J >= I) { J -= I; ++I; }
-      const int t = 16 * I + lr, r = 16 * I, jr = 16 * J + lr;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+
+    if (w < NB) {
+      // diagonal unit, row block I = w
+      const int I = w, t = 16 * I + lr, sub = lr >> 2;
+      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kt = 0; kt < KTD; ++kt) {
-        float ao[8], b8[8];
-        row8(P, t, kt, r, ao);
-        col8(jr, kt, r, true, b8);
-        acc = mma3(acc, split8(ao), split8(b8));
+        const int c0 = 32 * kt + 8 * lg;
+        float k8[8], q8[8], g8[8];
+        row_io8(sK, t, c0, k8);
+        row_io8(sQ, t, c0, q8);
+        row_g8(t, c0, g8);
+        float ra[8], rq[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float e = __expf(g8[j] - bcast_quad0(g8[j]));  // G_t - G_r' <= 0
+          ra[j] = k8[j] * e;
+          rq[j] = q8[j] * e;
+        }
+        const Frag fa = split8(ra), fq = split8(rq);
+#pragma unroll
+        for (int sb = 1; sb < 4; ++sb) {
+          float b8[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            float gref;
+            if (sb == 1) gref = bcast_row<4>(g8[j]);
+            else if (sb == 2) gref = bcast_row<8>(g8[j]);
+            else gref = bcast_row<12>(g8[j]);
+            // column j = t of this lane, reference 16 I + 4 sb: G_ref - G_j <= 0
+            // when j lies before the reference; other columns are zero
+            b8[j] = sub < sb ? k8[j] * __expf(gref - g8[j]) : 0.f;
+          }
+          const Frag fb = split8(b8);
+          const bool mine = sub == sb;
+          accA = mma3(accA, mine ? fa : zero, fb);
+          accQ = mma3(accQ, mine ? fq : zero, fb);
+        }
       }
-      store_tile(P, I, J, acc, false);
+      store_tile(I, I, accA, accQ, true);
+    } else {
+      int I, J0, nJ;
+      offdiag_group<NB>(w - NB, I, J0, nJ);
+      if (nJ > 0) {
+        const int t = 16 * I + lr;
+        f32x4 accA[2], accQ[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) accA[u] = accQ[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KTD; ++kt) {
+          const int c0 = 32 * kt + 8 * lg;
+          float k8[8], q8[8], g8[8], gr[8], ra[8], rq[8];
+          row_io8(sK, t, c0, k8);
+          row_io8(sQ, t, c0, q8);
+          row_g8(t, c0, g8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            gr[j] = bcast_row<0>(g8[j]);  // G at r = 16 I
+            const float e = __expf(g8[j] - gr[j]);
+            ra[j] = k8[j] * e;
+            rq[j] = q8[j] * e;
+          }
+          const Frag fa = split8(ra), fq = split8(rq);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (u < nJ) {
+              const int jr = 16 * (J0 + u) + lr;
+              float kj[8], gj[8], b8[8];
+              row_io8(sK, jr, c0, kj);
+              row_g8(jr, c0, gj);
+#pragma unroll
+              for (int j = 0; j < 8; ++j) b8[j] = kj[j] * __expf(gr[j] - gj[j]);
+              const Frag fb = split8(b8);
+              accA[u] = mma3(accA[u], fa, fb);
+              accQ[u] = mma3(accQ[u], fq, fb);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          if (u < nJ) store_tile(I, J0 + u, accA[u], accQ[u], false);
+      }
     }
   }
   // ---- 3b. pairs inside one 4-token sub-block, elementwise; CG lanes per
@@ -502,9 +602,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
         for (int i = 0; i < CPG; ++i) {
           const int c = i * CG + cg, t = t0 + a2;
-          kk[a2][i] = to_f32(sK[t * DPIO + c]);
-          qq[a2][i] = t < L ? to_f32(q[((int64_t)(ce.start + t) * H + h) * D + c]) : 0.f;
-          gg[a2][i] = sG[t * DP + c];
+          kk[a2][i] = to_f32(sK[iG(t, c)]);
+          qq[a2][i] = to_f32(sQ[iG(t, c)]);
+          gg[a2][i] = sG[iG(t, c)];
         }
       float pa[6], pq[6], pd[4];
       int n = 0;
@@ -545,11 +645,11 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
         for (int a2 = 1; a2 < 4; ++a2)
 #pragma unroll
           for (int b2 = 0; b2 < a2; ++b2, ++n) {
-            sAA[(t0 + b2) * CP + t0 + a2] = pa[n];  // A transposed
-            sAA[(t0 + a2) * CP + t0 + b2] = pq[n];
+            sAA[iA(t0 + b2, t0 + a2)] = pa[n];  // A transposed
+            sAA[iA(t0 + a2, t0 + b2)] = pq[n];
           }
 #pragma unroll
-        for (int a2 = 0; a2 < 4; ++a2) sAA[(t0 + a2) * CP + t0 + a2] = pd[a2];
+        for (int a2 = 0; a2 < 4; ++a2) sAA[iA(t0 + a2, t0 + a2)] = pd[a2];
       }
     }
   }
@@ -558,25 +658,23 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   // ---- 4. state-independent operands of the state pass
   // (scale Q e^G) as A fragments [NB][KTD]
   for (int tile = w; tile < NB * KTD; tile += NW) {
-    const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr;
-    float x[8];
-    qrow8(t, 32 * kt + 8 * lg, x);
+    const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr, c0 = 32 * kt + 8 * lg;
+    float x[8], g8[8];
+    row_io8(sQ, t, c0, x);
+    row_g8(t, c0, g8);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = 32 * kt + 8 * lg + j;
-      x[j] = c < D ? scale * x[j] * __expf(sG[t * DP + c]) : 0.f;
-    }
+    for (int j = 0; j < 8; ++j) x[j] = scale * x[j] * __expf(g8[j]);
     store_frag(rec + Gm::Q_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
   // (K e^{G_C - G})^T as A fragments [MTD][KTC]: rows = channels
   for (int tile = w; tile < MTD * KTC; tile += NW) {
     const int mt = tile / KTC, kt = tile % KTC, c = 16 * mt + lr;
-    const float glast = sG[(C - 1) * DP + c];
+    const float glast = sG[iG(C - 1, c)];
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int t = 32 * kt + 8 * lg + j;
-      x[j] = t < C ? to_f32(sK[t * DPIO + c]) * __expf(glast - sG[t * DP + c]) : 0.f;
+      x[j] = t < C ? to_f32(sK[iG(t, c)]) * __expf(glast - sG[iG(t, c)]) : 0.f;
     }
     store_frag(rec + Gm::KT_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
@@ -587,18 +685,26 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = 32 * kt + 8 * lg + j;
-      x[j] = (jj < C && jj <= t) ? scale * sAA[t * CP + jj] : 0.f;
+      x[j] = (jj < C && jj <= t) ? scale * sAA[iA(t, jj)] : 0.f;
     }
     store_frag(rec + Gm::AQ_OFF + (size_t)tile * FRAG_BYTES, split8(x));
   }
-  if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[(C - 1) * DP + tid]);
-  __syncthreads();
+  if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[iG(C - 1, tid)]);
+  __syncthreads();  // q is dead: its space takes beta
 
-  // ---- 5. K e^G in place of G (G no longer needed)
-  for (int e = tid; e < C * D; e += NT) {
-    const int t = e / D, c = e % D;
-    sG[t * DP + c] = to_f32(sK[t * DPIO + c]) * __expf(sG[t * DP + c]);
+  // ---- 5. K e^G in place of G (G no longer needed); beta into LDS
+  if (tid < C) sB[tid] = breg;
+  for (int e = tid; e < C * (D / 4); e += NT) {
+    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
+    const float4 kk = load4(sK + iG(t, c));
+    float4 gg = *reinterpret_cast<const float4*>(sG + iG(t, c));
+    gg.x = kk.x * __expf(gg.x);
+    gg.y = kk.y * __expf(gg.y);
+    gg.z = kk.z * __expf(gg.z);
+    gg.w = kk.w * __expf(gg.w);
+    *reinterpret_cast<float4*>(sG + iG(t, c)) = gg;
   }
+  __syncthreads();
 
   // ---- 6. X = (I + B A)^-1, B A strictly lower (A read transposed from the
   // upper triangle of sAA, X written to the lower one): 16 x 16 diagonal
@@ -621,13 +727,13 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = p + 4 * i;
-        if (r > m) x[i] = fmaf(-bb[i] * sAA[(b0 + m) * CP + b0 + r], xm, x[i]);
+        if (r > m) x[i] = fmaf(-bb[i] * sAA[iA(b0 + m, b0 + r)], xm, x[i]);
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = p + 4 * i;
-      if (r >= cl) sAA[(b0 + r) * CP + b0 + cl] = x[i];
+      if (r >= cl) sAA[iA(b0 + r, b0 + cl)] = x[i];
     }
   }
   __syncthreads();  // also: k (step 5) is dead, its space becomes scratch
@@ -642,8 +748,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
           float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 16 * J; m < 16 * I; ++m) {
-            const float xm = (m >= 16 * J + cc) ? sAA[m * CP + 16 * J + cc] : 0.f;
-            acc[m & 3] = fmaf(sAA[m * CP + 16 * I + rr], xm, acc[m & 3]);
+            const float xm = (m >= 16 * J + cc) ? sAA[iA(m, 16 * J + cc)] : 0.f;
+            acc[m & 3] = fmaf(sAA[iA(m, 16 * I + rr)], xm, acc[m & 3]);
             if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
           }
           sY[(16 * J + rr) * 16 + cc] = br * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
@@ -656,11 +762,11 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
           float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int m = 0; m < 16; ++m) {
-            const float xm = (m <= rr) ? sAA[(16 * I + rr) * CP + 16 * I + m] : 0.f;
+            const float xm = (m <= rr) ? sAA[iA(16 * I + rr, 16 * I + m)] : 0.f;
             acc[m & 3] = fmaf(xm, sY[(16 * J + m) * 16 + cc], acc[m & 3]);
             if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
           }
-          sAA[(16 * I + rr) * CP + 16 * J + cc] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
+          sAA[iA(16 * I + rr, 16 * J + cc)] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
         }
       }
       __syncthreads();
@@ -675,7 +781,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int jj = 32 * kt + 8 * lg + j;
-      x[j] = (jj < C && jj <= t) ? sAA[t * CP + jj] * sB[jj] : 0.f;
+      x[j] = (jj < C && jj <= t) ? sAA[iA(t, jj)] * sB[jj] : 0.f;
     }
     const Frag f = split8(x);
     sMf[tile * 128 + l] = f.hi;
@@ -695,7 +801,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int jj = 32 * kt + 8 * lg + j;
-          b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
+          b8[j] = jj < C ? sG[iG(jj, 16 * nt + lr)] : 0.f;
         }
         fb[kt] = split8(b8);
       }
@@ -713,7 +819,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
             acc = mma3(acc, fa, fb[kt]);
           }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sW[(16 * m2 + 4 * lg + i) * DP + 16 * nt + lr] = acc[i];
+          for (int i = 0; i < 4; ++i) sW[iW(16 * m2 + 4 * lg + i, 16 * nt + lr)] = acc[i];
         }
       }
     }
@@ -721,11 +827,13 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     for (int tile = w; tile < 2 * KTD; tile += NW) {
       const int m2 = tile / KTD, kt = tile % KTD, mt = 2 * half + m2;
       if (mt < NB) {
+        const int c0 = 32 * kt + 8 * lg;
         float x[8];
+        if (c0 < D) {
+          lds8(sW + iW(16 * m2 + lr, c0), x);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int c = 32 * kt + 8 * lg + j;
-          x[j] = c < D ? sW[(16 * m2 + lr) * DP + c] : 0.f;
+          for (int j = 0; j < 8; ++j) x[j] = 0.f;
         }
         store_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES, split8(x));
       }
@@ -737,7 +845,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-    if (e < C * (D / 4)) store4(sG + t * DP + c, vreg[i]);
+    if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iG(t, c)) = vreg[i];
   }
   __syncthreads();
 
@@ -751,7 +859,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int jj = 32 * kt + 8 * lg + j;
-        b8[j] = jj < C ? sG[jj * DP + 16 * nt + lr] : 0.f;
+        b8[j] = jj < C ? sG[iG(jj, 16 * nt + lr)] : 0.f;
       }
       fb[kt] = split8(b8);
     }
