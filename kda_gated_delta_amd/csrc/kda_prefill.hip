@@ -294,7 +294,7 @@ template <typename IO, int D, int C>
 struct IntraSmem {
   static constexpr int NB = C / 16, KTC = (C + 31) / 32;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
-  // sG [C][D] fp32 (groups of 8): G, then K e^G, then V
+  // sG [C][D] fp32: G (groups of 8), then K e^G and V (plain)
   static constexpr size_t G_BYTES = (size_t)C * D * 4;
   // sK [C][D] io (groups of 8): k; then the block-inverse scratch; then the
   // split fragments of M = X diag(beta)
@@ -303,9 +303,9 @@ struct IntraSmem {
                                          (size_t)3 * 256 * 4);
   // sQ [C][D] io (groups of 8): q; then beta
   static constexpr size_t Q_BYTES = cmax((size_t)C * D * sizeof(IO), (size_t)C * 4);
-  // sAA [C][C] fp32 (groups of 4): A transposed in the strict upper triangle
-  // and Aq in the lower one, Aq's triangle then reused for X; finally the
-  // 32-row staging of W ([32][D] fp32, groups of 8)
+  // sAA [C][C] fp32 (plain): A transposed in the strict upper triangle and
+  // Aq in the lower one, Aq's triangle then reused for X; finally the 32-row
+  // staging of W ([32][D] fp32, groups of 8)
   static constexpr size_t AA_BYTES = cmax((size_t)C * C * 4, (size_t)32 * D * 4);
   static constexpr size_t TOTAL = G_BYTES + K_BYTES + Q_BYTES + AA_BYTES;
 };
@@ -370,7 +370,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 
   // layouts
   auto iG = [](int t, int c) { return swz<D, 8>(t, c); };    // sG, sK, sQ
-  auto iA = [](int r, int c) { return swz<C, 4>(r, c); };    // sAA
+  auto iA = [](int r, int c) { return r * C + c; };          // sAA (plain)
+  auto iP = [](int t, int c) { return t * D + c; };          // sG from step 5 (plain)
   auto iW = [](int r, int c) { return swz<D, 8>(r, c); };    // sW
 
   const int chunk = blockIdx.x / H, h = blockIdx.x % H;
@@ -692,17 +693,28 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[iG(C - 1, tid)]);
   __syncthreads();  // q is dead: its space takes beta
 
-  // ---- 5. K e^G in place of G (G no longer needed); beta into LDS
+  // ---- 5. K e^G in place of G (G no longer needed), in the plain row-major
+  // layout that the column gathers of steps 8 and 10 read; beta into LDS
   if (tid < C) sB[tid] = breg;
-  for (int e = tid; e < C * (D / 4); e += NT) {
-    const int t = e / (D / 4), c = (e % (D / 4)) * 4;
-    const float4 kk = load4(sK + iG(t, c));
-    float4 gg = *reinterpret_cast<const float4*>(sG + iG(t, c));
-    gg.x = kk.x * __expf(gg.x);
-    gg.y = kk.y * __expf(gg.y);
-    gg.z = kk.z * __expf(gg.z);
-    gg.w = kk.w * __expf(gg.w);
-    *reinterpret_cast<float4*>(sG + iG(t, c)) = gg;
+  {
+    constexpr int G4 = (C * (D / 4) + NT - 1) / NT;
+    float4 ke[G4];
+#pragma unroll
+    for (int i = 0; i < G4; ++i) {
+      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      if (e < C * (D / 4)) {
+        const float4 kk = load4(sK + iG(t, c));
+        const float4 gg = *reinterpret_cast<const float4*>(sG + iG(t, c));
+        ke[i] = make_float4(kk.x * __expf(gg.x), kk.y * __expf(gg.y), kk.z * __expf(gg.z),
+                            kk.w * __expf(gg.w));
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < G4; ++i) {
+      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iP(t, c)) = ke[i];
+    }
   }
   __syncthreads();
 
@@ -801,7 +813,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int jj = 32 * kt + 8 * lg + j;
-          b8[j] = jj < C ? sG[iG(jj, 16 * nt + lr)] : 0.f;
+          b8[j] = jj < C ? sG[iP(jj, 16 * nt + lr)] : 0.f;
         }
         fb[kt] = split8(b8);
       }
@@ -845,7 +857,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-    if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iG(t, c)) = vreg[i];
+    if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iP(t, c)) = vreg[i];
   }
   __syncthreads();
 
@@ -859,7 +871,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int jj = 32 * kt + 8 * lg + j;
-        b8[j] = jj < C ? sG[iG(jj, 16 * nt + lr)] : 0.f;
+        b8[j] = jj < C ? sG[iP(jj, 16 * nt + lr)] : 0.f;
       }
       fb[kt] = split8(b8);
     }
