@@ -3,7 +3,8 @@
 One step = gate prep + chunkwise prefill of the packed varlen batch of four
 sequences {512, 1024, 2048, 4096} (H=32, K=V=128, bf16 q/k/v, fp32 gates and
 states, chunk 64), inputs resident in HBM.  ``value`` is prefill tokens/s of
-that step.  The same run also measures, each on its own workload:
+that step; the single kda_chunk_prefill_gated call (gate evaluated inside the
+prefill) is timed beside it.  The same run also measures, each on its own workload:
   decode  - 256 single-token requests on a 512-slot fp32 state pool
             (tokens/s and state GB/s against HBM peak);
   verify  - 64 requests x 8 draft tokens on a 128-slot pool;
@@ -153,13 +154,20 @@ def bench_prefill(steps, warmup):
         gate()
         prefill()
 
+    def step_gated():  # the gate applied inside the prefill: g and beta never hit HBM
+        kda.kda_chunk_prefill_gated(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
+                                    t["dt_bias"], t["cu"], scale, h0=t["h0"], chunk=C, o=o,
+                                    ht=ht, workspace=ws)
+
     ms_step = _time(step, steps, warmup)
+    ms_step_gated = _time(step_gated, steps, warmup)
     ms_gate = _time(gate, steps, warmup)
     ms_prefill = _time(prefill, steps, warmup)
     kernels = kernel_times(t, g, beta, o, ht, ws, scale, C, steps)
     pb = prefill_bytes(T, N, H, K, V)
     gb = gate_bytes(T, H, K)
-    return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_gate=ms_gate,
+    return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_step_gated=ms_step_gated,
+                ms_gate=ms_gate,
                 ms_prefill=ms_prefill, prefill_bytes=pb, gate_bytes=gb,
                 intra_bytes=intra_bytes(T, H, K, V), state_bytes=state_bytes(T, N, H, K, V),
                 kernels=kernels, flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
@@ -385,6 +393,7 @@ def main():
                    "global_batch": p["N"], "seq_len": p["T"], "parallelism": "none"},
         "roofline": roofline(p),
         "prefill": {"ms": p["ms_prefill"], "ms_gate": p["ms_gate"],
+                    "ms_step_gated_prefill": p["ms_step_gated"],
                     "kernel_ms": p["kernels"],
                     "tokens_per_s": p["T"] / (p["ms_prefill"] * 1e-3),
                     "algorithmic_bytes": p["prefill_bytes"],

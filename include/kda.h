@@ -137,6 +137,28 @@ kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
                                     void* const* marks);
 
 /*
+ * Chunkwise varlen prefill with the gate applied inside (tutorial, sections
+ * "Gated DeltaNet" and "KDA" for the gate, "两种计算形态" for the chunk form).
+ * Same as kda_gate_prep followed by kda_chunk_prefill, without g and beta
+ * ever being written to memory; the gate is evaluated by the same device
+ * code as kda_gate_prep, so the results are those of the two-call sequence.
+ *   a [T, H, K] fp32, b [T, H] fp32: raw gate inputs
+ *   A_log [H] fp32, dt_bias [H, K] fp32 or NULL, lower_bound: as in
+ *     kda_gate_prep (0 = softplus gate, < 0 = safe gate)
+ * Every other argument, the workspace and the errors are those of
+ * kda_chunk_prefill; additionally A_log must not be NULL when T > 0.
+ */
+kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,
+                                   const void* v, const float* a, const float* b,
+                                   const float* A_log, const float* dt_bias,
+                                   float lower_bound, const int32_t* cu_seqlens,
+                                   int32_t N, int64_t T, int32_t H, int32_t K,
+                                   int32_t V, int32_t chunk, float scale,
+                                   const float* h0, float* ht, void* o,
+                                   void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Single-token decode on a slot-indexed state pool, updated in place
  * (tutorial, section "两种计算形态": the recurrent kernel rewrites the pool
  * state; ReplaySSM analysis, section 3.6: a negative slot marks a padding row).

@@ -52,6 +52,10 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_prefill.restype = ctypes.c_int
     L.kda_chunk_prefill_marked.argtypes = L.kda_chunk_prefill.argtypes + [vp]
     L.kda_chunk_prefill_marked.restype = ctypes.c_int
+    L.kda_chunk_prefill_gated.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, f32, vp,
+                                          i32, i64, i32, i32, i32, i32, f32, vp, vp, vp, vp,
+                                          sz, vp]
+    L.kda_chunk_prefill_gated.restype = ctypes.c_int
     L.kda_recurrent_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64,
                                        vp, i32, i32, i32, i32, vp, vp]
     L.kda_recurrent_decode.restype = ctypes.c_int
@@ -63,8 +67,8 @@ def lib() -> ctypes.CDLL:
 
 
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
-            "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_recurrent_decode",
-            "kda_verify")
+            "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
+            "kda_recurrent_decode", "kda_verify")
 
 
 def status_string(status: int) -> str:
@@ -155,8 +159,26 @@ def kda_chunk_prefill_marked(marks, q, k, v, g, beta, cu_seqlens, scale: float, 
                     scale, h0, output_final_state, chunk, o, ht, workspace)
 
 
+def kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens, scale: float,
+                            lower_bound: float = 0.0, h0=None,
+                            output_final_state: bool = True, chunk: int = 64, o=None,
+                            ht=None, workspace=None):
+    """kda_gate_prep + kda_chunk_prefill in one call: a [T,H,K] and b [T,H]
+    are the raw gate inputs (A_log [H], dt_bias [H,K] or None)."""
+    T, H, K = q.shape
+    dev = q.device
+    _need(a, "a", torch.float32, (T, H, K), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (H, K), dev)
+    return _prefill("kda_chunk_prefill_gated", None, q, k, v, a, b, cu_seqlens, scale, h0,
+                    output_final_state, chunk, o, ht, workspace,
+                    gate=(A_log, dt_bias, float(lower_bound)))
+
+
 def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_state,
-             chunk, o, ht, workspace):
+             chunk, o, ht, workspace, gate=None):
     T, H, K = q.shape
     V = v.shape[2]
     dev = q.device
@@ -182,7 +204,13 @@ def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_st
     args = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T,
             H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace),
             workspace.numel(), _stream(dev)]
-    if marks is None:
+    if gate is not None:
+        A_log, dt_bias, lb = gate
+        gargs = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
+                 lb, _ptr(cu_seqlens), N, T, H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht),
+                 _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)]
+        _check(fn, lib().kda_chunk_prefill_gated(*gargs))
+    elif marks is None:
         _check(fn, lib().kda_chunk_prefill(*args))
     else:
         arr = (ctypes.c_void_p * 4)(*[m.cuda_event for m in marks])

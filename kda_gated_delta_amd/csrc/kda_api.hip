@@ -24,7 +24,9 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            int32_t N, int64_t T, int32_t H, int32_t K, int32_t V,
                            int32_t chunk, float scale, const float* h0, float* ht, void* o,
                            void* workspace, size_t workspace_bytes, void* stream,
-                           void* const* marks) {
+                           void* const* marks, int gate_mode = 0,
+                           const float* A_log = nullptr, const float* dt_bias = nullptr,
+                           float lower_bound = 0.f) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -39,8 +41,11 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
   const size_t need = kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u))
     return KDA_ERR_WORKSPACE;
+  if (gate_mode != 0 && T > 0 && (!A_log || (dt_bias && !aligned16(dt_bias))))
+    return KDA_ERR_INVALID_ARGUMENT;
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
-                     chunk, scale, h0, ht, o, workspace, workspace_bytes, marks};
+                     chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
+                     gate_mode, A_log, dt_bias, lower_bound};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -102,6 +107,19 @@ kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
     return KDA_ERR_INVALID_ARGUMENT;
   return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale,
                          h0, ht, o, workspace, workspace_bytes, stream, marks);
+}
+
+kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,
+                                   const void* v, const float* a, const float* b,
+                                   const float* A_log, const float* dt_bias,
+                                   float lower_bound, const int32_t* cu_seqlens, int32_t N,
+                                   int64_t T, int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                   float scale, const float* h0, float* ht, void* o,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (!(lower_bound <= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  return prefill_checked(io, q, k, v, a, b, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, stream, nullptr,
+                         lower_bound < 0.f ? 2 : 1, A_log, dt_bias, lower_bound);
 }
 
 kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,

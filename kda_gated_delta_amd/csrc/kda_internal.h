@@ -45,6 +45,11 @@ struct PrefillArgs {
   // Optional timing marks (hipEvent_t): recorded before the plan, intra and
   // state kernels and after the state kernel; nullptr for none.
   void* const* marks;
+  // 0: g and beta are activated gates.  1: softplus gate, 2: safe gate; then
+  // g and beta point to the raw a [T, H, K] and b [T, H].
+  int gate_mode;
+  const float *A_log, *dt_bias;
+  float lower_bound;
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

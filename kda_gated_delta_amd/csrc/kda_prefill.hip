@@ -35,6 +35,7 @@
 // exponentials and the triangular inverse are fp32 on the vector ALUs.
 
 #include "kda_common.h"
+#include "kda_gate_math.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -352,7 +353,8 @@ template <typename IO, int D, int C>
 __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
-    const ChunkEntry* __restrict__ table, char* __restrict__ recs) {
+    const ChunkEntry* __restrict__ table, char* __restrict__ recs, int gate_mode,
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound) {
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
   constexpr int NT = NT_INTRA, NW = NT / 64;
@@ -393,7 +395,12 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     vreg[i] = (e < C * (D / 4) && t < L) ? load4(v + ((int64_t)(ce.start + t) * H + h) * D + c)
                                           : f4(0.f);
   }
-  const float breg = (tid < C && tid < L) ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
+  // gate_mode 0: g and beta are given.  1 (softplus gate) and 2 (safe gate):
+  // g and beta hold the raw inputs a and b, activated here with the gate
+  // kernel's own functions (the same values it would have written).
+  const float rate = gate_mode != 0 ? exp_split(A_log[h]) : 0.f;
+  float breg = (tid < C && tid < L) ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
+  if (gate_mode != 0 && tid < C && tid < L) breg = sigmoid_fast(breg);
 
   // ---- 1. stage g, k, q (rows t >= L are zero); clear A / Aq.  All loads
   // of a thread are issued before its LDS stores.
@@ -415,6 +422,22 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
       kk[i] = in ? *reinterpret_cast<const uint4*>(k + row) : make_uint4(0, 0, 0, 0);
       qq[i] = in ? *reinterpret_cast<const uint4*>(q + row) : make_uint4(0, 0, 0, 0);
+    }
+    if (gate_mode != 0) {
+#pragma unroll
+      for (int i = 0; i < G4; ++i) {
+        const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+        if (e < C * (D / 4) && t < L) {
+          float4 x = gg[i];
+          if (dt_bias) x = x + load4(dt_bias + h * D + c);
+          if (gate_mode == 2)
+            gg[i] = make_float4(gate1<true>(x.x, rate, lower_bound), gate1<true>(x.y, rate, lower_bound),
+                                gate1<true>(x.z, rate, lower_bound), gate1<true>(x.w, rate, lower_bound));
+          else
+            gg[i] = make_float4(gate1<false>(x.x, rate, lower_bound), gate1<false>(x.y, rate, lower_bound),
+                                gate1<false>(x.z, rate, lower_bound), gate1<false>(x.w, rate, lower_bound));
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < G4; ++i) {
@@ -1256,7 +1279,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   if (a.T > 0)
     hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
-                       (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs);
+                       (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs, a.gate_mode,
+                       a.A_log, a.dt_bias, a.lower_bound);
   if ((e = mark(2)) != hipSuccess) return e;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;

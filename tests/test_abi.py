@@ -119,6 +119,17 @@ def test_prefill_validation_and_workspace():
     bad[18] = ws - 1
     assert L.kda_chunk_prefill_marked(*bad, marks) == WORKSPACE
 
+    # the gated variant: a positive lower bound, a missing A_log
+    def gated(**kw):
+        return L.kda_chunk_prefill_gated(
+            1, P, P, P, P, P, kw.get("A_log", P), None, kw.get("lb", 0.0), P, 4,
+            kw.get("T", 7680), 32, 128, 128, kw.get("chunk", 64), 1.0, None, P, P,
+            kw.get("ws", P), ws, None)
+    assert gated(lb=0.5) == INVALID
+    assert gated(A_log=None) == INVALID
+    assert gated(chunk=48) == UNSUPPORTED
+    assert gated(ws=None) == WORKSPACE
+
 
 def test_binding_rejects_cpu_and_wrong_dtypes():
     import torch

@@ -216,3 +216,33 @@ def test_marked_prefill_equals_unmarked():
     assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
     for i in range(3):
         assert marks[i].elapsed_time(marks[i + 1]) > 0
+
+
+@pytest.mark.parametrize("lower_bound,with_bias,D,seqlens", [
+    (0.0, True, 128, [300, 77, 640]),
+    (-5.0, True, 128, [64, 1, 129]),
+    (0.0, False, 64, [40, 9, 0, 100]),
+])
+def test_gated_prefill_equals_gate_prep_then_prefill(lower_bound, with_bias, D, seqlens):
+    """The gate applied inside the prefill is the gate kernel's own: the
+    fused call reproduces gate prep followed by prefill bit for bit, and
+    both match the oracle."""
+    c = kda_synth.prefill_case(seqlens, 4, D, D, "bf16", seed=31, h0_std=0.02)
+    io = TORCH_IO["bf16"]
+    q, k, v = dev(c["q"], io), dev(c["k"], io), dev(c["v"], io)
+    a, b, A_log = dev(c["a"]), dev(c["b"]), dev(c["A_log"])
+    dt_bias = dev(c["dt_bias"]) if with_bias else None
+    cu, h0 = dev(c["cu"], torch.int32), dev(c["h0"])
+    scale = D ** -0.5
+    g, beta = kda.kda_gate_prep(a, b, A_log, dt_bias, lower_bound=lower_bound)
+    o1, ht1 = kda.kda_chunk_prefill(q, k, v, g, beta, cu, scale, h0=h0)
+    o2, ht2 = kda.kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu, scale,
+                                          lower_bound=lower_bound, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    g_ref, b_ref = oracle.gate(c["a"], c["b"], c["A_log"],
+                               c["dt_bias"] if with_bias else None, lower_bound)
+    g32, b32 = g_ref.astype(np.float32), b_ref.astype(np.float32)
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g32, b32, c["cu"], scale, c["h0"])
+    assert_io_output(host(o2), o_ref, "bf16", 1)
+    assert rel_err_blocks(host(ht2), ht_ref, 2) <= TOL["bf16"]
