@@ -1,10 +1,11 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-One step = gate prep + chunkwise prefill of the packed varlen batch of four
-sequences {512, 1024, 2048, 4096} (H=32, K=V=128, bf16 q/k/v, fp32 gates and
-states, chunk 64), inputs resident in HBM.  ``value`` is prefill tokens/s of
-that step; the single kda_chunk_prefill_gated call (gate evaluated inside the
-prefill) is timed beside it.  The same run also measures, each on its own workload:
+One step = gate activation + chunkwise prefill of the packed varlen batch of
+four sequences {512, 1024, 2048, 4096} (H=32, K=V=128, bf16 q/k/v, fp32 raw
+gate inputs and states, chunk 64), inputs resident in HBM, as one
+kda_chunk_prefill_gated call (the gate evaluated inside the prefill; the
+two-call sequence kda_gate_prep + kda_chunk_prefill is timed beside it).
+``value`` is prefill tokens/s of that step.  The same run also measures, each on its own workload:
   decode  - 256 single-token requests on a 512-slot fp32 state pool
             (tokens/s and state GB/s against HBM peak);
   verify  - 64 requests x 8 draft tokens on a 128-slot pool;
@@ -66,7 +67,8 @@ def prefill_bytes(T, N, H, K, V, io_bytes=2):
 
 def intra_bytes(T, H, K, V, io_bytes=2):
     """Algorithmic bytes the intra-chunk kernel must move: it is the only
-    reader of q, k, v, g and beta."""
+    reader of q, k, v and of the gate inputs (a and b, or the activated g and
+    beta: the same sizes)."""
     return T * H * ((2 * K + V) * io_bytes + 4 * K + 4)
 
 
@@ -150,40 +152,42 @@ def bench_prefill(steps, warmup):
         kda.kda_chunk_prefill(t["q"], t["k"], t["v"], g, beta, t["cu"], scale, h0=t["h0"],
                               chunk=C, o=o, ht=ht, workspace=ws)
 
-    def step():
-        gate()
-        prefill()
-
-    def step_gated():  # the gate applied inside the prefill: g and beta never hit HBM
+    def step():  # the gate applied inside the prefill: g and beta never hit HBM
         kda.kda_chunk_prefill_gated(t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
                                     t["dt_bias"], t["cu"], scale, h0=t["h0"], chunk=C, o=o,
                                     ht=ht, workspace=ws)
 
+    def step_two_calls():
+        gate()
+        prefill()
+
     ms_step = _time(step, steps, warmup)
-    ms_step_gated = _time(step_gated, steps, warmup)
+    ms_step_two_calls = _time(step_two_calls, steps, warmup)
     ms_gate = _time(gate, steps, warmup)
     ms_prefill = _time(prefill, steps, warmup)
-    kernels = kernel_times(t, g, beta, o, ht, ws, scale, C, steps)
+    kernels = kernel_times(t, o, ht, ws, scale, C, steps)
     pb = prefill_bytes(T, N, H, K, V)
     gb = gate_bytes(T, H, K)
-    return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_step_gated=ms_step_gated,
+    return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_step_two_calls=ms_step_two_calls,
                 ms_gate=ms_gate,
                 ms_prefill=ms_prefill, prefill_bytes=pb, gate_bytes=gb,
                 intra_bytes=intra_bytes(T, H, K, V), state_bytes=state_bytes(T, N, H, K, V),
                 kernels=kernels, flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
 
 
-def kernel_times(t, g, beta, o, ht, ws, scale, C, steps):
-    """Average duration (ms) of each of the prefill's three kernels, from HIP
-    events that kda_chunk_prefill_marked records between them on the launch
-    stream.  Before every call a 512 MiB buffer is overwritten (outside the
-    marks) so that no input is served from the 256 MB last-level cache."""
+def kernel_times(t, o, ht, ws, scale, C, steps):
+    """Average duration (ms) of each of the step's three kernels, from HIP
+    events that kda_chunk_prefill_marked (the gated call with marks) records
+    between them on the launch stream.  Before every call a 512 MiB buffer is
+    overwritten (outside the marks) so that no input is served from the
+    256 MB last-level cache."""
     flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     for m in marks:
         flush.zero_()
-        kda.kda_chunk_prefill_marked(m, t["q"], t["k"], t["v"], g, beta, t["cu"], scale,
-                                     h0=t["h0"], chunk=C, o=o, ht=ht, workspace=ws)
+        kda.kda_chunk_prefill_marked(m, t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
+                                     t["dt_bias"], t["cu"], scale, h0=t["h0"], chunk=C, o=o,
+                                     ht=ht, workspace=ws)
     torch.cuda.synchronize()
     names = ("plan", "intra", "state")
     return {n: sum(m[i].elapsed_time(m[i + 1]) for m in marks) / steps
@@ -389,11 +393,12 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "varlen_prefill_7680: 4 packed sequences {512,1024,2048,4096}, "
-                               "H=32, K=V=128, chunk 64, gate prep + prefill per step",
+                               "H=32, K=V=128, chunk 64, gate + prefill per step "
+                               "(kda_chunk_prefill_gated)",
                    "global_batch": p["N"], "seq_len": p["T"], "parallelism": "none"},
         "roofline": roofline(p),
         "prefill": {"ms": p["ms_prefill"], "ms_gate": p["ms_gate"],
-                    "ms_step_gated_prefill": p["ms_step_gated"],
+                    "ms_step_gate_prep_then_prefill": p["ms_step_two_calls"],
                     "kernel_ms": p["kernels"],
                     "tokens_per_s": p["T"] / (p["ms_prefill"] * 1e-3),
                     "algorithmic_bytes": p["prefill_bytes"],

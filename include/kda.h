@@ -116,27 +116,6 @@ kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
                              void* stream);
 
 /*
- * kda_chunk_prefill with kernel timing marks, for benchmarks and profilers.
- * Same arguments, work and results as kda_chunk_prefill; in addition it
- * records four caller-created HIP events (hipEvent_t passed as void*) on
- * `stream`: marks[0] before the chunk-table kernel, marks[1] before the
- * intra-chunk kernel, marks[2] before the inter-chunk state kernel and
- * marks[3] after it, so that the elapsed time between consecutive marks is
- * one kernel's duration.  A NULL `marks` or a NULL entry returns
- * KDA_ERR_INVALID_ARGUMENT with nothing enqueued; a failed event record
- * returns KDA_ERR_LAUNCH.
- */
-kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
-                                    const void* v, const float* g,
-                                    const float* beta,
-                                    const int32_t* cu_seqlens, int32_t N,
-                                    int64_t T, int32_t H, int32_t K, int32_t V,
-                                    int32_t chunk, float scale, const float* h0,
-                                    float* ht, void* o, void* workspace,
-                                    size_t workspace_bytes, void* stream,
-                                    void* const* marks);
-
-/*
  * Chunkwise varlen prefill with the gate applied inside (tutorial, sections
  * "Gated DeltaNet" and "KDA" for the gate, "两种计算形态" for the chunk form).
  * Same as kda_gate_prep followed by kda_chunk_prefill, without g and beta
@@ -157,6 +136,27 @@ kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,
                                    const float* h0, float* ht, void* o,
                                    void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * kda_chunk_prefill_gated with kernel timing marks, for benchmarks and
+ * profilers.  Same arguments, work and results as kda_chunk_prefill_gated;
+ * in addition it records four caller-created HIP events (hipEvent_t passed
+ * as void*) on `stream`: marks[0] before the chunk-table kernel, marks[1]
+ * before the intra-chunk kernel, marks[2] before the inter-chunk state kernel
+ * and marks[3] after it, so that the elapsed time between consecutive marks
+ * is one kernel's duration.  A NULL `marks` or a NULL entry returns
+ * KDA_ERR_INVALID_ARGUMENT with nothing enqueued; a failed event record
+ * returns KDA_ERR_LAUNCH.
+ */
+kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
+                                    const void* v, const float* a, const float* b,
+                                    const float* A_log, const float* dt_bias,
+                                    float lower_bound, const int32_t* cu_seqlens,
+                                    int32_t N, int64_t T, int32_t H, int32_t K,
+                                    int32_t V, int32_t chunk, float scale,
+                                    const float* h0, float* ht, void* o,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* marks);
 
 /*
  * Single-token decode on a slot-indexed state pool, updated in place

@@ -50,12 +50,12 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i64,
                                     i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.kda_chunk_prefill.restype = ctypes.c_int
-    L.kda_chunk_prefill_marked.argtypes = L.kda_chunk_prefill.argtypes + [vp]
-    L.kda_chunk_prefill_marked.restype = ctypes.c_int
     L.kda_chunk_prefill_gated.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, f32, vp,
                                           i32, i64, i32, i32, i32, i32, f32, vp, vp, vp, vp,
                                           sz, vp]
     L.kda_chunk_prefill_gated.restype = ctypes.c_int
+    L.kda_chunk_prefill_marked.argtypes = L.kda_chunk_prefill_gated.argtypes + [vp]
+    L.kda_chunk_prefill_marked.restype = ctypes.c_int
     L.kda_recurrent_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64,
                                        vp, i32, i32, i32, i32, vp, vp]
     L.kda_recurrent_decode.restype = ctypes.c_int
@@ -144,21 +144,6 @@ def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
                     output_final_state, chunk, o, ht, workspace)
 
 
-def kda_chunk_prefill_marked(marks, q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
-                             output_final_state: bool = True, chunk: int = 64, o=None,
-                             ht=None, workspace=None):
-    """kda_chunk_prefill that also records the four ``torch.cuda.Event``s in
-    ``marks`` around its three kernels (chunk table, intra-chunk, state pass):
-    ``marks[i].elapsed_time(marks[i + 1])`` is kernel i's duration."""
-    if len(marks) != 4:
-        raise ValueError("marks: expected 4 events")
-    for m in marks:
-        if not m.cuda_event:  # events are created lazily by their first record
-            m.record()
-    return _prefill("kda_chunk_prefill_marked", marks, q, k, v, g, beta, cu_seqlens,
-                    scale, h0, output_final_state, chunk, o, ht, workspace)
-
-
 def kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens, scale: float,
                             lower_bound: float = 0.0, h0=None,
                             output_final_state: bool = True, chunk: int = 64, o=None,
@@ -173,6 +158,30 @@ def kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens, scale: fl
     if dt_bias is not None:
         _need(dt_bias, "dt_bias", torch.float32, (H, K), dev)
     return _prefill("kda_chunk_prefill_gated", None, q, k, v, a, b, cu_seqlens, scale, h0,
+                    output_final_state, chunk, o, ht, workspace,
+                    gate=(A_log, dt_bias, float(lower_bound)))
+
+
+def kda_chunk_prefill_marked(marks, q, k, v, a, b, A_log, dt_bias, cu_seqlens,
+                             scale: float, lower_bound: float = 0.0, h0=None,
+                             output_final_state: bool = True, chunk: int = 64, o=None,
+                             ht=None, workspace=None):
+    """kda_chunk_prefill_gated that also records the four ``torch.cuda.Event``s
+    in ``marks`` around its three kernels (chunk table, intra-chunk, state
+    pass): ``marks[i].elapsed_time(marks[i + 1])`` is kernel i's duration."""
+    if len(marks) != 4:
+        raise ValueError("marks: expected 4 events")
+    for m in marks:
+        if not m.cuda_event:  # events are created lazily by their first record
+            m.record()
+    T, H, K = q.shape
+    dev = q.device
+    _need(a, "a", torch.float32, (T, H, K), dev)
+    _need(b, "b", torch.float32, (T, H), dev)
+    _need(A_log, "A_log", torch.float32, (H,), dev)
+    if dt_bias is not None:
+        _need(dt_bias, "dt_bias", torch.float32, (H, K), dev)
+    return _prefill("kda_chunk_prefill_marked", marks, q, k, v, a, b, cu_seqlens, scale, h0,
                     output_final_state, chunk, o, ht, workspace,
                     gate=(A_log, dt_bias, float(lower_bound)))
 
@@ -209,12 +218,13 @@ def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_st
         gargs = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(A_log), _ptr(dt_bias),
                  lb, _ptr(cu_seqlens), N, T, H, K, V, chunk, float(scale), _ptr(h0), _ptr(ht),
                  _ptr(o), _ptr(workspace), workspace.numel(), _stream(dev)]
-        _check(fn, lib().kda_chunk_prefill_gated(*gargs))
-    elif marks is None:
-        _check(fn, lib().kda_chunk_prefill(*args))
+        if marks is None:
+            _check(fn, lib().kda_chunk_prefill_gated(*gargs))
+        else:
+            arr = (ctypes.c_void_p * 4)(*[m.cuda_event for m in marks])
+            _check(fn, lib().kda_chunk_prefill_marked(*gargs, arr))
     else:
-        arr = (ctypes.c_void_p * 4)(*[m.cuda_event for m in marks])
-        _check(fn, lib().kda_chunk_prefill_marked(*args, arr))
+        _check(fn, lib().kda_chunk_prefill(*args))
     return o, ht
 
 

@@ -97,16 +97,19 @@ kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
 }
 
 kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
-                                    const void* v, const float* g, const float* beta,
-                                    const int32_t* cu_seqlens, int32_t N, int64_t T,
-                                    int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                    const void* v, const float* a, const float* b,
+                                    const float* A_log, const float* dt_bias,
+                                    float lower_bound, const int32_t* cu_seqlens, int32_t N,
+                                    int64_t T, int32_t H, int32_t K, int32_t V, int32_t chunk,
                                     float scale, const float* h0, float* ht, void* o,
-                                    void* workspace, size_t workspace_bytes,
-                                    void* stream, void* const* marks) {
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    void* const* marks) {
   if (!marks || !marks[0] || !marks[1] || !marks[2] || !marks[3])
     return KDA_ERR_INVALID_ARGUMENT;
-  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale,
-                         h0, ht, o, workspace, workspace_bytes, stream, marks);
+  if (!(lower_bound <= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  return prefill_checked(io, q, k, v, a, b, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, stream, marks,
+                         lower_bound < 0.f ? 2 : 1, A_log, dt_bias, lower_bound);
 }
 
 kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,

@@ -106,18 +106,23 @@ def test_prefill_validation_and_workspace():
     assert call(ws_bytes=ws - 1) == WORKSPACE
     assert call(ws=ctypes.c_void_p(4096 + 64)) == WORKSPACE  # not 256-aligned
 
-    # the marked variant validates the same way, and needs four events
+    # the marked variant (of the gated call) validates the same way, and
+    # needs four events
     marks = (ctypes.c_void_p * 4)(P, P, P, P)
     no_mark = (ctypes.c_void_p * 4)(P, P, None, P)
-    base = [1, P, P, P, P, P, P, 4, 7680, 32, 128, 128, 64, 1.0, None, P, P, P, ws, None]
+    base = [1, P, P, P, P, P, P, None, 0.0, P, 4, 7680, 32, 128, 128, 64, 1.0, None, P, P, P,
+            ws, None]
     assert L.kda_chunk_prefill_marked(*base, None) == INVALID
     assert L.kda_chunk_prefill_marked(*base, no_mark) == INVALID
     bad = list(base)
-    bad[12] = 48
+    bad[15] = 48
     assert L.kda_chunk_prefill_marked(*bad, marks) == UNSUPPORTED
     bad = list(base)
-    bad[18] = ws - 1
+    bad[21] = ws - 1
     assert L.kda_chunk_prefill_marked(*bad, marks) == WORKSPACE
+    bad = list(base)
+    bad[8] = 0.5
+    assert L.kda_chunk_prefill_marked(*bad, marks) == INVALID
 
     # the gated variant: a positive lower bound, a missing A_log
     def gated(**kw):

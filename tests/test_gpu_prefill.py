@@ -203,15 +203,18 @@ def test_prefill_then_decodes_equals_longer_prefill():
 
 
 def test_marked_prefill_equals_unmarked():
-    """The timing-mark variant does the same work: bit-identical results, and
-    each mark pair brackets a kernel of positive duration."""
+    """The timing-mark variant does the same work as the gated call:
+    bit-identical results, and each mark pair brackets a kernel of positive
+    duration."""
     c = kda_synth.prefill_case([300, 77, 640], 4, 128, 128, "bf16", seed=21, regime="long")
-    t, g, beta = _inputs(c)
-    o1, ht1 = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"],
-                                    0.1, h0=t["h0"])
+    io = TORCH_IO["bf16"]
+    q, k, v = dev(c["q"], io), dev(c["k"], io), dev(c["v"], io)
+    a, b, A_log, dt_bias = dev(c["a"]), dev(c["b"]), dev(c["A_log"]), dev(c["dt_bias"])
+    cu, h0 = dev(c["cu"], torch.int32), dev(c["h0"])
+    o1, ht1 = kda.kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu, 0.1, h0=h0)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    o2, ht2 = kda.kda_chunk_prefill_marked(marks, t["q"], t["k"], t["v"], t["g"], t["beta"],
-                                           t["cu"], 0.1, h0=t["h0"])
+    o2, ht2 = kda.kda_chunk_prefill_marked(marks, q, k, v, a, b, A_log, dt_bias, cu, 0.1,
+                                           h0=h0)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
     for i in range(3):
