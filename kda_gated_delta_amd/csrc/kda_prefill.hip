@@ -38,6 +38,8 @@
 #include "kda_gate_math.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -335,6 +337,11 @@ __device__ __forceinline__ void offdiag_group(int idx, int& I, int& J0, int& nJ)
     }
 }
 
+// The intra pass keeps G log2(e) in LDS: e^{G_a - G_b} is then one base-2
+// exponential (v_exp_f32) of the difference of two stored values.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Lane-broadcast helpers (DPP, no LDS): row_newbcast:n gives every lane of a
 // 16-lane row the value of lane n of that row; quad_perm[0,0,0,0] gives every
 // lane of a 4-lane quad the value of the quad's first lane.
@@ -344,6 +351,20 @@ __device__ __forceinline__ float bcast_row(float x) {
 }
 __device__ __forceinline__ float bcast_quad0(float x) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x00, 0xf, 0xf, false));
+}
+
+// One step of a transposing reduction over a 16-lane row: the lane's first
+// 2 H sums are halved into H, keeping the upper half when `upper` (the index
+// bit of this step) is set and adding the partner lane's copy of the same
+// half, fetched by the DPP control CTRL.
+template <int H, int CTRL>
+__device__ __forceinline__ void butterfly_step(float (&v)[16], int upper) {
+#pragma unroll
+  for (int j = 0; j < H; ++j) {
+    const float send = upper ? v[j] : v[H + j];
+    const float keep = upper ? v[H + j] : v[j];
+    v[j] = keep + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(send), CTRL, 0xf, 0xf, false));
+  }
 }
 
 // LDS use (bf16 io, C = 64, D = 128: 80 KB, two workgroups per CU): see
@@ -383,67 +404,94 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   // records are head-major, so that one head's chain of chunks is contiguous
   const int ncb = gridDim.x / H;
   char* rec = recs + ((size_t)h * ncb + chunk) * Gm::REC;
+  // Record stores go through one buffer resource per tile: the lane's byte
+  // offset is their only per-lane operand and stays in one register for the
+  // whole kernel, so no register an outstanding store addresses is ever
+  // rewritten (which would make the wave wait for the store).  The scalar
+  // offset operand stays the constant 0: with a register there, the compiler
+  // lets the next instruction rewrite the store's data registers, and on this
+  // chip that corrupts the stored data.
   const int tid = threadIdx.x, l = tid & 63, lg = l >> 4, lr = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lane16 = (uint32_t)l * 16;
+  auto put_frag = [&](uint32_t off, const Frag& f) {
+    const auto r = buffer_rsrc(rec + off, FRAG_BYTES);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.hi), r, lane16, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.lo), r, lane16 + 1024, 0, 0);
+  };
 
-  // v is only needed in step 9 and beta from step 6: fetch them now
-  constexpr int VPT = (C * (D / 4) + NT - 1) / NT;  // float4 groups per thread
-  float4 vreg[VPT];
-#pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-    vreg[i] = (e < C * (D / 4) && t < L) ? load4(v + ((int64_t)(ce.start + t) * H + h) * D + c)
-                                          : f4(0.f);
-  }
+  // Rows t = 0 .. L-1 of this chunk and head of a [T, H, width] tensor as a
+  // buffer resource: element (t, c) sits at byte (t H width + c) esz, and
+  // rows at or past L fall outside the range and read as zero.  Every load
+  // below is unconditional, so a thread issues all of them back to back.
+  auto rows = [&](const void* base, int width, int esz) {
+    return buffer_rsrc(static_cast<const char*>(base) + ((size_t)ce.start * H + h) * width * esz,
+                       (uint32_t)L * (uint32_t)(H * width * esz));
+  };
   // gate_mode 0: g and beta are given.  1 (softplus gate) and 2 (safe gate):
   // g and beta hold the raw inputs a and b, activated here with the gate
-  // kernel's own functions (the same values it would have written).
+  // kernel's own functions (the same values it would have written); beta is
+  // activated in step 5, where it is first stored.
   const float rate = gate_mode != 0 ? exp_split(A_log[h]) : 0.f;
-  float breg = (tid < C && tid < L) ? beta[(int64_t)(ce.start + tid) * H + h] : 0.f;
-  if (gate_mode != 0 && tid < C && tid < L) breg = sigmoid_fast(breg);
+  const float braw = __builtin_bit_cast(
+      float, __builtin_amdgcn_raw_buffer_load_b32(rows(beta, 1, 4), (uint32_t)(tid * H * 4), 0, 0));
 
-  // ---- 1. stage g, k, q (rows t >= L are zero); clear A / Aq.  All loads
-  // of a thread are issued before its LDS stores.
+  // ---- 1. stage g, k, q (rows t >= L are zero) with the chunk-local
+  // inclusive cumulative sum of g folded in.  A thread holds RPT consecutive
+  // rows of one four-channel group of g and scans them in registers; the
+  // totals of the NU row groups pass through sAA (free until step 3), and
+  // each thread adds those of the groups before its own.  sG keeps G log2(e),
+  // so that every exponential below is a single base-2 exponential of a
+  // difference.  All loads of a thread are issued before any LDS access.
   {
-    constexpr int G4 = (C * (D / 4) + NT - 1) / NT;     // float4 groups of g
+    constexpr int GQ = D / 4;                    // four-channel groups per row
+    constexpr int NGR = NT / GQ;                 // row groups
+    constexpr int RPT = (C + NGR - 1) / NGR;     // rows per thread
+    constexpr int NU = (C + RPT - 1) / RPT;      // row groups that hold rows
     constexpr int K16 = (C * (D / IOV) + NT - 1) / NT;  // 16-byte groups of k, q
-    float4 gg[G4];
+    static_assert(NU * D * 4 <= (int)Sm::AA_BYTES, "group totals fit in sAA");
+    const int cq = tid % GQ, grp = tid / GQ, c4 = 4 * cq;
+    const auto rG = rows(g, D, 4), rK = rows(k, D, (int)sizeof(IO)), rQ = rows(q, D, (int)sizeof(IO));
+    const bool biased = gate_mode != 0 && dt_bias != nullptr;
+    const auto rB = buffer_rsrc(biased ? dt_bias + (size_t)h * D : g, biased ? D * 4 : 0);
+    float4 gg[RPT];
     uint4 kk[K16], qq[K16];
 #pragma unroll
-    for (int i = 0; i < G4; ++i) {
-      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-      gg[i] = (e < C * (D / 4) && t < L) ? load4(g + ((int64_t)(ce.start + t) * H + h) * D + c)
-                                          : f4(0.f);
+    for (int i = 0; i < RPT; ++i) {
+      const int t = grp * RPT + i;
+      const uint32_t off = (uint32_t)(t * H * D + c4) * 4;
+      gg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, 0));
     }
 #pragma unroll
     for (int i = 0; i < K16; ++i) {
       const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
-      const bool in = e < C * (D / IOV) && t < L;
-      const int64_t row = ((int64_t)(ce.start + t) * H + h) * D + c;
-      kk[i] = in ? *reinterpret_cast<const uint4*>(k + row) : make_uint4(0, 0, 0, 0);
-      qq[i] = in ? *reinterpret_cast<const uint4*>(q + row) : make_uint4(0, 0, 0, 0);
+      const uint32_t off = (uint32_t)(t * H * D + c) * (uint32_t)sizeof(IO);
+      kk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
+      qq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0));
     }
+    // dt_bias of this thread's channels (zero without one)
+    const float4 db = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)c4 * 4, 0, 0));
     if (gate_mode != 0) {
 #pragma unroll
-      for (int i = 0; i < G4; ++i) {
-        const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-        if (e < C * (D / 4) && t < L) {
-          float4 x = gg[i];
-          if (dt_bias) x = x + load4(dt_bias + h * D + c);
-          if (gate_mode == 2)
-            gg[i] = make_float4(gate1<true>(x.x, rate, lower_bound), gate1<true>(x.y, rate, lower_bound),
-                                gate1<true>(x.z, rate, lower_bound), gate1<true>(x.w, rate, lower_bound));
-          else
-            gg[i] = make_float4(gate1<false>(x.x, rate, lower_bound), gate1<false>(x.y, rate, lower_bound),
-                                gate1<false>(x.z, rate, lower_bound), gate1<false>(x.w, rate, lower_bound));
-        }
+      for (int i = 0; i < RPT; ++i) {
+        const float4 x = gg[i] + db;
+        float4 y;
+        if (gate_mode == 2)
+          y = make_float4(gate1<true>(x.x, rate, lower_bound), gate1<true>(x.y, rate, lower_bound),
+                          gate1<true>(x.z, rate, lower_bound), gate1<true>(x.w, rate, lower_bound));
+        else
+          y = make_float4(gate1<false>(x.x, rate, lower_bound), gate1<false>(x.y, rate, lower_bound),
+                          gate1<false>(x.z, rate, lower_bound), gate1<false>(x.w, rate, lower_bound));
+        gg[i] = grp * RPT + i < L ? y : f4(0.f);  // rows past the sequence keep g = 0
       }
     }
+    float4 acc = f4(0.f);
 #pragma unroll
-    for (int i = 0; i < G4; ++i) {
-      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-      if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iG(t, c)) = gg[i];
+    for (int i = 0; i < RPT; ++i) {
+      acc = fma4(LOG2E, gg[i], acc);
+      gg[i] = acc;
     }
+    if (grp < NU) *reinterpret_cast<float4*>(sAA + grp * D + c4) = acc;
 #pragma unroll
     for (int i = 0; i < K16; ++i) {
       const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
@@ -452,32 +500,13 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
         *reinterpret_cast<uint4*>(sQ + iG(t, c)) = qq[i];
       }
     }
-    for (int e = tid; e < C * C / 4; e += NT) reinterpret_cast<float4*>(sAA)[e] = f4(0.f);
-  }
-  __syncthreads();
-
-  // ---- 2. chunk-local inclusive cumulative sum of g, per channel, in NSEG
-  // row segments scanned in parallel and then offset
-  {
-    constexpr int NSEG = (NT / D < C / 4) ? NT / D : C / 4;
-    constexpr int RPS = C / NSEG;
-    const int c = tid % D, seg = tid / D;
-    if (seg < NSEG) {
-      float acc = 0.f;
-#pragma unroll
-      for (int r = 0; r < RPS; ++r) {
-        acc += sG[iG(seg * RPS + r, c)];
-        sG[iG(seg * RPS + r, c)] = acc;
-      }
-    }
     __syncthreads();
-    float offs = 0.f;
-    if (seg < NSEG)
-      for (int s2 = 0; s2 < seg; ++s2) offs += sG[iG(s2 * RPS + RPS - 1, c)];
-    __syncthreads();
-    if (seg < NSEG && seg > 0) {
+    if (grp < NU) {
+      float4 offs = f4(0.f);
+      for (int g2 = 0; g2 < grp; ++g2) offs = offs + *reinterpret_cast<const float4*>(sAA + g2 * D + c4);
 #pragma unroll
-      for (int r = 0; r < RPS; ++r) sG[iG(seg * RPS + r, c)] += offs;
+      for (int i = 0; i < RPT; ++i)
+        if (grp * RPT + i < C) *reinterpret_cast<float4*>(sG + iG(grp * RPT + i, c4)) = gg[i] + offs;
     }
   }
   __syncthreads();
@@ -514,8 +543,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   //    exp(G_r - G_j) through the block's first row r = 16 I, both <= 1.
   //  - Diagonal block: pairs in different 4-token sub-blocks factor through
   //    the first token r' of t's sub-block: three products (rows of
-  //    sub-block s = 1..3 against the columns before r') accumulate into one
-  //    tile.  Pairs inside one sub-block (and Aq's diagonal) follow in 3b.
+  //    sub-block s = 1..3 against the columns before r'), one tile each.
+  //    Pairs inside one sub-block (and Aq's diagonal) follow in 3b.
   {
     auto store_tile = [&](int I, int J, const f32x4& accA, const f32x4& accQ, bool diag) {
       // keep, on the diagonal, rows of a later sub-block than the column only
@@ -527,15 +556,17 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
         for (int i = 0; i < 4; ++i) sAA[iA(16 * I + 4 * lg + i, 16 * J + lr)] = accQ[i];
       }
     };
-    Frag zero;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) zero.hi[j] = zero.lo[j] = (bf16)0.f;
-
     if (w < NB) {
-      // diagonal unit, row block I = w
-      const int I = w, t = 16 * I + lr, sub = lr >> 2;
-      f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accQ = {0.f, 0.f, 0.f, 0.f};
+      // diagonal unit, row block I = w.  Product p (reference token
+      // 16 I + 4 p, p = 1..3) has its own accumulators; only the rows of
+      // sub-block p keep it, and of those only the columns before the
+      // reference, so nothing is masked: entries that mix other sub-blocks
+      // (or overflow) are never stored.
+      const int I = w, t = 16 * I + lr;
+      f32x4 accA[3], accQ[3];
 #pragma unroll
+      for (int p = 0; p < 3; ++p) accA[p] = accQ[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
       for (int kt = 0; kt < KTD; ++kt) {
         const int c0 = 32 * kt + 8 * lg;
         float k8[8], q8[8], g8[8];
@@ -545,7 +576,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
         float ra[8], rq[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float e = __expf(g8[j] - bcast_quad0(g8[j]));  // G_t - G_r' <= 0
+          const float e = ex2(g8[j] - bcast_quad0(g8[j]));  // G_t - G_r' <= 0
           ra[j] = k8[j] * e;
           rq[j] = q8[j] * e;
         }
@@ -559,17 +590,17 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
             if (sb == 1) gref = bcast_row<4>(g8[j]);
             else if (sb == 2) gref = bcast_row<8>(g8[j]);
             else gref = bcast_row<12>(g8[j]);
-            // column j = t of this lane, reference 16 I + 4 sb: G_ref - G_j <= 0
-            // when j lies before the reference; other columns are zero
-            b8[j] = sub < sb ? k8[j] * __expf(gref - g8[j]) : 0.f;
+            b8[j] = k8[j] * ex2(gref - g8[j]);  // G_ref - G_j <= 0 for kept columns
           }
           const Frag fb = split8(b8);
-          const bool mine = sub == sb;
-          accA = mma3(accA, mine ? fa : zero, fb);
-          accQ = mma3(accQ, mine ? fq : zero, fb);
+          accA[sb - 1] = mma3(accA[sb - 1], fa, fb);
+          accQ[sb - 1] = mma3(accQ[sb - 1], fq, fb);
         }
       }
-      store_tile(I, I, accA, accQ, true);
+      // accumulator rows 4 lg + i lie in sub-block lg (lg = 0 keeps nothing)
+      const f32x4 A = lg == 1 ? accA[0] : (lg == 2 ? accA[1] : accA[2]);
+      const f32x4 Q = lg == 1 ? accQ[0] : (lg == 2 ? accQ[1] : accQ[2]);
+      store_tile(I, I, A, Q, true);
     } else {
       int I, J0, nJ;
       offdiag_group<NB>(w - NB, I, J0, nJ);
@@ -581,14 +612,23 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
         for (int kt = 0; kt < KTD; ++kt) {
           const int c0 = 32 * kt + 8 * lg;
-          float k8[8], q8[8], g8[8], gr[8], ra[8], rq[8];
+          // every LDS read of this step first (a wave with one column block
+          // reads it twice), so that they are in flight together
+          float k8[8], q8[8], g8[8], kj[2][8], gj[2][8];
           row_io8(sK, t, c0, k8);
           row_io8(sQ, t, c0, q8);
           row_g8(t, c0, g8);
 #pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int jr = 16 * (J0 + (u < nJ ? u : 0)) + lr;
+            row_io8(sK, jr, c0, kj[u]);
+            row_g8(jr, c0, gj[u]);
+          }
+          float gr[8], ra[8], rq[8];
+#pragma unroll
           for (int j = 0; j < 8; ++j) {
             gr[j] = bcast_row<0>(g8[j]);  // G at r = 16 I
-            const float e = __expf(g8[j] - gr[j]);
+            const float e = ex2(g8[j] - gr[j]);
             ra[j] = k8[j] * e;
             rq[j] = q8[j] * e;
           }
@@ -596,12 +636,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             if (u < nJ) {
-              const int jr = 16 * (J0 + u) + lr;
-              float kj[8], gj[8], b8[8];
-              row_io8(sK, jr, c0, kj);
-              row_g8(jr, c0, gj);
+              float b8[8];
 #pragma unroll
-              for (int j = 0; j < 8; ++j) b8[j] = kj[j] * __expf(gr[j] - gj[j]);
+              for (int j = 0; j < 8; ++j) b8[j] = kj[u][j] * ex2(gr[j] - gj[u][j]);
               const Frag fb = split8(b8);
               accA[u] = mma3(accA[u], fa, fb);
               accQ[u] = mma3(accQ[u], fq, fb);
@@ -614,96 +651,112 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       }
     }
   }
-  // ---- 3b. pairs inside one 4-token sub-block, elementwise; CG lanes per
-  // sub-block, channels interleaved across them
-  {
-    constexpr int CG = D < 32 ? D : 32, CPG = D / CG, NSB = C / 4;
-    if (tid < NSB * CG) {
-      const int sb = tid / CG, cg = tid % CG, t0 = 4 * sb;
-      float kk[4][CPG], qq[4][CPG], gg[4][CPG];
+  // ---- 3b. pairs inside one 4-token sub-block (and Aq's diagonal),
+  // elementwise, on the diagonal waves (they finish step 3 first): one
+  // 16-lane row per sub-block, D / 16 consecutive channels per lane.  The 16
+  // sums of a sub-block (6 of A, 6 of Aq, 4 diagonal) are reduced over the
+  // row by a transposing butterfly: each step pairs lanes that differ in one
+  // more index bit (mirror, half mirror, xor 2, xor 1), and each lane keeps
+  // the half of its sums picked by that bit, so sum i ends in lane i.
+  if (w < NB) {
+    constexpr int CPL = D / 16;
+    const int sb = tid >> 4, r = tid & 15, t0 = 4 * sb, c0 = CPL * r;
+    float kk[4][CPL], qq[4][CPL], gg[4][CPL];
 #pragma unroll
-      for (int a2 = 0; a2 < 4; ++a2)
+    for (int a2 = 0; a2 < 4; ++a2) {
+      if constexpr (CPL == 8) {
+        row_io8(sK, t0 + a2, c0, kk[a2]);
+        row_io8(sQ, t0 + a2, c0, qq[a2]);
+        row_g8(t0 + a2, c0, gg[a2]);
+      } else {
 #pragma unroll
-        for (int i = 0; i < CPG; ++i) {
-          const int c = i * CG + cg, t = t0 + a2;
-          kk[a2][i] = to_f32(sK[iG(t, c)]);
-          qq[a2][i] = to_f32(sQ[iG(t, c)]);
-          gg[a2][i] = sG[iG(t, c)];
+        for (int i = 0; i < CPL; ++i) {
+          kk[a2][i] = to_f32(sK[iG(t0 + a2, c0 + i)]);
+          qq[a2][i] = to_f32(sQ[iG(t0 + a2, c0 + i)]);
+          gg[a2][i] = sG[iG(t0 + a2, c0 + i)];
         }
-      float pa[6], pq[6], pd[4];
-      int n = 0;
-#pragma unroll
-      for (int a2 = 1; a2 < 4; ++a2)
-#pragma unroll
-        for (int b2 = 0; b2 < a2; ++b2, ++n) {
-          float sa = 0.f, sq2 = 0.f;
-#pragma unroll
-          for (int i = 0; i < CPG; ++i) {
-            const float e = __expf(gg[a2][i] - gg[b2][i]) * kk[b2][i];
-            sa = fmaf(kk[a2][i], e, sa);
-            sq2 = fmaf(qq[a2][i], e, sq2);
-          }
-          pa[n] = sa;
-          pq[n] = sq2;
-        }
-#pragma unroll
-      for (int a2 = 0; a2 < 4; ++a2) {
-        float sd = 0.f;
-#pragma unroll
-        for (int i = 0; i < CPG; ++i) sd = fmaf(qq[a2][i], kk[a2][i], sd);
-        pd[a2] = sd;
-      }
-#pragma unroll
-      for (int m = 1; m < CG; m <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 6; ++i) {
-          pa[i] += __shfl_xor(pa[i], m, 64);
-          pq[i] += __shfl_xor(pq[i], m, 64);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pd[i] += __shfl_xor(pd[i], m, 64);
-      }
-      if (cg == 0) {
-        n = 0;
-#pragma unroll
-        for (int a2 = 1; a2 < 4; ++a2)
-#pragma unroll
-          for (int b2 = 0; b2 < a2; ++b2, ++n) {
-            sAA[iA(t0 + b2, t0 + a2)] = pa[n];  // A transposed
-            sAA[iA(t0 + a2, t0 + b2)] = pq[n];
-          }
-#pragma unroll
-        for (int a2 = 0; a2 < 4; ++a2) sAA[iA(t0 + a2, t0 + a2)] = pd[a2];
       }
     }
+    float v[16];
+    int n = 0;
+#pragma unroll
+    for (int a2 = 1; a2 < 4; ++a2)
+#pragma unroll
+      for (int b2 = 0; b2 < a2; ++b2, ++n) {
+        float sa = 0.f, sq2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < CPL; ++i) {
+          const float e = ex2(gg[a2][i] - gg[b2][i]) * kk[b2][i];
+          sa = fmaf(kk[a2][i], e, sa);
+          sq2 = fmaf(qq[a2][i], e, sq2);
+        }
+        v[n] = sa;
+        v[6 + n] = sq2;
+      }
+#pragma unroll
+    for (int a2 = 0; a2 < 4; ++a2) {
+      float sd = 0.f;
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) sd = fmaf(qq[a2][i], kk[a2][i], sd);
+      v[12 + a2] = sd;
+    }
+    butterfly_step<8, 0x140>(v, r & 8);  // partner 15 - r
+    butterfly_step<4, 0x141>(v, r & 4);  // partner (r & 8) + 7 - (r & 7)
+    butterfly_step<2, 0x4E>(v, r & 2);   // partner r ^ 2
+    butterfly_step<1, 0xB1>(v, r & 1);   // partner r ^ 1
+    // sum r: pairs n = r (A, stored transposed), n = r - 6 (Aq), diagonal r - 12
+    const int m = r < 6 ? r : r - 6;
+    const int a2 = 1 + (m >= 1) + (m >= 3), b2 = m - a2 * (a2 - 1) / 2;
+    const int idx = r < 6 ? iA(t0 + b2, t0 + a2)
+                          : (r < 12 ? iA(t0 + a2, t0 + b2) : iA(t0 + r - 12, t0 + r - 12));
+    sAA[idx] = v[0];
   }
   __syncthreads();
 
+  // Nothing is in flight on the vector memory counter here (every load so
+  // far has been consumed); saying so resets the compiler's conservative
+  // tracking, which would otherwise make the stores below wait for each other.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
   // ---- 4. state-independent operands of the state pass
   // (scale Q e^G) as A fragments [NB][KTD]
-  for (int tile = w; tile < NB * KTD; tile += NW) {
+  #pragma unroll
+  for (int it_ = 0; it_ < (NB * KTD + NW - 1) / NW; ++it_) {
+    const int tile = w + it_ * NW;
+    if (tile >= NB * KTD) break;
     const int mt = tile / KTD, kt = tile % KTD, t = 16 * mt + lr, c0 = 32 * kt + 8 * lg;
     float x[8], g8[8];
     row_io8(sQ, t, c0, x);
     row_g8(t, c0, g8);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = scale * x[j] * __expf(g8[j]);
-    store_frag(rec + Gm::Q_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+    for (int j = 0; j < 8; ++j) x[j] = scale * x[j] * ex2(g8[j]);
+    put_frag(Gm::Q_OFF + (uint32_t)tile * FRAG_BYTES, split8(x));
   }
   // (K e^{G_C - G})^T as A fragments [MTD][KTC]: rows = channels
-  for (int tile = w; tile < MTD * KTC; tile += NW) {
+  #pragma unroll
+  for (int it_ = 0; it_ < (MTD * KTC + NW - 1) / NW; ++it_) {
+    const int tile = w + it_ * NW;
+    if (tile >= MTD * KTC) break;
     const int mt = tile / KTC, kt = tile % KTC, c = 16 * mt + lr;
     const float glast = sG[iG(C - 1, c)];
+    // rows t0 + j share one swizzle base: the group index of (t0 + j, c) is
+    // that of (t0, c) with its low three bits flipped by j (t0 % 8 == 0)
+    constexpr int NG = D / 8;
+    const int t0 = 32 * kt + 8 * lg;
+    const int base = t0 * D + (c & 7), X = ((c >> 3) ^ t0) & (NG - 1);
     float x[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int t = 32 * kt + 8 * lg + j;
-      x[j] = t < C ? to_f32(sK[iG(t, c)]) * __expf(glast - sG[iG(t, c)]) : 0.f;
+      const int idx = base + j * D + (((X ^ j) & (NG - 1)) << 3);
+      x[j] = t0 + j < C ? to_f32(sK[idx]) * ex2(glast - sG[idx]) : 0.f;
     }
-    store_frag(rec + Gm::KT_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+    put_frag(Gm::KT_OFF + (uint32_t)tile * FRAG_BYTES, split8(x));
   }
   // scale Aq as A fragments [NB][KTC] (lower triangle of sAA)
-  for (int tile = w; tile < NB * KTC; tile += NW) {
+  #pragma unroll
+  for (int it_ = 0; it_ < (NB * KTC + NW - 1) / NW; ++it_) {
+    const int tile = w + it_ * NW;
+    if (tile >= NB * KTC) break;
     const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
@@ -711,14 +764,16 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       const int jj = 32 * kt + 8 * lg + j;
       x[j] = (jj < C && jj <= t) ? scale * sAA[iA(t, jj)] : 0.f;
     }
-    store_frag(rec + Gm::AQ_OFF + (size_t)tile * FRAG_BYTES, split8(x));
+    put_frag(Gm::AQ_OFF + (uint32_t)tile * FRAG_BYTES, split8(x));
   }
-  if (tid < D) reinterpret_cast<float*>(rec + Gm::GC_OFF)[tid] = __expf(sG[iG(C - 1, tid)]);
+  if (tid < D)
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(ex2(sG[iG(C - 1, tid)])),
+                                          buffer_rsrc(rec + Gm::GC_OFF, D * 4), (uint32_t)tid * 4, 0, 0);
   __syncthreads();  // q is dead: its space takes beta
 
   // ---- 5. K e^G in place of G (G no longer needed), in the plain row-major
   // layout that the column gathers of steps 8 and 10 read; beta into LDS
-  if (tid < C) sB[tid] = breg;
+  if (tid < C) sB[tid] = (gate_mode != 0 && tid < L) ? sigmoid_fast(braw) : braw;
   {
     constexpr int G4 = (C * (D / 4) + NT - 1) / NT;
     float4 ke[G4];
@@ -728,8 +783,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       if (e < C * (D / 4)) {
         const float4 kk = load4(sK + iG(t, c));
         const float4 gg = *reinterpret_cast<const float4*>(sG + iG(t, c));
-        ke[i] = make_float4(kk.x * __expf(gg.x), kk.y * __expf(gg.y), kk.z * __expf(gg.z),
-                            kk.w * __expf(gg.w));
+        ke[i] = make_float4(kk.x * ex2(gg.x), kk.y * ex2(gg.y), kk.z * ex2(gg.z),
+                            kk.w * ex2(gg.w));
       }
     }
     __syncthreads();
@@ -740,6 +795,25 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     }
   }
   __syncthreads();
+
+  // v is only needed in step 9: its loads are issued here, past the steps
+  // that need the most registers, and land while steps 6 - 8 run (raw io
+  // bits; converted where they are used)
+  constexpr int VPT = (C * (D / 4) + NT - 1) / NT;  // groups of four per thread
+  typedef typename std::conditional<sizeof(IO) == 2, uint2, float4>::type Raw4;
+  Raw4 vraw[VPT];
+  {
+    const auto rV = rows(v, D, (int)sizeof(IO));
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      const uint32_t off = (uint32_t)(t * H * D + c) * (uint32_t)sizeof(IO);
+      if constexpr (sizeof(IO) == 2)
+        vraw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rV, off, 0, 0));
+      else
+        vraw[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0));
+    }
+  }
 
   // ---- 6. X = (I + B A)^-1, B A strictly lower (A read transposed from the
   // upper triangle of sAA, X written to the lower one): 16 x 16 diagonal
@@ -810,7 +884,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 
   // ---- 7. M = X diag(beta) as split A fragments [NB][KTC] (over k), shared
   // by all waves
-  for (int tile = w; tile < NB * KTC; tile += NW) {
+  #pragma unroll
+  for (int it_ = 0; it_ < (NB * KTC + NW - 1) / NW; ++it_) {
+    const int tile = w + it_ * NW;
+    if (tile >= NB * KTC) break;
     const int mt = tile / KTC, kt = tile % KTC, t = 16 * mt + lr;
     float x[8];
 #pragma unroll
@@ -828,7 +905,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   // written out as A fragments; a wave owns a 16-channel column tile and
   // splits its B fragments once
   for (int half = 0; half < (NB + 1) / 2; ++half) {
-    for (int nt = w; nt < MTD; nt += NW) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (MTD + NW - 1) / NW; ++it_) {
+      const int nt = w + it_ * NW;
+      if (nt >= MTD) break;
       Frag fb[KTC];
 #pragma unroll
       for (int kt = 0; kt < KTC; ++kt) {
@@ -859,7 +939,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       }
     }
     __syncthreads();
-    for (int tile = w; tile < 2 * KTD; tile += NW) {
+    #pragma unroll
+    for (int it_ = 0; it_ < (2 * KTD + NW - 1) / NW; ++it_) {
+      const int tile = w + it_ * NW;
+      if (tile >= 2 * KTD) break;
       const int m2 = tile / KTD, kt = tile % KTD, mt = 2 * half + m2;
       if (mt < NB) {
         const int c0 = 32 * kt + 8 * lg;
@@ -870,7 +953,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
           for (int j = 0; j < 8; ++j) x[j] = 0.f;
         }
-        store_frag(rec + Gm::W_OFF + (size_t)(mt * KTD + kt) * FRAG_BYTES, split8(x));
+        put_frag(Gm::W_OFF + (uint32_t)(mt * KTD + kt) * FRAG_BYTES, split8(x));
       }
     }
     __syncthreads();
@@ -880,13 +963,24 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
-    if (e < C * (D / 4)) *reinterpret_cast<float4*>(sG + iP(t, c)) = vreg[i];
+    if (e < C * (D / 4)) {
+      float4 x;
+      if constexpr (sizeof(IO) == 2)  // bf16 pairs: element 2j in the low half of word j
+        x = make_float4(__uint_as_float(vraw[i].x << 16), __uint_as_float(vraw[i].x & 0xffff0000u),
+                        __uint_as_float(vraw[i].y << 16), __uint_as_float(vraw[i].y & 0xffff0000u));
+      else
+        x = vraw[i];
+      *reinterpret_cast<float4*>(sG + iP(t, c)) = x;
+    }
   }
   __syncthreads();
 
   // ---- 10. U = M V, stored as accumulator tiles [NB][MTD].  A bf16 V is
   // exact in bf16, so its lo part is zero and that product is skipped.
-  for (int nt = w; nt < MTD; nt += NW) {
+  #pragma unroll
+  for (int it_ = 0; it_ < (MTD + NW - 1) / NW; ++it_) {
+    const int nt = w + it_ * NW;
+    if (nt >= MTD) break;
     Frag fb[KTC];
 #pragma unroll
     for (int kt = 0; kt < KTC; ++kt) {
@@ -914,7 +1008,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
           acc = mma3(acc, fa, fb[kt]);
         }
       }
-      *reinterpret_cast<f32x4*>(rec + Gm::U_OFF + (((size_t)mt * MTD + nt) * 64 + l) * 16) = acc;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(u32x4, acc), buffer_rsrc(rec + Gm::U_OFF + (size_t)(mt * MTD + nt) * 1024, 1024),
+          lane16, 0, 0);
     }
   }
 }
