@@ -60,13 +60,30 @@ struct Frag {
   bf16x8 hi, lo;
 };
 
+//
+// hi = bf16(x) (round to nearest even, two values per v_cvt_pk_bf16_f32) and
+// lo = bf16(x - hi).  x - hi is exact in fp32; it is taken as one v_dot2 of
+// the packed hi pair with (-1, 0) or (0, -1), plus x, which saves the
+// bf16 -> fp32 unpack.  The pair's other element enters as 0 * h: zero for
+// every finite h (an infinite h, from an overflowed x, makes both lo NaN).
+// The two multipliers are kept in scalar registers (materialised by asm):
+// the compiler would otherwise encode (-1, 0) as the inline constant -1.0,
+// which the hardware reads as the fp32 value, i.e. as the pair (0, -1).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ Frag split8(const float (&x)[8]) {
+  unsigned m0, m1;
+  asm("s_mov_b32 %0, 0x0000bf80" : "=s"(m0));  // (-1, 0)
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(m1));  // (0, -1)
   Frag f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const bf16 h = (bf16)x[j];
-    f.hi[j] = h;
-    f.lo[j] = (bf16)(x[j] - (float)h);
+  for (int p = 0; p < 4; ++p) {
+    const bf16x2 h = {(bf16)x[2 * p], (bf16)x[2 * p + 1]};
+    const float l0 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m0), x[2 * p], false);
+    const float l1 = __builtin_amdgcn_fdot2_f32_bf16(h, __builtin_bit_cast(bf16x2, m1), x[2 * p + 1], false);
+    f.hi[2 * p] = h[0];
+    f.hi[2 * p + 1] = h[1];
+    f.lo[2 * p] = (bf16)l0;
+    f.lo[2 * p + 1] = (bf16)l1;
   }
   return f;
 }
