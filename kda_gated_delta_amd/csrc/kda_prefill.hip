@@ -863,40 +863,48 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     }
   }
   __syncthreads();  // also: k (step 5) is dead, its space becomes scratch
-  {
-    const int rr = (tid >> 4) & 15, cc = tid & 15, half = tid >> 8;
+  // Block rows I = 1 .. NB - 1 of X on the matrix cores, block (I, J) on
+  // wave J < I:
+  //   Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ},   X_IJ = -X_II Y_J.
+  // (B A)[t][j] = beta_t A[t][j] is read from A's transpose in the upper
+  // triangle of sAA, X from the lower one (zero above the diagonal of X_JJ
+  // and X_II).  Y_J passes through the wave's own scratch slot to turn from
+  // the accumulator into the B-operand layout (one wave: no barrier).
 #pragma unroll
-    for (int I = 1; I < NB; ++I) {
+  for (int I = 1; I < NB; ++I) {
+    if (w < I) {
+      const int J = w;
+      const float bt = sB[16 * I + lr];
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int J = 0; J < I; ++J) {  // Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ}
-        if ((J & 1) == half) {
-          const float br = sB[16 * I + rr];
-          float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < 16 * NB; j0 += 32) {
+        const int jb = 16 * J + j0;
+        if (jb >= 16 * I) break;
+        float a8[8], b8[8];
 #pragma unroll
-          for (int m = 16 * J; m < 16 * I; ++m) {
-            const float xm = (m >= 16 * J + cc) ? sAA[iA(m, 16 * J + cc)] : 0.f;
-            acc[m & 3] = fmaf(sAA[iA(m, 16 * I + rr)], xm, acc[m & 3]);
-            if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-          }
-          sY[(16 * J + rr) * 16 + cc] = br * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+        for (int jj = 0; jj < 8; ++jj) {
+          const int j = jb + 8 * lg + jj;
+          const bool in = j < 16 * I;
+          a8[jj] = in ? bt * sAA[iA(j, 16 * I + lr)] : 0.f;
+          b8[jj] = (in && j >= 16 * J + lr) ? sAA[iA(j, 16 * J + lr)] : 0.f;
         }
+        y = mma3(y, split8(a8), split8(b8));
       }
-      __syncthreads();
+      float* yj = sY + w * 256;
 #pragma unroll
-      for (int J = 0; J < I; ++J) {  // X_IJ = -X_II Y_J
-        if ((J & 1) == half) {
-          float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < 4; ++i) yj[(4 * lg + i) * 16 + lr] = y[i];
+      float a8[8], b8[8];
 #pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            const float xm = (m <= rr) ? sAA[iA(16 * I + rr, 16 * I + m)] : 0.f;
-            acc[m & 3] = fmaf(xm, sY[(16 * J + m) * 16 + cc], acc[m & 3]);
-            if ((m & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-          }
-          sAA[iA(16 * I + rr, 16 * J + cc)] = -((acc[0] + acc[1]) + (acc[2] + acc[3]));
-        }
+      for (int jj = 0; jj < 8; ++jj) {
+        const int m = 8 * lg + jj;
+        a8[jj] = (lg < 2 && m <= lr) ? sAA[iA(16 * I + lr, 16 * I + m)] : 0.f;
+        b8[jj] = lg < 2 ? yj[m * 16 + lr] : 0.f;
       }
-      __syncthreads();
+      const f32x4 x = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, split8(a8), split8(b8));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sAA[iA(16 * I + 4 * lg + i, 16 * J + lr)] = -x[i];
     }
+    __syncthreads();
   }
 
   // ---- 7. M = X diag(beta) as split A fragments [NB][KTC] (over k), shared
