@@ -62,6 +62,17 @@ __device__ __forceinline__ float4 fma4(float s, float4 b, float4 a) {
 
 // Butterfly sum over the lanes whose index differs only in bits
 // [lo_mask, 32]; every participating lane ends with the same bits.
+// Four consecutive fp32 values with the non-temporal hint (streamed once:
+// the caches need not keep them).
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load4_nt(const float* p) {
+  const f32x4_nt y = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+  return make_float4(y[0], y[1], y[2], y[3]);
+}
+__device__ __forceinline__ void store4_nt(float* p, float4 x) {
+  __builtin_nontemporal_store(f32x4_nt{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4_nt*>(p));
+}
+
 __device__ __forceinline__ float xor_sum(float x, int lo_mask) {
   for (int m = lo_mask; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;

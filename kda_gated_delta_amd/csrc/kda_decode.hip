@@ -1,11 +1,13 @@
 // Recurrent decode and multi-token verify of the KDA gated delta rule.
 //
-// One workgroup per (request, head).  The head's K x V fp32 state is held in
-// registers: thread t owns the float4 column group cg = t % (V/4) of the rows
-// rg, rg + RG, rg + 2 RG, ... (rg = t / (V/4)), so each wave reads and writes
-// whole 512-byte state rows with 128-bit accesses and the state crosses HBM
-// exactly once in each direction.  The reductions over K (k.S', q.S' and
-// q.k) are a butterfly inside the wave plus one LDS exchange across waves.
+// One workgroup of up to 1024 threads per (request, head).  The head's
+// K x V fp32 state is held in registers: thread t owns the float4 column
+// group cg = t % (V/4) of the rows rg, rg + RG, rg + 2 RG, ... (rg = t /
+// (V/4)), so each wave reads and writes whole 512-byte state rows with
+// 128-bit non-temporal accesses, a thread holds only four of them (many
+// loads in flight per CU), and the state crosses HBM exactly once in each
+// direction.  The reductions over K (k.S', q.S' and q.k) are a butterfly
+// inside the wave, then an LDS exchange across waves in two levels.
 //
 // Per token ("Linear attention" tutorial, sections "Gated DeltaNet" and
 // "KDA：逐通道的遗忘门"):  S' = Diag(exp g) S;  v_hat = k S';
@@ -20,13 +22,18 @@
 namespace kda {
 namespace {
 
+// State columns per workgroup (all of them: whole 512-byte rows stream best).
+template <int V>
+constexpr int slice_cols() { return V; }
+
 template <int K, int V>
-struct StepShape {
-  static constexpr int NT = (K * V / 4 < 256) ? K * V / 4 : 256;  // threads
+struct StepShape {  // V: the columns one workgroup holds
+  static constexpr int NT = (K * V / 4 < 1024) ? K * V / 4 : 1024;  // threads
   static constexpr int CG = V / 4;     // float4 column groups per row
   static constexpr int RG = NT / CG;   // row groups
   static constexpr int RPT = K / RG;   // state rows per thread
   static constexpr int NW = NT / 64;   // waves
+  static constexpr int RED = NW * CG * 9 + CG * 9;  // reduction scratch (floats)
   static_assert(NT % 64 == 0 && RPT >= 1 && RG * RPT == K, "bad shape");
 };
 
@@ -37,7 +44,8 @@ struct Partials {
 };
 
 // Sums the partials of the threads sharing a column group.  red is an LDS
-// buffer of NW * CG * 9 floats; the caller synchronises before reuse.
+// buffer of RED floats (per-wave partials, then the column sums); the caller
+// synchronises before reuse.
 template <int K, int V>
 __device__ __forceinline__ Partials reduce_rows(Partials p, float* red) {
   typedef StepShape<K, V> Sh;
@@ -61,16 +69,34 @@ __device__ __forceinline__ Partials reduce_rows(Partials p, float* red) {
   }
   __syncthreads();
   Partials s;
-  s.vh = f4(0.f);
-  s.qs = f4(0.f);
-  s.qk = 0.f;
+  if (Sh::NW <= 4) {
+    s.vh = f4(0.f);
+    s.qs = f4(0.f);
+    s.qk = 0.f;
 #pragma unroll
-  for (int i = 0; i < Sh::NW; ++i) {
-    const float* src = red + (i * Sh::CG + cg) * 9;
-    s.vh = s.vh + make_float4(src[0], src[1], src[2], src[3]);
-    s.qs = s.qs + make_float4(src[4], src[5], src[6], src[7]);
-    s.qk += src[8];
+    for (int i = 0; i < Sh::NW; ++i) {
+      const float* src = red + (i * Sh::CG + cg) * 9;
+      s.vh = s.vh + make_float4(src[0], src[1], src[2], src[3]);
+      s.qs = s.qs + make_float4(src[4], src[5], src[6], src[7]);
+      s.qk += src[8];
+    }
+    return s;
   }
+  // many waves: CG * 9 threads each sum one value over the waves, then every
+  // thread reads the nine sums of its column group
+  float* sums = red + Sh::NW * Sh::CG * 9;
+  if (t < Sh::CG * 9) {
+    const int c = t / 9, j = t % 9;
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < Sh::NW; ++i) acc += red[(i * Sh::CG + c) * 9 + j];
+    sums[t] = acc;
+  }
+  __syncthreads();
+  const float* src = sums + cg * 9;
+  s.vh = make_float4(src[0], src[1], src[2], src[3]);
+  s.qs = make_float4(src[4], src[5], src[6], src[7]);
+  s.qk = src[8];
   return s;
 }
 
@@ -111,68 +137,73 @@ __device__ __forceinline__ float4 token_step(Rows<StepShape<K, V>::RPT>& st,
 }
 
 template <typename IO, int K, int V>
-__global__ __launch_bounds__((StepShape<K, V>::NT)) void decode_kernel(
+__global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, float* __restrict__ pool,
     const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o) {
-  typedef StepShape<K, V> Sh;
+  constexpr int VS = slice_cols<V>(), NS = V / VS;
+  typedef StepShape<K, VS> Sh;
   __shared__ float sq[K], sk[K], sa[K];
-  __shared__ float red[Sh::NW * Sh::CG * 9];
+  __shared__ float red[Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
-  const int r = blockIdx.x / H, h = blockIdx.x % H;
-  const int64_t rh = (int64_t)r * H + h;
+  const int64_t rh = blockIdx.x / NS;  // r * H + h
+  const int r = (int)(rh / H), h = (int)(rh % H);
+  const int c0 = (blockIdx.x % NS) * VS + 4 * cg;  // this thread's first state column
   const int64_t slot = slot_idx[r];
   if (slot < 0) {
-    if (rg == 0) store4(o + rh * V + 4 * cg, f4(0.f));
+    if (rg == 0) store4(o + rh * V + c0, f4(0.f));
     return;
   }
   float* S = pool + (slot * H + h) * (int64_t)(K * V);
   Rows<Sh::RPT> st;
   float4* s = st.s;
 #pragma unroll
-  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4(S + (rg + Sh::RG * i) * V + 4 * cg);
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S + (rg + Sh::RG * i) * V + c0);
   for (int c = t; c < K; c += Sh::NT) {
     sq[c] = to_f32(q[rh * K + c]);
     sk[c] = to_f32(k[rh * K + c]);
     sa[c] = expf(g[rh * K + c]);
   }
-  const float4 vv = load4(v + rh * V + 4 * cg);
+  const float4 vv = load4(v + rh * V + c0);
   const float b = beta[rh];
   __syncthreads();
-  const float4 oq = token_step<K, V>(st, sq, sk, sa, vv, b, red);
-  if (rg == 0) store4(o + rh * V + 4 * cg, scale * oq);
+  const float4 oq = token_step<K, VS>(st, sq, sk, sa, vv, b, red);
+  if (rg == 0) store4(o + rh * V + c0, scale * oq);
 #pragma unroll
-  for (int i = 0; i < Sh::RPT; ++i) store4(S + (rg + Sh::RG * i) * V + 4 * cg, s[i]);
+  for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
 }
 
 // Draft tokens are staged TVB at a time.
 constexpr int TVB = 8;
 
 template <typename IO, int K, int V>
-__global__ __launch_bounds__((StepShape<K, V>::NT)) void verify_kernel(
+__global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale,
     const float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
     int Tv, int H, float* __restrict__ inter, IO* __restrict__ o) {
-  typedef StepShape<K, V> Sh;
+  constexpr int VS = slice_cols<V>(), NS = V / VS;
+  typedef StepShape<K, VS> Sh;
   __shared__ float sq[TVB][K], sk[TVB][K], sa[TVB][K], sb[TVB];
-  __shared__ float red[2][Sh::NW * Sh::CG * 9];
+  __shared__ float red[2][Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
-  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int rh = blockIdx.x / NS;  // r * H + h
+  const int r = rh / H, h = rh % H;
+  const int c0 = (blockIdx.x % NS) * VS + 4 * cg;  // this thread's first state column
   const int64_t slot = slot_idx[r];
   if (slot < 0) {
     if (rg == 0)
       for (int s = 0; s < Tv; ++s)
-        store4(o + (((int64_t)r * Tv + s) * H + h) * V + 4 * cg, f4(0.f));
+        store4(o + (((int64_t)r * Tv + s) * H + h) * V + c0, f4(0.f));
     return;
   }
   const float* S0 = pool + (slot * H + h) * (int64_t)(K * V);
   Rows<Sh::RPT> st;
   float4* s = st.s;
 #pragma unroll
-  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4(S0 + (rg + Sh::RG * i) * V + 4 * cg);
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S0 + (rg + Sh::RG * i) * V + c0);
   int step = 0;
   for (int s0 = 0; s0 < Tv; s0 += TVB) {
     const int nb = (Tv - s0 < TVB) ? Tv - s0 : TVB;
@@ -188,19 +219,19 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) void verify_kernel(
     float4 vv[TVB];
 #pragma unroll
     for (int j = 0; j < TVB; ++j)
-      if (j < nb) vv[j] = load4(v + (((int64_t)r * Tv + s0 + j) * H + h) * V + 4 * cg);
+      if (j < nb) vv[j] = load4(v + (((int64_t)r * Tv + s0 + j) * H + h) * V + c0);
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < TVB; ++j) {
       if (j < nb) {
         const int64_t rsh = ((int64_t)r * Tv + s0 + j) * H + h;
-        const float4 oq = token_step<K, V>(st, sq[j], sk[j], sa[j], vv[j], sb[j],
-                                           red[step & 1]);
+        const float4 oq = token_step<K, VS>(st, sq[j], sk[j], sa[j], vv[j], sb[j],
+                                            red[step & 1]);
         ++step;
-        if (rg == 0) store4(o + rsh * V + 4 * cg, scale * oq);
+        if (rg == 0) store4(o + rsh * V + c0, scale * oq);
         float* I = inter + rsh * (int64_t)(K * V);
 #pragma unroll
-        for (int i = 0; i < Sh::RPT; ++i) store4(I + (rg + Sh::RG * i) * V + 4 * cg, s[i]);
+        for (int i = 0; i < Sh::RPT; ++i) store4_nt(I + (rg + Sh::RG * i) * V + c0, s[i]);
       }
     }
   }
@@ -211,8 +242,8 @@ hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* g, const float* beta, float scale,
                          float* pool, const int32_t* slot_idx, int B, int H,
                          void* o, hipStream_t stream) {
-  typedef StepShape<K, V> Sh;
-  hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)B * H), dim3(Sh::NT),
+  typedef StepShape<K, slice_cols<V>()> Sh;
+  hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)B * H * (V / slice_cols<V>())), dim3(Sh::NT),
                      0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
                      scale, pool, slot_idx, H, (IO*)o);
   return hipGetLastError();
@@ -224,8 +255,8 @@ hipError_t launch_verify(const void* q, const void* k, const void* v,
                          const float* pool, const int32_t* slot_idx, int B,
                          int Tv, int H, float* inter, void* o,
                          hipStream_t stream) {
-  typedef StepShape<K, V> Sh;
-  hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)B * H), dim3(Sh::NT),
+  typedef StepShape<K, slice_cols<V>()> Sh;
+  hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)B * H * (V / slice_cols<V>())), dim3(Sh::NT),
                      0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
                      scale, pool, slot_idx, Tv, H, inter, (IO*)o);
   return hipGetLastError();
