@@ -332,6 +332,10 @@ struct IntraSmem {
 
 constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
 
+// Cache policy of the intra kernel's streams (inputs read once, records
+// written once and read by the next kernel): the non-temporal hint.
+constexpr int NT_HINT = 2;
+
 // Off-diagonal work of A and Aq: wave NB + idx takes row block I and the
 // column blocks J0 .. J0 + nJ - 1 (at most two, sharing the row operand);
 // row blocks are dealt from the last one.
@@ -433,8 +437,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   const uint32_t lane16 = (uint32_t)l * 16;
   auto put_frag = [&](uint32_t off, const Frag& f) {
     const auto r = buffer_rsrc(rec + off, FRAG_BYTES);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.hi), r, lane16, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.lo), r, lane16 + 1024, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.hi), r, lane16, 0, NT_HINT);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.lo), r, lane16 + 1024, 0, NT_HINT);
   };
 
   // Rows t = 0 .. L-1 of this chunk and head of a [T, H, width] tensor as a
@@ -477,14 +481,14 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     for (int i = 0; i < RPT; ++i) {
       const int t = grp * RPT + i;
       const uint32_t off = (uint32_t)(t * H * D + c4) * 4;
-      gg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, 0));
+      gg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, NT_HINT));
     }
 #pragma unroll
     for (int i = 0; i < K16; ++i) {
       const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
       const uint32_t off = (uint32_t)(t * H * D + c) * (uint32_t)sizeof(IO);
-      kk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, 0));
-      qq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, 0));
+      kk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, NT_HINT));
+      qq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, NT_HINT));
     }
     // dt_bias of this thread's channels (zero without one)
     const float4 db = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)c4 * 4, 0, 0));
@@ -826,9 +830,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
       const uint32_t off = (uint32_t)(t * H * D + c) * (uint32_t)sizeof(IO);
       if constexpr (sizeof(IO) == 2)
-        vraw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rV, off, 0, 0));
+        vraw[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rV, off, 0, NT_HINT));
       else
-        vraw[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, 0));
+        vraw[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rV, off, 0, NT_HINT));
     }
   }
 
@@ -1035,7 +1039,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       }
       __builtin_amdgcn_raw_buffer_store_b128(
           __builtin_bit_cast(u32x4, acc), buffer_rsrc(rec + Gm::U_OFF + (size_t)(mt * MTD + nt) * 1024, 1024),
-          lane16, 0, 0);
+          lane16, 0, NT_HINT);
     }
   }
 }
