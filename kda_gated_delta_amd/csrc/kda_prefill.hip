@@ -227,17 +227,38 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   __shared__ int scan[NTHREADS];
   __shared__ int carry;
   __shared__ int bcount[33], bbase[33];
+  __shared__ int s_lo[NTHREADS], s_hi[NTHREADS];
   const int t = threadIdx.x;
+  // Clamped bounds and chunk count of sequence n.  A batch of at most
+  // NTHREADS sequences reads cu_seqlens once (thread t keeps sequence t);
+  // larger ones re-read it in each pass.
+  auto bounds = [&](int n, int& lo, int& hi) {
+    const int64_t a = cu[n], b = cu[n + 1];
+    lo = (int)(a < 0 ? 0 : (a > T ? T : a));
+    hi = (int)(b < lo ? lo : (b > T ? T : b));
+  };
+  const bool small = N <= NTHREADS;
+  int my_lo = 0, my_hi = 0;
+  if (small && t < N) bounds(t, my_lo, my_hi);
+  auto seq = [&](int n, int& lo, int& hi) {
+    if (small) {
+      lo = my_lo;
+      hi = my_hi;
+    } else {
+      bounds(n, lo, hi);
+    }
+  };
+  auto bucket_of = [](int nch) { return nch <= 0 ? 0 : 32 - __clz(nch); };
   if (t == 0) carry = 0;
+  if (t < 33) bcount[t] = 0;
   __syncthreads();
   for (int base = 0; base < N; base += NTHREADS) {
     const int n = base + t;
     int lo = 0, hi = 0, nch = 0;
     if (n < N) {
-      const int64_t a = cu[n], b = cu[n + 1];
-      lo = (int)(a < 0 ? 0 : (a > T ? T : a));
-      hi = (int)(b < lo ? lo : (b > T ? T : b));
+      seq(n, lo, hi);
       nch = (hi - lo + C - 1) / C;
+      atomicAdd(&bcount[bucket_of(nch)], 1);
     }
     scan[t] = nch;
     __syncthreads();
@@ -250,13 +271,39 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int first = carry + scan[t] - nch;
     if (n < N) {
       off[n] = first;
-      for (int j = 0; j < nch && first + j < ncb; ++j) {
+      if (!small) {
+        for (int j = 0; j < nch && first + j < ncb; ++j) {
+          ChunkEntry e;
+          e.seq = n;
+          e.start = lo + j * C;
+          e.len = (hi - e.start < C) ? hi - e.start : C;
+          e.pad = 0;
+          table[first + j] = e;
+        }
+      }
+    }
+    if (small) {
+      // all threads fill the table: entry i belongs to the sequence whose
+      // chunk range holds it (a search over the inclusive scan in LDS)
+      if (n < N) {
+        s_lo[t] = lo;
+        s_hi[t] = hi;
+      }
+      __syncthreads();
+      const int total = scan[N - 1];
+      for (int i = t; i < total && i < ncb; i += NTHREADS) {
+        int a = 0, b = N - 1;  // first m with scan[m] > i
+        while (a < b) {
+          const int m = (a + b) >> 1;
+          if (scan[m] > i) b = m; else a = m + 1;
+        }
+        const int first_a = scan[a] - ((s_hi[a] - s_lo[a] + C - 1) / C);
         ChunkEntry e;
-        e.seq = n;
-        e.start = lo + j * C;
-        e.len = (hi - e.start < C) ? hi - e.start : C;
+        e.seq = a;
+        e.start = s_lo[a] + (i - first_a) * C;
+        e.len = (s_hi[a] - e.start < C) ? s_hi[a] - e.start : C;
         e.pad = 0;
-        table[first + j] = e;
+        table[i] = e;
       }
     }
     __syncthreads();
@@ -267,17 +314,6 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   // Longest sequences first: order[] lists the sequences by descending
   // power-of-two bucket of their chunk count, so the state pass starts the
   // longest serial chains first.
-  if (t < 33) bcount[t] = 0;
-  __syncthreads();
-  auto bucket = [&](int n) {  // chunk count from the clamped bounds, as above
-    const int64_t a = cu[n], b = cu[n + 1];
-    const int lo = (int)(a < 0 ? 0 : (a > T ? T : a));
-    const int hi = (int)(b < lo ? lo : (b > T ? T : b));
-    const int nch = (hi - lo + C - 1) / C;
-    return nch <= 0 ? 0 : 32 - __clz(nch);
-  };
-  for (int n = t; n < N; n += NTHREADS) atomicAdd(&bcount[bucket(n)], 1);
-  __syncthreads();
   if (t == 0) {
     int acc = 0;
     for (int b = 32; b >= 0; --b) {
@@ -286,7 +322,11 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     }
   }
   __syncthreads();
-  for (int n = t; n < N; n += NTHREADS) order[atomicAdd(&bbase[bucket(n)], 1)] = n;
+  for (int n = t; n < N; n += NTHREADS) {
+    int lo, hi;
+    seq(n, lo, hi);
+    order[atomicAdd(&bbase[bucket_of((hi - lo + C - 1) / C)], 1)] = n;
+  }
   for (int64_t i = carry + t; i < ncb; i += NTHREADS) {
     ChunkEntry e;
     e.seq = 0;
