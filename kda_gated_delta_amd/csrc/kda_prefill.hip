@@ -360,7 +360,7 @@ struct IntraSmem {
   // split fragments of M = X diag(beta)
   static constexpr size_t K_BYTES = cmax(cmax((size_t)C * D * sizeof(IO),
                                               (size_t)NB * KTC * FRAG_BYTES),
-                                         (size_t)3 * 256 * 4);
+                                         (size_t)6 * 256 * 4);
   // sQ [C][D] io (groups of 8): q; then beta
   static constexpr size_t Q_BYTES = cmax((size_t)C * D * sizeof(IO), (size_t)C * 4);
   // sAA [C][C] fp32 (plain): A transposed in the strict upper triangle and
@@ -907,48 +907,98 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     }
   }
   __syncthreads();  // also: k (step 5) is dead, its space becomes scratch
-  // Block rows I = 1 .. NB - 1 of X on the matrix cores, block (I, J) on
-  // wave J < I:
-  //   Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ},   X_IJ = -X_II Y_J.
-  // (B A)[t][j] = beta_t A[t][j] is read from A's transpose in the upper
-  // triangle of sAA, X from the lower one (zero above the diagonal of X_JJ
-  // and X_II).  Y_J passes through the wave's own scratch slot to turn from
-  // the accumulator into the B-operand layout (one wave: no barrier).
+  // The off-diagonal blocks of X on the matrix cores.  (B A)[t][j] =
+  // beta_t A[t][j] is read from A's transpose in the upper triangle of sAA, X
+  // from the lower one (zero above the diagonal of a diagonal block).  An
+  // accumulator tile passes through LDS scratch (sY) to become a B operand.
+  // Helpers: the (B A) rows of block I against columns jb .. jb+31 of A
+  // (below jend), and the X columns of block J over the same rows.
+  auto ba_frag = [&](int I, int jb, int jend) {
+    const float bt = sB[16 * I + lr];
+    float a8[8];
 #pragma unroll
-  for (int I = 1; I < NB; ++I) {
-    if (w < I) {
-      const int J = w;
-      const float bt = sB[16 * I + lr];
-      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = jb + 8 * lg + jj;
+      a8[jj] = j < jend ? bt * sAA[iA(j, 16 * I + lr)] : 0.f;
+    }
+    return split8(a8);
+  };
+  auto x_frag = [&](int J, int jb, int jend) {
+    float b8[8];
 #pragma unroll
-      for (int j0 = 0; j0 < 16 * NB; j0 += 32) {
-        const int jb = 16 * J + j0;
-        if (jb >= 16 * I) break;
-        float a8[8], b8[8];
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = jb + 8 * lg + jj;
+      b8[jj] = (j < jend && j >= 16 * J + lr) ? sAA[iA(j, 16 * J + lr)] : 0.f;
+    }
+    return split8(b8);
+  };
+  // X_IJ = -X_II Y for the 16 x 16 tile Y held in accumulator layout
+  auto x_times = [&](int I, int J, const f32x4& y, float* scratch) {
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) {
-          const int j = jb + 8 * lg + jj;
-          const bool in = j < 16 * I;
-          a8[jj] = in ? bt * sAA[iA(j, 16 * I + lr)] : 0.f;
-          b8[jj] = (in && j >= 16 * J + lr) ? sAA[iA(j, 16 * J + lr)] : 0.f;
-        }
-        y = mma3(y, split8(a8), split8(b8));
-      }
-      float* yj = sY + w * 256;
+    for (int i = 0; i < 4; ++i) scratch[(4 * lg + i) * 16 + lr] = y[i];
+    float a8[8], b8[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) yj[(4 * lg + i) * 16 + lr] = y[i];
+    for (int jj = 0; jj < 8; ++jj) {
+      const int m = 8 * lg + jj;
+      a8[jj] = (lg < 2 && m <= lr) ? sAA[iA(16 * I + lr, 16 * I + m)] : 0.f;
+      b8[jj] = lg < 2 ? scratch[m * 16 + lr] : 0.f;
+    }
+    const f32x4 x = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, split8(a8), split8(b8));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sAA[iA(16 * I + 4 * lg + i, 16 * J + lr)] = -x[i];
+  };
+  if constexpr (NB == 4) {
+    // Two levels of 2 x 2 block inversion (4 products on the critical path):
+    //  A. X_10 and X_32: X_{I,I-1} = -X_II (B A)_{I,I-1} X_{I-1,I-1};
+    //  B. the lower-left 32 x 32 block: T = (B A)_{[23],[01]} X_{[01],[01]},
+    //     then X_{[23],[01]} = -X_{[23],[23]} T, one 16 x 16 tile per wave.
+    if (w < 2) {
+      const int I = 1 + 2 * w, J = I - 1;
+      const f32x4 y = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, ba_frag(I, 16 * J, 16 * I),
+                           x_frag(J, 16 * J, 16 * I));
+      x_times(I, J, y, sY + w * 256);
+    }
+    __syncthreads();
+    float* sT = sY + 512;  // T tiles (I - 2) * 2 + J
+    if (w < 4) {
+      const int I = 2 + (w >> 1), J = w & 1;
+      const f32x4 tt = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, ba_frag(I, 16 * J, 32), x_frag(J, 16 * J, 32));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sT[w * 256 + (4 * lg + i) * 16 + lr] = tt[i];
+    }
+    __syncthreads();
+    if (w < 4) {
+      const int I = 2 + (w >> 1), J = w & 1, t = 16 * I + lr;
       float a8[8], b8[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
-        const int m = 8 * lg + jj;
-        a8[jj] = (lg < 2 && m <= lr) ? sAA[iA(16 * I + lr, 16 * I + m)] : 0.f;
-        b8[jj] = lg < 2 ? yj[m * 16 + lr] : 0.f;
+        const int m = 32 + 8 * lg + jj;  // block K' = m / 16 of X_{I K'} and T_{K' J}
+        a8[jj] = m <= t ? sAA[iA(t, m)] : 0.f;
+        b8[jj] = sT[((m >> 4) - 2) * 512 + J * 256 + (m & 15) * 16 + lr];
       }
       const f32x4 x = mma3(f32x4{0.f, 0.f, 0.f, 0.f}, split8(a8), split8(b8));
 #pragma unroll
       for (int i = 0; i < 4; ++i) sAA[iA(16 * I + 4 * lg + i, 16 * J + lr)] = -x[i];
     }
     __syncthreads();
+  } else {
+    // block rows I = 1 .. NB - 1 in turn, block (I, J) on wave J < I:
+    //   Y_J = sum_{K=J}^{I-1} (B A)_{IK} X_{KJ},   X_IJ = -X_II Y_J
+#pragma unroll
+    for (int I = 1; I < NB; ++I) {
+      if (w < I) {
+        const int J = w;
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j0 = 0; j0 < 16 * NB; j0 += 32) {
+          const int jb = 16 * J + j0;
+          if (jb >= 16 * I) break;
+          y = mma3(y, ba_frag(I, jb, 16 * I), x_frag(J, jb, 16 * I));
+        }
+        x_times(I, J, y, sY + w * 256);
+      }
+      __syncthreads();
+    }
   }
 
   // ---- 7. M = X diag(beta) as split A fragments [NB][KTC] (over k), shared
