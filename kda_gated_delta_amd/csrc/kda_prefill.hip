@@ -1310,7 +1310,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
 
   auto process = [&](Ops& ops, int ch) {
     const __amdgpu_buffer_rsrc_t rn = rsrc_of(min(ch + 1, c_last - 1));
-    prefetch(ch);
     // -- 1. S^T (hi, lo) into LDS
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
@@ -1438,6 +1437,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
                                     c16 * (16 / sizeof(IO))) = val;
       }
     }
+    // the L2 prefetch goes last: the wave's wait counter drains in issue
+    // order, so a fetch of the next chunk's operands never waits for it
+    prefetch(ch);
   };
 
   // One operand set in registers: each part is refetched for chunk i+1 as
