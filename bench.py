@@ -41,11 +41,19 @@ def _dev(x, dtype=torch.float32):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
 
 
-def _time(fn, steps: int, warmup: int) -> float:
-    """Average milliseconds per call of fn over `steps` calls."""
+def _time(fn, steps: int, warmup: int, settle_s: float = 0.2) -> float:
+    """Average milliseconds per call of fn over `steps` calls.  The `warmup`
+    calls are followed by further untimed calls until `settle_s` seconds have
+    passed: the GPU's clocks take tens of milliseconds to rise from idle, and
+    a timed region that starts earlier measures that ramp, not the kernels."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
