@@ -41,7 +41,10 @@ def _dev(x, dtype=torch.float32):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda().to(dtype).contiguous()
 
 
-def _time(fn, steps: int, warmup: int, settle_s: float = 0.2) -> float:
+SETTLE_S = 0.2  # --settle
+
+
+def _time(fn, steps: int, warmup: int, settle_s: float | None = None) -> float:
     """Average milliseconds per call of fn over `steps` calls.  The `warmup`
     calls are followed by further untimed calls until `settle_s` seconds have
     passed: the GPU's clocks take tens of milliseconds to rise from idle, and
@@ -49,6 +52,7 @@ def _time(fn, steps: int, warmup: int, settle_s: float = 0.2) -> float:
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    settle_s = SETTLE_S if settle_s is None else settle_s
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < settle_s:
         for _ in range(10):
@@ -284,10 +288,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_varlen_7680_traffic.md")
 PREFILL_SOURCE = os.path.join(ROOT, "kda_gated_delta_amd", "csrc", "kda_prefill.hip")
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a copy kernel of known size),
-    or None when there is none or the kernel source has changed since."""
+def measured_counters(kernel):
+    """The committed rocprofv3 counter record of `kernel` (HBM bytes per
+    launch from FETCH_SIZE + WRITE_SIZE scaled by a copy kernel of known
+    size; MFMA and VALU busy fractions), or None when there is none or the
+    kernel source has changed since the counters were taken."""
     import hashlib
 
     try:
@@ -299,8 +304,13 @@ def measured_traffic(kernel):
         if ln.startswith('{"traffic"'):
             rec = json.loads(ln)["traffic"].get(kernel)
             if rec and rec.get("source_sha256") == sha:
-                return rec["bytes_per_launch"]
+                return rec
     return None
+
+
+def measured_traffic(kernel):
+    rec = measured_counters(kernel)
+    return None if rec is None else rec["bytes_per_launch"]
 
 
 def roofline(p):
@@ -359,7 +369,11 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the 65536-token workload")
     ap.add_argument("--only", choices=["prefill", "decode", "verify", "long"], default=None,
                     help="time a single workload (for profiler runs)")
+    ap.add_argument("--settle", type=float, default=0.2,
+                    help="seconds of untimed calls before each timed region (0 under a profiler)")
     args = ap.parse_args()
+    global SETTLE_S
+    SETTLE_S = args.settle
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the recurrence shards by head or request with no communication, "
@@ -415,7 +429,10 @@ def main():
                     "tflops": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12,
                     "mfma_frac_of_bf16_peak": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12
                     / BF16_MFMA_PEAK_TFLOPS,
-                    "gate_gbs": p["gate_bytes"] / (p["ms_gate"] * 1e-3) / 1e9},
+                    "gate_gbs": p["gate_bytes"] / (p["ms_gate"] * 1e-3) / 1e9,
+                    "counters": {n: ({x: r[x] for x in ("mfma_busy", "valu_busy") if x in r}
+                                     if (r := measured_counters(n)) else None)
+                                 for n in ("intra_kernel", "state_kernel")}},
     }
     d = bench_decode(args.steps, args.warmup)
     line["decode"] = {"workload": "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",

@@ -60,8 +60,6 @@ __device__ __forceinline__ float4 fma4(float s, float4 b, float4 a) {
                      fmaf(s, b.w, a.w));
 }
 
-// Butterfly sum over the lanes whose index differs only in bits
-// [lo_mask, 32]; every participating lane ends with the same bits.
 // Four consecutive fp32 values with the non-temporal hint (streamed once:
 // the caches need not keep them).
 typedef float f32x4_nt __attribute__((ext_vector_type(4)));
@@ -73,6 +71,9 @@ __device__ __forceinline__ void store4_nt(float* p, float4 x) {
   __builtin_nontemporal_store(f32x4_nt{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4_nt*>(p));
 }
 
+// Butterfly sum over the lanes whose index differs only in the bits from
+// lo_mask (a power of two) up to 32; every lane of such a group ends with
+// the group's sum.  xor_sum(x, 1) is the sum over the whole wave.
 __device__ __forceinline__ float xor_sum(float x, int lo_mask) {
   for (int m = lo_mask; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
