@@ -198,6 +198,51 @@ kda_status kda_verify(kda_dtype io, const void* q, const void* k,
                       int32_t H, int32_t K, int32_t V, float* inter_states,
                       void* o, void* stream);
 
+/* Longest ring kda_replay_decode accepts. */
+#define KDA_RING_MAX 32
+
+/*
+ * Buffered single-token decode ("ReplaySSM" analysis, sections 2 and 3): the
+ * pool holds per-slot checkpoints that are read every step and written only
+ * every ring_len steps; in between, each (slot, head) appends the step's
+ * (d, k, g) to a small ring, and the state the step needs is replayed from
+ * the checkpoint and the ring without being formed.  Halves the state
+ * traffic of kda_recurrent_decode for long rings.
+ *   q, k [B, H, K], v [B, H, V] io dtype; g [B, H, K] fp32; beta [B, H] fp32;
+ *   state_pool [n_slots, H, K, V] fp32: the checkpoint of each slot;
+ *   slot_idx [B] int32 (device): as in kda_recurrent_decode (negative =
+ *     padding row: o = 0, pool and ring untouched);
+ *   write_pos [B] int32 (device): ring cursor of each row = steps decoded on
+ *     the slot since its checkpoint, 0 .. ring_len-1.  A live row with a
+ *     cursor outside that range gets o = NaN and touches nothing else.
+ *   force_flush [B] int32 (device) or NULL: nonzero writes the checkpoint at
+ *     this step whatever the cursor;
+ *   ring_len L in 1 .. KDA_RING_MAX; the rings, indexed [slot, head, entry]:
+ *     ring_d [n_slots, H, L, V] fp32, ring_k [n_slots, H, L, K] io dtype,
+ *     ring_g [n_slots, H, L, K] fp32.  Entries 0 .. write_pos-1 of a live
+ *     row's slot must hold the steps since its checkpoint (as this function
+ *     left them); their contents are otherwise irrelevant.
+ *   o [B, H, V] io dtype;
+ *   next_write_pos [B] int32 (device) or NULL: receives 0 for rows that wrote
+ *     their checkpoint, write_pos + 1 for the others, and write_pos for
+ *     padding rows; it must not overlap write_pos or force_flush.
+ * A row writes its checkpoint (S' + k^T d, the state after this step) when
+ * write_pos = L-1 or force_flush is set, and otherwise appends
+ * (d, k, g) at entry write_pos.  Every row's o equals that of
+ * kda_recurrent_decode on the state the slot would hold after the same
+ * steps; with L = 1 (or write_pos = 0 and a forced flush) the results are
+ * bit-identical to kda_recurrent_decode.  Live slots must be distinct
+ * within one call.
+ */
+kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             float scale, float* state_pool, int64_t n_slots,
+                             const int32_t* slot_idx, const int32_t* write_pos,
+                             const int32_t* force_flush, int32_t ring_len,
+                             float* ring_d, void* ring_k, float* ring_g,
+                             int32_t B, int32_t H, int32_t K, int32_t V, void* o,
+                             int32_t* next_write_pos, void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

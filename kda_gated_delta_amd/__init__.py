@@ -62,13 +62,16 @@ def lib() -> ctypes.CDLL:
     L.kda_verify.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, i32,
                              i32, i32, i32, i32, vp, vp, vp]
     L.kda_verify.restype = ctypes.c_int
+    L.kda_replay_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp,
+                                    i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.kda_replay_decode.restype = ctypes.c_int
     _lib = L
     return L
 
 
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
-            "kda_recurrent_decode", "kda_verify")
+            "kda_recurrent_decode", "kda_verify", "kda_replay_decode")
 
 
 def status_string(status: int) -> str:
@@ -276,3 +279,40 @@ def kda_verify(q, k, v, g, beta, scale: float, state_pool, slot_idx,
         _ptr(state_pool), n_slots, _ptr(slot_idx), B, Tv, H, K, V,
         _ptr(inter_states), _ptr(o), _stream(dev)))
     return o, inter_states
+
+
+def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, write_pos,
+                      ring_d, ring_k, ring_g, force_flush=None, o=None, next_write_pos=None):
+    """Buffered single-token decode.  ``state_pool`` [n_slots,H,K,V] holds the
+    checkpoints; the rings ring_d [n_slots,H,L,V] fp32, ring_k [n_slots,H,L,K]
+    (io dtype) and ring_g [n_slots,H,L,K] fp32 hold the steps since them;
+    ``write_pos`` [B] int32 is each row's cursor.  Returns (o [B,H,V],
+    next_write_pos [B] int32)."""
+    B, H, K = q.shape
+    V = v.shape[2]
+    dev = q.device
+    io = _io_dtype(q)
+    n_slots = state_pool.shape[0]
+    L = ring_d.shape[2]
+    _need(k, "k", q.dtype, (B, H, K), dev)
+    _need(v, "v", q.dtype, (B, H, V), dev)
+    _need(g, "g", torch.float32, (B, H, K), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    _need(write_pos, "write_pos", torch.int32, (B,), dev)
+    if force_flush is not None:
+        _need(force_flush, "force_flush", torch.int32, (B,), dev)
+    _need(ring_d, "ring_d", torch.float32, (n_slots, H, L, V), dev)
+    _need(ring_k, "ring_k", q.dtype, (n_slots, H, L, K), dev)
+    _need(ring_g, "ring_g", torch.float32, (n_slots, H, L, K), dev)
+    o = torch.empty((B, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (B, H, V), dev)
+    if next_write_pos is None:
+        next_write_pos = torch.empty((B,), dtype=torch.int32, device=dev)
+    _need(next_write_pos, "next_write_pos", torch.int32, (B,), dev)
+    _check("kda_replay_decode", lib().kda_replay_decode(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state_pool),
+        n_slots, _ptr(slot_idx), _ptr(write_pos), _ptr(force_flush), L, _ptr(ring_d),
+        _ptr(ring_k), _ptr(ring_g), B, H, K, V, _ptr(o), _ptr(next_write_pos), _stream(dev)))
+    return o, next_write_pos

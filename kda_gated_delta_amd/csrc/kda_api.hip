@@ -165,4 +165,39 @@ kda_status kda_verify(kda_dtype io, const void* q, const void* k,
   return launch_status(kda::run_verify(p, (hipStream_t)stream));
 }
 
+kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
+                             const void* v, const float* g, const float* beta,
+                             float scale, float* state_pool, int64_t n_slots,
+                             const int32_t* slot_idx, const int32_t* write_pos,
+                             const int32_t* force_flush, int32_t ring_len, float* ring_d,
+                             void* ring_k, float* ring_g, int32_t B, int32_t H,
+                             int32_t K, int32_t V, void* o, int32_t* next_write_pos,
+                             void* stream) {
+  if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (B < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
+  if (ring_len < 1 || ring_len > KDA_RING_MAX) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
+  if ((uint64_t)B * (uint64_t)H >= (1ull << 31)) return KDA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !g || !beta || !state_pool || !slot_idx || !write_pos || !ring_d ||
+      !ring_k || !ring_g || !o)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!io_aligned(io, v) || !io_aligned(io, o) || !aligned16(state_pool) || !aligned16(ring_d))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (next_write_pos) {
+    // the cursor output is written while other workgroups still read the
+    // cursors and flush flags: it must not overlap them
+    const uintptr_t n0 = (uintptr_t)next_write_pos, n1 = n0 + (uintptr_t)B * 4;
+    const uintptr_t w0 = (uintptr_t)write_pos, w1 = w0 + (uintptr_t)B * 4;
+    if (n0 < w1 && w0 < n1) return KDA_ERR_INVALID_ARGUMENT;
+    if (force_flush) {
+      const uintptr_t f0 = (uintptr_t)force_flush, f1 = f0 + (uintptr_t)B * 4;
+      if (n0 < f1 && f0 < n1) return KDA_ERR_INVALID_ARGUMENT;
+    }
+  }
+  kda::ReplayArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
+                    write_pos, force_flush, ring_len, ring_d, ring_k, ring_g, B, H, K, V, o,
+                    next_write_pos};
+  return launch_status(kda::run_replay(p, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -16,6 +16,7 @@
 // (section 3.12): it avoids a second pass over the updated state.
 // A negative slot index marks a padding row (ReplaySSM analysis, section 3.6).
 
+#include "kda.h"
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -237,6 +238,177 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
   }
 }
 
+// ---------------------------------------------------------------- replay
+
+// Buffered ("replay") decode (ReplaySSM analysis, sections 2 and 3): the pool
+// holds a checkpoint S0 that is only read, and a per-(slot, head) ring keeps
+// (d_j, k_j, g_j) of the m = write_pos tokens decoded since the checkpoint.
+// The state before the current token is
+//   S_m = Diag(e^{G_m}) S0 + sum_j Diag(e^{G_m - G_j}) k_j^T d_j,
+// G_j the sum of g_1 .. g_j.  The current token decays it by a = e^{g}; its
+// products with k and q need no rebuilt state: with A = a e^{G_m} and
+// w_j = a e^{G_m - G_j} (per key channel),
+//   k S' = (k A) S0 + sum_j (k . (w_j k_j)) d_j,  and the same for q,
+// one pass over S0 plus m dot products of length K.  Then d = beta (v - k S'),
+// o = scale (q S' + (q.k) d).  At the ring's last position (or when forced)
+// the state S' + k^T d is written back as the new checkpoint; otherwise
+// (d, k, g) is appended at write_pos.  With an empty ring every operation is
+// that of the plain decode step in the same order, so the results are
+// bit-identical to it.
+constexpr int RING_MAX = KDA_RING_MAX;
+
+template <typename IO, int K, int V>
+__global__ __launch_bounds__((StepShape<K, V>::NT)) void replay_kernel(
+    const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float scale,
+    float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
+    const int32_t* __restrict__ write_pos, const int32_t* __restrict__ force_flush, int L,
+    float* __restrict__ ring_d, IO* __restrict__ ring_k, float* __restrict__ ring_g, int H,
+    IO* __restrict__ o, int32_t* __restrict__ next_pos) {
+  typedef StepShape<K, V> Sh;
+  __shared__ float sq[K], sk[K], sa[K], sg[K];
+  __shared__ float swk[RING_MAX][K], sgr[RING_MAX][K];
+  __shared__ __align__(16) float sd[RING_MAX][V];
+  __shared__ float sck[RING_MAX], scq[RING_MAX];
+  __shared__ float red[Sh::RED];
+  const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
+  const int64_t rh = blockIdx.x;  // r * H + h
+  const int r = (int)(rh / H), h = (int)(rh % H);
+  const int c0 = 4 * cg;
+  const int64_t slot = slot_idx[r];
+  const int pos = write_pos[r];
+  if (slot < 0 || pos < 0 || pos >= L) {
+    // padding row: o = 0; a cursor outside the ring: o = NaN (a caller
+    // error made visible).  Neither touches the pool or the ring.
+    if (rg == 0) store4(o + rh * V + c0, f4(slot < 0 ? 0.f : __builtin_nanf("")));
+    if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = pos;
+    return;
+  }
+  const bool flush = pos == L - 1 || (force_flush != nullptr && force_flush[r] != 0);
+  const int m = pos;  // ring entries since the checkpoint
+  float* S = pool + (slot * H + h) * (int64_t)(K * V);
+  const int64_t e0 = (slot * H + h) * (int64_t)L;  // ring entry (slot, h, 0)
+  Rows<Sh::RPT> st;
+  float4* s = st.s;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S + (rg + Sh::RG * i) * V + c0);
+  for (int c = t; c < K; c += Sh::NT) {
+    sq[c] = to_f32(q[rh * K + c]);
+    sk[c] = to_f32(k[rh * K + c]);
+    sg[c] = g[rh * K + c];
+  }
+  for (int e = t; e < m * K; e += Sh::NT) {
+    const int j = e / K, c = e % K;
+    swk[j][c] = to_f32(ring_k[(e0 + j) * K + c]);
+    sgr[j][c] = ring_g[(e0 + j) * K + c];
+  }
+  for (int e = t; e < m * (V / 4); e += Sh::NT) {
+    const int j = e / (V / 4), c = 4 * (e % (V / 4));
+    *reinterpret_cast<float4*>(&sd[j][c]) = load4(ring_d + (e0 + j) * V + c);
+  }
+  const float4 vv = load4(v + rh * V + c0);
+  const float b = beta[rh];
+  __syncthreads();
+  // per key channel, newest entry first: w_j k_j in place of k_j, then A
+  for (int c = t; c < K; c += Sh::NT) {
+    float suf = sg[c];
+    for (int j = m - 1; j >= 0; --j) {
+      swk[j][c] *= expf(suf);
+      suf += sgr[j][c];
+    }
+    sa[c] = expf(suf);
+  }
+  __syncthreads();
+  // ring coefficients k . (w_j k_j) and q . (w_j k_j), one wave per entry
+  {
+    const int lane = t & 63, wv = t >> 6;
+    for (int j = wv; j < m; j += Sh::NW) {
+      float pk = 0.f, pq = 0.f;
+      for (int c = lane; c < K; c += 64) {
+        pk = fmaf(sk[c], swk[j][c], pk);
+        pq = fmaf(sq[c], swk[j][c], pq);
+      }
+      pk = xor_sum(pk, 1);
+      pq = xor_sum(pq, 1);
+      if (lane == 0) {
+        sck[j] = pk;
+        scq[j] = pq;
+      }
+    }
+  }
+  __syncthreads();
+  Partials p;
+  p.vh = f4(0.f);
+  p.qs = f4(0.f);
+  p.qk = 0.f;
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) {
+    const int row = rg + Sh::RG * i;
+    s[i] = sa[row] * s[i];
+    p.vh = fma4(sk[row], s[i], p.vh);
+    p.qs = fma4(sq[row], s[i], p.qs);
+    p.qk = fmaf(sq[row], sk[row], p.qk);
+  }
+  for (int j = rg; j < m; j += Sh::RG) {
+    const float4 dj = *reinterpret_cast<const float4*>(&sd[j][c0]);
+    p.vh = fma4(sck[j], dj, p.vh);
+    p.qs = fma4(scq[j], dj, p.qs);
+  }
+  p = reduce_rows<K, V>(p, red);
+  const float4 d = b * (vv - p.vh);
+  const float4 oq = fma4(p.qk, d, p.qs);
+  if (rg == 0) store4(o + rh * V + c0, scale * oq);
+  if (flush) {
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i) {
+      const int row = rg + Sh::RG * i;
+      s[i] = fma4(sk[row], d, s[i]);
+      for (int j = 0; j < m; ++j)
+        s[i] = fma4(swk[j][row], *reinterpret_cast<const float4*>(&sd[j][c0]), s[i]);
+      store4_nt(S + row * V + c0, s[i]);
+    }
+  } else {
+    if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
+    for (int c = t; c < K; c += Sh::NT) {
+      ring_k[(e0 + pos) * K + c] = k[rh * K + c];
+      ring_g[(e0 + pos) * K + c] = sg[c];
+    }
+  }
+  if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = flush ? 0 : pos + 1;
+}
+
+template <typename IO, int K, int V>
+hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
+  typedef StepShape<K, V> Sh;
+  hipLaunchKernelGGL((replay_kernel<IO, K, V>), dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0,
+                     stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
+                     a.scale, a.pool, a.slot_idx, a.write_pos, a.force_flush, a.L, a.ring_d,
+                     (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos);
+  return hipGetLastError();
+}
+
+template <typename IO, int K>
+hipError_t replay_v(const ReplayArgs& a, hipStream_t st) {
+  switch (a.V) {
+    case 16: return launch_replay<IO, K, 16>(a, st);
+    case 32: return launch_replay<IO, K, 32>(a, st);
+    case 64: return launch_replay<IO, K, 64>(a, st);
+    case 128: return launch_replay<IO, K, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename IO>
+hipError_t replay_k(const ReplayArgs& a, hipStream_t st) {
+  switch (a.K) {
+    case 16: return replay_v<IO, 16>(a, st);
+    case 32: return replay_v<IO, 32>(a, st);
+    case 64: return replay_v<IO, 64>(a, st);
+    case 128: return replay_v<IO, 128>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename IO, int K, int V>
 hipError_t launch_decode(const void* q, const void* k, const void* v,
                          const float* g, const float* beta, float scale,
@@ -314,6 +486,10 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t stream) {
 
 hipError_t run_verify(const DecodeArgs& a, hipStream_t stream) {
   return a.bf16_io ? verify_k<bf16>(a, stream) : verify_k<float>(a, stream);
+}
+
+hipError_t run_replay(const ReplayArgs& a, hipStream_t stream) {
+  return a.bf16_io ? replay_k<bf16>(a, stream) : replay_k<float>(a, stream);
 }
 
 }  // namespace kda

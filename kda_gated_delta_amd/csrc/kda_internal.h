@@ -28,6 +28,22 @@ struct DecodeArgs {
   void* o;
 };
 
+struct ReplayArgs {
+  bool bf16_io;
+  const void *q, *k, *v;
+  const float *g, *beta;
+  float scale;
+  float* pool;  // checkpoints: read, and written by flushing rows
+  const int32_t *slot_idx, *write_pos, *force_flush;
+  int L;  // ring length
+  float* ring_d;
+  void* ring_k;  // io dtype
+  float* ring_g;
+  int B, H, K, V;
+  void* o;
+  int32_t* next_pos;
+};
+
 struct PrefillArgs {
   bool bf16_io;
   const void *q, *k, *v;
@@ -55,6 +71,7 @@ struct PrefillArgs {
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);
 hipError_t run_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t run_verify(const DecodeArgs& a, hipStream_t stream);
+hipError_t run_replay(const ReplayArgs& a, hipStream_t stream);
 hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream);
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C);
 

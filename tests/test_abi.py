@@ -144,3 +144,28 @@ def test_binding_rejects_cpu_and_wrong_dtypes():
                                  torch.zeros(4, 4, 16, 16), torch.zeros(2, dtype=torch.int32))
     with pytest.raises(ValueError):
         kda.kda_gate_prep(torch.zeros(3, 2, 16), torch.zeros(3, 3), torch.zeros(2))
+
+
+def test_replay_decode_validation():
+    L = kda.lib()
+    W, N, F = ctypes.c_void_p(8192), ctypes.c_void_p(8192 + 64), ctypes.c_void_p(8192 + 128)
+
+    def args(**kw):
+        return [kw.get("io", 1), P, P, P, P, P, 1.0, kw.get("pool", P), kw.get("n_slots", 8),
+                P, kw.get("wp", W), kw.get("ff", F), kw.get("L", 16), kw.get("rd", P), P, P,
+                kw.get("B", 4), 2, kw.get("K", 128), 128, kw.get("o", P), kw.get("nx", N), None]
+    assert L.kda_replay_decode(*args(io=5)) == UNSUPPORTED
+    assert L.kda_replay_decode(*args(B=0)) == INVALID
+    assert L.kda_replay_decode(*args(n_slots=0)) == INVALID
+    assert L.kda_replay_decode(*args(L=0)) == INVALID
+    assert L.kda_replay_decode(*args(L=33)) == INVALID
+    assert L.kda_replay_decode(*args(K=24)) == UNSUPPORTED
+    assert L.kda_replay_decode(*args(wp=None)) == INVALID
+    assert L.kda_replay_decode(*args(rd=None)) == INVALID
+    assert L.kda_replay_decode(*args(o=None)) == INVALID
+    assert L.kda_replay_decode(*args(pool=P_MIS)) == INVALID
+    assert L.kda_replay_decode(*args(rd=P_MIS)) == INVALID
+    # the cursor output may not overlap the cursors or the flush flags
+    assert L.kda_replay_decode(*args(nx=W)) == INVALID
+    assert L.kda_replay_decode(*args(nx=ctypes.c_void_p(8192 + 12))) == INVALID
+    assert L.kda_replay_decode(*args(nx=ctypes.c_void_p(8192 + 120))) == INVALID
