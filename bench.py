@@ -126,6 +126,18 @@ def verify_bytes(B, Tv, H, K, V, io_bytes=2):
     return B * H * (K * V * 4 * (1 + Tv) + Tv * ((2 * K + 2 * V) * io_bytes + 4 * K + 4))
 
 
+def replay_bytes(write_pos, flush, H, K, V, io_bytes=2):
+    """Buffered decode: the checkpoint read, the ring entries read (m of
+    them: k in the io dtype, g and d fp32), the checkpoint written by a
+    flushing row or one ring entry appended by the others, and the token's
+    q, k, v, o, g, beta, per request-head."""
+    entry = K * io_bytes + 4 * K + 4 * V
+    tok = (2 * K + 2 * V) * io_bytes + 4 * K + 4
+    per_row = [K * V * 4 + m * entry + (K * V * 4 if f else entry) + tok
+               for m, f in zip(write_pos, flush)]
+    return int(H * sum(int(x) for x in per_row))
+
+
 # -------------------------------------------------------------- workloads
 
 def prefill_setup(name):
@@ -223,6 +235,42 @@ def bench_decode(steps, warmup):
     state = 2 * B * H * K * V * 4
     return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes,
                 gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9)
+
+
+def bench_replay(steps, warmup, L=16):
+    """kda_replay_decode on the decode_256 shapes with a ring of L: cursors
+    staggered over the rows (row r at r % L, so 1/L of the rows write their
+    checkpoint per call), rings filled by L earlier calls."""
+    w = kda_synth.WORKLOADS["decode_256"]
+    c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
+                              seed=w["seed"], dt_bias_std=w["dt_bias_std"],
+                              state_std=w["state_std"])
+    B, H, K, V = w["B"], w["H"], w["K"], w["V"]
+    a, b = _dev(c["a"]), _dev(c["b"])
+    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+    n = w["n_slots"]
+    ring_d = torch.zeros((n, H, L, V), device="cuda")
+    ring_k = torch.zeros((n, H, L, K), dtype=torch.bfloat16, device="cuda")
+    ring_g = torch.zeros((n, H, L, K), device="cuda")
+    o = torch.empty_like(v)
+    rows = torch.arange(B, device="cuda", dtype=torch.int32)
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nxt = torch.empty_like(pos)
+    for s in range(L):  # row r first writes its checkpoint at call r % L
+        force = ((rows % L) == s).to(torch.int32)
+        kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d, ring_k,
+                              ring_g, force_flush=force, o=o, next_write_pos=nxt)
+        pos, nxt = nxt, pos
+    wp = pos.cpu().numpy()
+    fn = lambda: kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d,
+                                       ring_k, ring_g, o=o, next_write_pos=nxt)
+    ms = _time(fn, max(steps, 20), warmup)
+    nbytes = replay_bytes(wp, wp == L - 1, H, K, V)
+    return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes, L=L,
+                mean_ring_entries=float(wp.mean()), flush_frac=float((wp == L - 1).mean()),
+                gbs=nbytes / (ms * 1e-3) / 1e9)
 
 
 def bench_verify(steps, warmup):
@@ -367,7 +415,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-long", action="store_true", help="skip the 65536-token workload")
-    ap.add_argument("--only", choices=["prefill", "decode", "verify", "long"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "replay", "verify", "long"],
+                    default=None,
                     help="time a single workload (for profiler runs)")
     ap.add_argument("--settle", type=float, default=0.2,
                     help="seconds of untimed calls before each timed region (0 under a profiler)")
@@ -389,6 +438,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(bench_decode(args.steps, args.warmup)))
+        return
+    if args.only == "replay":
+        print(json.dumps(bench_replay(args.steps, args.warmup)))
         return
     if args.only == "verify":
         print(json.dumps(bench_verify(args.steps, args.warmup)))
@@ -439,6 +491,15 @@ def main():
                       "tokens_per_s": d["tokens_per_s"], "ms": d["ms"],
                       "state_gbs": d["state_gbs"], "total_gbs": d["gbs"],
                       "frac_of_hbm_peak": d["gbs"] / HBM_PEAK_GBS}
+    rp = bench_replay(args.steps, args.warmup)
+    line["replay_decode"] = {"workload": "decode_256 with a 16-entry ring per slot, cursors "
+                                         "staggered over the rows (kda_replay_decode)",
+                             "tokens_per_s": rp["tokens_per_s"], "ms": rp["ms"],
+                             "algorithmic_bytes": rp["bytes"], "total_gbs": rp["gbs"],
+                             "frac_of_hbm_peak": rp["gbs"] / HBM_PEAK_GBS,
+                             "mean_ring_entries": rp["mean_ring_entries"],
+                             "flush_frac": rp["flush_frac"],
+                             "speedup_vs_decode": d["ms"] / rp["ms"]}
     vr = bench_verify(args.steps, args.warmup)
     line["verify"] = {"workload": "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool",
                       "tokens_per_s": vr["tokens_per_s"], "ms": vr["ms"],

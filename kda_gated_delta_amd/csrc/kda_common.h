@@ -71,6 +71,14 @@ __device__ __forceinline__ void store4_nt(float* p, float4 x) {
   __builtin_nontemporal_store(f32x4_nt{x.x, x.y, x.z, x.w}, reinterpret_cast<f32x4_nt*>(p));
 }
 
+// A buffer resource over `bytes` bytes from `base`: loads through it at or
+// past that range return zero without touching memory, and stores there are
+// dropped.  Word 3 of the descriptor selects 32-bit raw data (the gfx9 value).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Butterfly sum over the lanes whose index differs only in the bits from
 // lo_mask (a power of two) up to 32; every lane of such a group ends with
 // the group's sum.  xor_sum(x, 1) is the sum over the whole wave.

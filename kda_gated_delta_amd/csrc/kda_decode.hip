@@ -20,6 +20,8 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 namespace {
 
@@ -258,7 +260,7 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
 constexpr int RING_MAX = KDA_RING_MAX;
 
 template <typename IO, int K, int V>
-__global__ __launch_bounds__((StepShape<K, V>::NT)) void replay_kernel(
+__global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_per_eu(StepShape<K, V>::NT == 1024 ? 8 : 1))) void replay_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float scale,
     float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
@@ -267,9 +269,9 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) void replay_kernel(
     IO* __restrict__ o, int32_t* __restrict__ next_pos) {
   typedef StepShape<K, V> Sh;
   __shared__ float sq[K], sk[K], sa[K], sg[K];
-  __shared__ float swk[RING_MAX][K], sgr[RING_MAX][K];
-  __shared__ __align__(16) float sd[RING_MAX][V];
-  __shared__ float sck[RING_MAX], scq[RING_MAX];
+  __shared__ __align__(16) float swk[RING_MAX][K], sgr[RING_MAX][K], sd[RING_MAX][V];
+  __shared__ float sck[RING_MAX], scq[RING_MAX], sdump[3];
+  __shared__ float spart[Sh::NT / K][K];
   __shared__ float red[Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
   const int64_t rh = blockIdx.x;  // r * H + h
@@ -288,35 +290,112 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) void replay_kernel(
   const int m = pos;  // ring entries since the checkpoint
   float* S = pool + (slot * H + h) * (int64_t)(K * V);
   const int64_t e0 = (slot * H + h) * (int64_t)L;  // ring entry (slot, h, 0)
-  Rows<Sh::RPT> st;
-  float4* s = st.s;
+  // Every load is unconditional and the small ones go first: ring entries
+  // 0 .. m-1 and the token's q, k, g are buffer resources whose range ends
+  // there (reads past it return zero without touching memory), then the
+  // checkpoint.  Staging the small ones in LDS then waits for them alone,
+  // and the ring arithmetic below runs while the checkpoint is in flight.
+  constexpr int RK = (RING_MAX * K / 4 + Sh::NT - 1) / Sh::NT;  // 4-channel groups
+  constexpr int RD = (RING_MAX * V / 4 + Sh::NT - 1) / Sh::NT;  // 4-column groups
+  typedef typename std::conditional<sizeof(IO) == 2, uint2, uint4>::type RawK;
+  const auto rk = buffer_rsrc(ring_k + e0 * K, (uint32_t)(m * K * sizeof(IO)));
+  const auto rgr = buffer_rsrc(ring_g + e0 * K, (uint32_t)(m * K * 4));
+  const auto rd = buffer_rsrc(ring_d + e0 * V, (uint32_t)(m * V * 4));
+  RawK kr[RK];
+  float4 gr[RK], dr[RD];
 #pragma unroll
-  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S + (rg + Sh::RG * i) * V + c0);
-  for (int c = t; c < K; c += Sh::NT) {
-    sq[c] = to_f32(q[rh * K + c]);
-    sk[c] = to_f32(k[rh * K + c]);
-    sg[c] = g[rh * K + c];
+  for (int i = 0; i < RK; ++i) {
+    const uint32_t e = (uint32_t)(t + i * Sh::NT) * 4;  // first element of the group
+    if constexpr (sizeof(IO) == 2)
+      kr[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rk, e * 2, 0, 0));
+    else
+      kr[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, e * 4, 0, 0));
+    gr[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rgr, e * 4, 0, 0));
   }
-  for (int e = t; e < m * K; e += Sh::NT) {
-    const int j = e / K, c = e % K;
-    swk[j][c] = to_f32(ring_k[(e0 + j) * K + c]);
-    sgr[j][c] = ring_g[(e0 + j) * K + c];
+#pragma unroll
+  for (int i = 0; i < RD; ++i) {
+    const uint32_t e = (uint32_t)(t + i * Sh::NT) * 4;
+    dr[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rd, e * 4, 0, 0));
   }
-  for (int e = t; e < m * (V / 4); e += Sh::NT) {
-    const int j = e / (V / 4), c = 4 * (e % (V / 4));
-    *reinterpret_cast<float4*>(&sd[j][c]) = load4(ring_d + (e0 + j) * V + c);
+  // the token: thread c < K holds channel c of q, k and g (K <= NT)
+  static_assert(K <= Sh::NT, "one channel per thread");
+  float tq, tk, tg;
+  {
+    const uint32_t off = (uint32_t)t * (uint32_t)sizeof(IO);
+    if constexpr (sizeof(IO) == 2) {
+      tq = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+               buffer_rsrc(q + rh * K, K * 2), off, 0, 0) << 16);
+      tk = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
+               buffer_rsrc(k + rh * K, K * 2), off, 0, 0) << 16);
+    } else {
+      tq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+               buffer_rsrc(q + rh * K, K * 4), off, 0, 0));
+      tk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+               buffer_rsrc(k + rh * K, K * 4), off, 0, 0));
+    }
+    tg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+             buffer_rsrc(g + rh * K, K * 4), (uint32_t)t * 4, 0, 0));
   }
   const float4 vv = load4(v + rh * V + c0);
   const float b = beta[rh];
-  __syncthreads();
-  // per key channel, newest entry first: w_j k_j in place of k_j, then A
-  for (int c = t; c < K; c += Sh::NT) {
-    float suf = sg[c];
-    for (int j = m - 1; j >= 0; --j) {
-      swk[j][c] *= expf(suf);
-      suf += sgr[j][c];
+  Rows<Sh::RPT> st;
+  float4* s = st.s;
+  __builtin_amdgcn_sched_barrier(0);  // keep the checkpoint's loads last
+#pragma unroll
+  for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S + (rg + Sh::RG * i) * V + c0);
+  // stage the ring and the token in LDS (threads past K store to a dump
+  // word: a store on every thread keeps the token's loads ahead of the
+  // checkpoint's instead of sunk into a branch behind them)
+  {
+    const bool tok = t < K;
+    *(tok ? sq + t : sdump) = tq;
+    *(tok ? sk + t : sdump + 1) = tk;
+    *(tok ? sg + t : sdump + 2) = tg;
+  }
+#pragma unroll
+  for (int i = 0; i < RK; ++i) {
+    const int e = (t + i * Sh::NT) * 4, j = e / K, c = e % K;
+    if (j < RING_MAX) {
+      float4 kf;
+      if constexpr (sizeof(IO) == 2)
+        kf = make_float4(__uint_as_float(kr[i].x << 16), __uint_as_float(kr[i].x & 0xffff0000u),
+                         __uint_as_float(kr[i].y << 16), __uint_as_float(kr[i].y & 0xffff0000u));
+      else
+        kf = __builtin_bit_cast(float4, kr[i]);
+      *reinterpret_cast<float4*>(&swk[j][c]) = kf;
+      *reinterpret_cast<float4*>(&sgr[j][c]) = gr[i];
     }
-    sa[c] = expf(suf);
+  }
+#pragma unroll
+  for (int i = 0; i < RD; ++i) {
+    const int e = (t + i * Sh::NT) * 4, j = e / V, c = e % V;
+    if (j < RING_MAX) *reinterpret_cast<float4*>(&sd[j][c]) = dr[i];
+  }
+  __syncthreads();
+  // Decay weights per key channel, newest entry first: w_j k_j in place of
+  // k_j, then A.  The NG = NT / K thread groups of a channel take EPG
+  // consecutive entries each; a group starts from the sum of the current g
+  // and of the entries of the groups after it.
+  {
+    constexpr int NG = Sh::NT / K, EPG = (RING_MAX + NG - 1) / NG;
+    const int c = t % K, grp = t / K, j0 = grp * EPG;
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < EPG; ++i)
+      if (j0 + i < m) part += sgr[j0 + i][c];
+    spart[grp][c] = part;
+    __syncthreads();
+    float suf = sg[c];
+    for (int q2 = NG - 1; q2 > grp; --q2) suf += spart[q2][c];
+#pragma unroll
+    for (int i = EPG - 1; i >= 0; --i) {
+      const int j = j0 + i;
+      if (j < m) {
+        swk[j][c] *= expf(suf);
+        suf += sgr[j][c];
+      }
+    }
+    if (grp == 0) sa[c] = expf(suf);
   }
   __syncthreads();
   // ring coefficients k . (w_j k_j) and q . (w_j k_j), one wave per entry
@@ -369,9 +448,9 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) void replay_kernel(
     }
   } else {
     if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
-    for (int c = t; c < K; c += Sh::NT) {
-      ring_k[(e0 + pos) * K + c] = k[rh * K + c];
-      ring_g[(e0 + pos) * K + c] = sg[c];
+    if (t < K) {  // k was read as io values: converting back is exact
+      ring_k[(e0 + pos) * K + t] = from_f32<IO>(tk);
+      ring_g[(e0 + pos) * K + t] = tg;
     }
   }
   if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = flush ? 0 : pos + 1;

@@ -114,15 +114,10 @@ __device__ __forceinline__ Frag load_frag(const char* tile) {
   return f;
 }
 
-// Buffer-resource loads: the base and every tile offset stay in scalar
-// registers, the only per-lane address is the lane's 16-byte slot.  Word 3 of
-// the descriptor selects 32-bit raw data (the gfx9 value).
+// Buffer-resource loads (buffer_rsrc in kda_common.h): the base and every
+// tile offset stay in scalar registers, the only per-lane address is the
+// lane's 16-byte slot.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
 
 // A fragment tile at byte `tile` of the resource (hi plane, then lo plane).
 __device__ __forceinline__ Frag buffer_frag(__amdgpu_buffer_rsrc_t r, uint32_t lane16,
