@@ -398,21 +398,29 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     if (grp == 0) sa[c] = expf(suf);
   }
   __syncthreads();
-  // ring coefficients k . (w_j k_j) and q . (w_j k_j), one wave per entry
+  // ring coefficients k . (w_j k_j) and q . (w_j k_j): LPE lanes per entry,
+  // each over every LPE-th channel, then summed across the group
   {
-    const int lane = t & 63, wv = t >> 6;
-    for (int j = wv; j < m; j += Sh::NW) {
-      float pk = 0.f, pq = 0.f;
-      for (int c = lane; c < K; c += 64) {
+    constexpr int LPE = Sh::NT / RING_MAX, CPL = K / LPE;
+    static_assert(LPE >= 1 && LPE <= 64 && CPL >= 1, "entry groups fit a wave");
+    const int j = t / LPE, pl = t % LPE;
+    float pk = 0.f, pq = 0.f;
+    if (j < m) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = pl + LPE * i;
         pk = fmaf(sk[c], swk[j][c], pk);
         pq = fmaf(sq[c], swk[j][c], pq);
       }
-      pk = xor_sum(pk, 1);
-      pq = xor_sum(pq, 1);
-      if (lane == 0) {
-        sck[j] = pk;
-        scq[j] = pq;
-      }
+    }
+#pragma unroll
+    for (int x = 1; x < LPE; x <<= 1) {
+      pk += __shfl_xor(pk, x, 64);
+      pq += __shfl_xor(pq, x, 64);
+    }
+    if (pl == 0 && j < m) {
+      sck[j] = pk;
+      scq[j] = pq;
     }
   }
   __syncthreads();
@@ -439,13 +447,14 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   if (rg == 0) store4(o + rh * V + c0, scale * oq);
   if (flush) {
 #pragma unroll
-    for (int i = 0; i < Sh::RPT; ++i) {
-      const int row = rg + Sh::RG * i;
-      s[i] = fma4(sk[row], d, s[i]);
-      for (int j = 0; j < m; ++j)
-        s[i] = fma4(swk[j][row], *reinterpret_cast<const float4*>(&sd[j][c0]), s[i]);
-      store4_nt(S + row * V + c0, s[i]);
+    for (int i = 0; i < Sh::RPT; ++i) s[i] = fma4(sk[rg + Sh::RG * i], d, s[i]);
+    for (int j = 0; j < m; ++j) {
+      const float4 dj = *reinterpret_cast<const float4*>(&sd[j][c0]);
+#pragma unroll
+      for (int i = 0; i < Sh::RPT; ++i) s[i] = fma4(swk[j][rg + Sh::RG * i], dj, s[i]);
     }
+#pragma unroll
+    for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
   } else {
     if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
     if (t < K) {  // k was read as io values: converting back is exact
