@@ -138,6 +138,33 @@ kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,
                                    void* stream);
 
 /*
+ * kda_chunk_prefill that also records chunk-boundary states, for prefix
+ * caching and verify rollback (tutorial, section "两种计算形态": the chunk
+ * form materialises the state at every chunk boundary; section "prefix cache
+ * 与投机解码": those states are kept as prefix snapshots, at a tracking
+ * interval).
+ *   snapshot_interval: a positive multiple of chunk.  Sequence n contributes
+ *     floor(len_n / snapshot_interval) rows: the state after its first
+ *     snapshot_interval, 2 snapshot_interval, ... tokens.
+ *   snapshots [snapshot_rows, H, K, V] fp32: rows of sequence n start after
+ *     those of sequences 0 .. n-1 (row sum_{m<n} floor(len_m / interval) + j
+ *     holds the state after (j + 1) interval tokens of sequence n); rows past
+ *     the total are left untouched.  snapshot_rows must be at least
+ *     T / snapshot_interval (a bound on the total for any split of T).
+ * Every other argument, o, ht and the errors are those of kda_chunk_prefill
+ * (the same kernels: o and ht are bit-identical to it), and each snapshot is
+ * bit-identical to the ht of kda_chunk_prefill run on that prefix alone.
+ */
+kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* k,
+                                       const void* v, const float* g, const float* beta,
+                                       const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                       int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                       float scale, const float* h0, float* ht, void* o,
+                                       float* snapshots, int64_t snapshot_rows,
+                                       int32_t snapshot_interval, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * kda_chunk_prefill_gated with kernel timing marks, for benchmarks and
  * profilers.  Same arguments, work and results as kda_chunk_prefill_gated;
  * in addition it records four caller-created HIP events (hipEvent_t passed

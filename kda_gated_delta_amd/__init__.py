@@ -54,6 +54,10 @@ def lib() -> ctypes.CDLL:
                                           i32, i64, i32, i32, i32, i32, f32, vp, vp, vp, vp,
                                           sz, vp]
     L.kda_chunk_prefill_gated.restype = ctypes.c_int
+    L.kda_chunk_prefill_snapshots.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i64,
+                                              i32, i32, i32, i32, f32, vp, vp, vp, vp, i64, i32,
+                                              vp, sz, vp]
+    L.kda_chunk_prefill_snapshots.restype = ctypes.c_int
     L.kda_chunk_prefill_marked.argtypes = L.kda_chunk_prefill_gated.argtypes + [vp]
     L.kda_chunk_prefill_marked.restype = ctypes.c_int
     L.kda_recurrent_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64,
@@ -71,6 +75,7 @@ def lib() -> ctypes.CDLL:
 
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
+            "kda_chunk_prefill_snapshots",
             "kda_recurrent_decode", "kda_verify", "kda_replay_decode")
 
 
@@ -147,6 +152,27 @@ def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
                     output_final_state, chunk, o, ht, workspace)
 
 
+def kda_chunk_prefill_snapshots(q, k, v, g, beta, cu_seqlens, scale: float,
+                                snapshot_interval: int, h0=None,
+                                output_final_state: bool = True, chunk: int = 64, o=None,
+                                ht=None, snapshots=None, workspace=None):
+    """kda_chunk_prefill that also records each sequence's state after every
+    ``snapshot_interval`` tokens (a multiple of ``chunk``) into
+    ``snapshots`` [rows, H, K, V] fp32, sequence after sequence (allocated
+    with T // snapshot_interval rows if None).  Returns (o, ht, snapshots)."""
+    T, H, K = q.shape
+    V = v.shape[2]
+    dev = q.device
+    if snapshots is None:
+        snapshots = torch.empty((max(T // snapshot_interval, 1), H, K, V), dtype=torch.float32,
+                                device=dev)
+    _need(snapshots, "snapshots", torch.float32, (snapshots.shape[0], H, K, V), dev)
+    o, ht = _prefill("kda_chunk_prefill_snapshots", None, q, k, v, g, beta, cu_seqlens, scale,
+                     h0, output_final_state, chunk, o, ht, workspace,
+                     snap=(snapshots, int(snapshot_interval)))
+    return o, ht, snapshots
+
+
 def kda_chunk_prefill_gated(q, k, v, a, b, A_log, dt_bias, cu_seqlens, scale: float,
                             lower_bound: float = 0.0, h0=None,
                             output_final_state: bool = True, chunk: int = 64, o=None,
@@ -190,7 +216,7 @@ def kda_chunk_prefill_marked(marks, q, k, v, a, b, A_log, dt_bias, cu_seqlens,
 
 
 def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_state,
-             chunk, o, ht, workspace, gate=None):
+             chunk, o, ht, workspace, gate=None, snap=None):
     T, H, K = q.shape
     V = v.shape[2]
     dev = q.device
@@ -226,6 +252,10 @@ def _prefill(fn, marks, q, k, v, g, beta, cu_seqlens, scale, h0, output_final_st
         else:
             arr = (ctypes.c_void_p * 4)(*[m.cuda_event for m in marks])
             _check(fn, lib().kda_chunk_prefill_marked(*gargs, arr))
+    elif snap is not None:
+        snapshots, interval = snap
+        sargs = args[:17] + [_ptr(snapshots), snapshots.shape[0], interval] + args[17:]
+        _check(fn, lib().kda_chunk_prefill_snapshots(*sargs))
     else:
         _check(fn, lib().kda_chunk_prefill(*args))
     return o, ht

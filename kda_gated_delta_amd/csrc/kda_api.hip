@@ -26,7 +26,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* marks, int gate_mode = 0,
                            const float* A_log = nullptr, const float* dt_bias = nullptr,
-                           float lower_bound = 0.f) {
+                           float lower_bound = 0.f, float* snaps = nullptr,
+                           int snap_interval = 0) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -45,7 +46,7 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
     return KDA_ERR_INVALID_ARGUMENT;
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
-                     gate_mode, A_log, dt_bias, lower_bound};
+                     gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -94,6 +95,23 @@ kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
                              void* stream) {
   return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale,
                          h0, ht, o, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* k,
+                                       const void* v, const float* g, const float* beta,
+                                       const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                       int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                       float scale, const float* h0, float* ht, void* o,
+                                       float* snapshots, int64_t snapshot_rows,
+                                       int32_t snapshot_interval, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  if (snapshot_interval < 1 || chunk < 1 || snapshot_interval % chunk != 0)
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (!snapshots || !aligned16(snapshots) || T < 0 || snapshot_rows < T / snapshot_interval)
+    return KDA_ERR_INVALID_ARGUMENT;
+  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, stream, nullptr, 0, nullptr, nullptr,
+                         0.f, snapshots, snapshot_interval);
 }
 
 kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,

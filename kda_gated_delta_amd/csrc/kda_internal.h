@@ -66,6 +66,10 @@ struct PrefillArgs {
   int gate_mode;
   const float *A_log, *dt_bias;
   float lower_bound;
+  // Optional chunk-boundary states: [rows, H, K, V] fp32, the state of each
+  // sequence after every snap_interval tokens (nullptr for none).
+  float* snaps;
+  int snap_interval;
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

@@ -213,6 +213,15 @@ size_t rec_bytes(int D, int C) {
 
 // ------------------------------------------------------------------- plan
 
+// Token range lo .. hi-1 of sequence n, with the bounds clamped to
+// 0 <= lo <= hi <= T (the plan and the snapshot rows both use this).
+__device__ __forceinline__ void seq_bounds(const int32_t* __restrict__ cu, int n, int64_t T,
+                                           int& lo, int& hi) {
+  const int64_t a = cu[n], b = cu[n + 1];
+  lo = (int)(a < 0 ? 0 : (a > T ? T : a));
+  hi = (int)(b < lo ? lo : (b > T ? T : b));
+}
+
 // Chunk table of the packed batch: sequence n owns chunks
 // off[n] .. off[n+1]-1; entries past the last chunk get len = 0.  Sequence
 // bounds are clamped to 0 <= lo <= hi <= T.
@@ -227,11 +236,7 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   // Clamped bounds and chunk count of sequence n.  A batch of at most
   // NTHREADS sequences reads cu_seqlens once (thread t keeps sequence t);
   // larger ones re-read it in each pass.
-  auto bounds = [&](int n, int& lo, int& hi) {
-    const int64_t a = cu[n], b = cu[n + 1];
-    lo = (int)(a < 0 ? 0 : (a > T ? T : a));
-    hi = (int)(b < lo ? lo : (b > T ? T : b));
-  };
+  auto bounds = [&](int n, int& lo, int& hi) { seq_bounds(cu, n, T, lo, hi); };
   const bool small = N <= NTHREADS;
   int my_lo = 0, my_hi = 0;
   if (small && t < N) bounds(t, my_lo, my_hi);
@@ -1161,7 +1166,8 @@ template <typename IO, int D, int C, int VT>
 __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     const ChunkEntry* __restrict__ table, const int* __restrict__ off,
     const int* __restrict__ order, const char* __restrict__ recs, int ncb, int N, int H,
-    const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o) {
+    const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o,
+    const int32_t* __restrict__ cu, int64_t T, float* __restrict__ snaps, int snap_interval) {
   typedef Geom<D, C> Gm;
   typedef StateSmem<IO, D, C, VT> Sm;
   typedef StateOps<D, C, VT> Ops;
@@ -1221,6 +1227,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
   if (c_first < c_last) {
     seq_start = __builtin_amdgcn_readfirstlane(table[c_first].start);
     seq_end = __builtin_amdgcn_readfirstlane(table[c_last - 1].start + table[c_last - 1].len);
+  }
+  // Snapshot rows of this sequence follow those of sequences 0 .. n-1:
+  // sum over them of floor(length / snap_interval).
+  int snap_base = 0;
+  if (snaps != nullptr) {
+    __shared__ int s_snap[NTHREADS / 64];
+    int acc = 0;
+    for (int i = tid; i < n; i += NTHREADS) {
+      int lo, hi;
+      seq_bounds(cu, i, T, lo, hi);
+      acc += (hi - lo) / snap_interval;
+    }
+    for (int x = 1; x < 64; x <<= 1) acc += __shfl_xor(acc, x, 64);
+    if (l == 0) s_snap[w] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NTHREADS / 64; ++i) snap_base += s_snap[i];
+    snap_base = __builtin_amdgcn_readfirstlane(snap_base);
   }
   // Every operand of a chunk is loaded unconditionally (including Aq tiles
   // above the diagonal, which are never multiplied), so the loads form one
@@ -1432,6 +1456,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
                                     c16 * (16 / sizeof(IO))) = val;
       }
     }
+    // chunk-boundary snapshot: the state after this chunk, when the chunk
+    // ends a whole multiple of snap_interval tokens into the sequence
+    if (snaps != nullptr) {
+      const int end_tok = (ch - c_first + 1) * C;
+      if (end_tok <= seq_end - seq_start && end_tok % snap_interval == 0) {
+        float* P = snaps + ((int64_t)(snap_base + end_tok / snap_interval - 1) * H + h) * D * D;
+#pragma unroll
+        for (int i = 0; i < MS; ++i) {
+          const int ms = w + 4 * i;
+          if (ALL_MS || ms < MTD) {
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                __builtin_nontemporal_store(
+                    S[i][nt][e], P + (16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr);
+          }
+        }
+      }
+    }
     // the L2 prefetch goes last: the wave's wait counter drains in issue
     // order, so a fetch of the next chunk's operands never waits for it
     prefetch(ch);
@@ -1498,8 +1542,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
                      dim3(NTHREADS), 0, st, table, off, order, recs, (int)ws.ncb, a.N, a.H,
-                     a.h0, a.ht,
-                     (IO*)a.o);
+                     a.h0, a.ht, (IO*)a.o, a.cu_seqlens, a.T, a.snaps, a.snap_interval);
   if ((e = mark(3)) != hipSuccess) return e;
   (void)sizeof(Gm);
   return hipGetLastError();

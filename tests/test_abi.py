@@ -169,3 +169,19 @@ def test_replay_decode_validation():
     assert L.kda_replay_decode(*args(nx=W)) == INVALID
     assert L.kda_replay_decode(*args(nx=ctypes.c_void_p(8192 + 12))) == INVALID
     assert L.kda_replay_decode(*args(nx=ctypes.c_void_p(8192 + 120))) == INVALID
+
+
+def test_prefill_snapshots_validation():
+    L = kda.lib()
+    WS = ctypes.c_void_p(1 << 20)
+
+    def args(**kw):
+        return [1, P, P, P, P, P, P, 2, kw.get("T", 256), 2, 64, 64, kw.get("chunk", 64), 1.0,
+                None, None, P, kw.get("snap", P), kw.get("rows", 4), kw.get("iv", 64), WS,
+                1 << 30, None]
+    assert L.kda_chunk_prefill_snapshots(*args(iv=0)) == INVALID
+    assert L.kda_chunk_prefill_snapshots(*args(iv=96)) == INVALID  # not a multiple of 64
+    assert L.kda_chunk_prefill_snapshots(*args(snap=None)) == INVALID
+    assert L.kda_chunk_prefill_snapshots(*args(snap=P_MIS)) == INVALID
+    assert L.kda_chunk_prefill_snapshots(*args(rows=3)) == INVALID  # 256 / 64 = 4 rows needed
+    assert L.kda_chunk_prefill_snapshots(*args(chunk=48, iv=96)) == UNSUPPORTED
