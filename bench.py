@@ -185,16 +185,26 @@ def bench_prefill(steps, warmup):
         gate()
         prefill()
 
+    snaps = torch.empty((T // 256, H, K, V), device="cuda")
+
+    def prefill_snapshots():  # the state after every 256 tokens kept as well
+        kda.kda_chunk_prefill_snapshots(t["q"], t["k"], t["v"], g, beta, t["cu"], scale, 256,
+                                        h0=t["h0"], chunk=C, o=o, ht=ht, snapshots=snaps,
+                                        workspace=ws)
+
     ms_step = _time(step, steps, warmup)
     ms_step_two_calls = _time(step_two_calls, steps, warmup)
     ms_gate = _time(gate, steps, warmup)
     ms_prefill = _time(prefill, steps, warmup)
+    ms_snapshots = _time(prefill_snapshots, steps, warmup)
+    n_snaps = sum(int(c["cu"][i + 1] - c["cu"][i]) // 256 for i in range(N))
     kernels = kernel_times(t, o, ht, ws, scale, C, steps)
     pb = prefill_bytes(T, N, H, K, V)
     gb = gate_bytes(T, H, K)
     return dict(workload=w, T=T, N=N, ms_step=ms_step, ms_step_two_calls=ms_step_two_calls,
                 ms_gate=ms_gate,
                 ms_prefill=ms_prefill, prefill_bytes=pb, gate_bytes=gb,
+                ms_snapshots=ms_snapshots, snapshot_bytes=n_snaps * H * K * V * 4,
                 intra_bytes=intra_bytes(T, H, K, V), state_bytes=state_bytes(T, N, H, K, V),
                 kernels=kernels, flops=prefill_flops(T, H, K, V, C), inputs=(c, g, beta))
 
@@ -482,6 +492,11 @@ def main():
                     "mfma_frac_of_bf16_peak": p["flops"] / (p["ms_prefill"] * 1e-3) / 1e12
                     / BF16_MFMA_PEAK_TFLOPS,
                     "gate_gbs": p["gate_bytes"] / (p["ms_gate"] * 1e-3) / 1e9,
+                    "with_snapshots_every_256": {
+                        "ms": p["ms_snapshots"],
+                        "snapshot_bytes": p["snapshot_bytes"],
+                        "gbs": (p["prefill_bytes"] + p["snapshot_bytes"])
+                        / (p["ms_snapshots"] * 1e-3) / 1e9},
                     "counters": {n: ({x: r[x] for x in ("mfma_busy", "valu_busy") if x in r}
                                      if (r := measured_counters(n)) else None)
                                  for n in ("intra_kernel", "state_kernel")}},
