@@ -225,6 +225,69 @@ kda_status kda_verify(kda_dtype io, const void* q, const void* k,
                       int32_t H, int32_t K, int32_t V, float* inter_states,
                       void* o, void* stream);
 
+/*
+ * Model-layer options of kda_recurrent_decode_ex and kda_verify_ex; a NULL
+ * options pointer, or all fields zero, is the plain step.
+ *   gate_mode: 0 = g and beta are the activated log decay and strength;
+ *     1 = softplus gate, 2 = safe gate: g and beta hold the raw a and b and
+ *     the gate is applied in the kernel with kda_gate_prep's arithmetic
+ *     (tutorial, sections "Gated DeltaNet" and "KDA"; the values are those
+ *     kda_gate_prep would write).  A_log [H] is then required; dt_bias
+ *     (per_head_gate ? [H] : [H, K]) may be NULL; lower_bound (< 0) is the
+ *     safe gate's bound.
+ *   per_head_gate: g (or a) is [.., H], one log decay per head that every
+ *     key channel shares: the Gated DeltaNet gate (tutorial, "Gated
+ *     DeltaNet"), run through the same kernels.
+ *   qk_l2norm: q and k are L2-normalised in the kernel, x / sqrt(|x|^2 +
+ *     1e-6) (ReplaySSM analysis, section 3.10).
+ *   qk_heads: heads of q and k (0 = H); H must be a multiple.  Value head h
+ *     reads q and k of head h / (H / qk_heads) (grouped value heads).
+ *   o_gate: NULL, or [.., H, V] io dtype: o is replaced by the gated RMSNorm
+ *     of the layer's output norm (tutorial, "一层 GDN / KDA 的完整数据流"):
+ *     o / sqrt(mean_v o^2 + o_norm_eps) * o_norm_w[v] * act(o_gate), with
+ *     act = sigmoid (o_gate_act 0, the KDA form) or silu (1, the GDN form);
+ *     o_norm_w [V] fp32 is then required.
+ */
+typedef struct {
+  int32_t gate_mode;
+  const float* A_log;
+  const float* dt_bias;
+  float lower_bound;
+  int32_t per_head_gate;
+  int32_t qk_l2norm;
+  int32_t qk_heads;
+  const void* o_gate;
+  const float* o_norm_w;
+  float o_norm_eps;
+  int32_t o_gate_act;
+} kda_step_opts;
+
+/*
+ * kda_recurrent_decode with model-layer options.  q, k are [B, qk_heads, K];
+ * g is [B, H, K] (or [B, H] with per_head_gate); every other argument is as
+ * in kda_recurrent_decode.  With opts NULL the results are bit-identical to
+ * kda_recurrent_decode.
+ */
+kda_status kda_recurrent_decode_ex(kda_dtype io, const void* q, const void* k,
+                                   const void* v, const float* g,
+                                   const float* beta, float scale,
+                                   float* state_pool, int64_t n_slots,
+                                   const int32_t* slot_idx, int32_t B, int32_t H,
+                                   int32_t K, int32_t V, void* o,
+                                   const kda_step_opts* opts, void* stream);
+
+/*
+ * kda_verify with model-layer options.  q, k are [B, Tv, qk_heads, K]; g is
+ * [B, Tv, H, K] (or [B, Tv, H]); o_gate, when given, is [B, Tv, H, V].
+ * inter_states hold the states (the output norm does not touch them).
+ */
+kda_status kda_verify_ex(kda_dtype io, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta,
+                         float scale, const float* state_pool, int64_t n_slots,
+                         const int32_t* slot_idx, int32_t B, int32_t Tv,
+                         int32_t H, int32_t K, int32_t V, float* inter_states,
+                         void* o, const kda_step_opts* opts, void* stream);
+
 /* Longest ring kda_replay_decode accepts. */
 #define KDA_RING_MAX 32
 

@@ -24,6 +24,16 @@ _IO = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 _lib = None
 
 
+class StepOpts(ctypes.Structure):
+    """kda_step_opts of include/kda.h (model-layer options of decode/verify)."""
+    _fields_ = [("gate_mode", ctypes.c_int32), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float),
+                ("per_head_gate", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32),
+                ("qk_heads", ctypes.c_int32), ("o_gate", ctypes.c_void_p),
+                ("o_norm_w", ctypes.c_void_p), ("o_norm_eps", ctypes.c_float),
+                ("o_gate_act", ctypes.c_int32)]
+
+
 class KdaError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn} failed: {status_string(status)} ({status})")
@@ -66,6 +76,11 @@ def lib() -> ctypes.CDLL:
     L.kda_verify.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, i32,
                              i32, i32, i32, i32, vp, vp, vp]
     L.kda_verify.restype = ctypes.c_int
+    L.kda_recurrent_decode_ex.argtypes = L.kda_recurrent_decode.argtypes[:-1] + [
+        ctypes.POINTER(StepOpts), vp]
+    L.kda_recurrent_decode_ex.restype = ctypes.c_int
+    L.kda_verify_ex.argtypes = L.kda_verify.argtypes[:-1] + [ctypes.POINTER(StepOpts), vp]
+    L.kda_verify_ex.restype = ctypes.c_int
     L.kda_replay_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp,
                                     i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.kda_replay_decode.restype = ctypes.c_int
@@ -76,7 +91,8 @@ def lib() -> ctypes.CDLL:
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
             "kda_chunk_prefill_snapshots",
-            "kda_recurrent_decode", "kda_verify", "kda_replay_decode")
+            "kda_recurrent_decode", "kda_verify", "kda_replay_decode",
+            "kda_recurrent_decode_ex", "kda_verify_ex")
 
 
 def status_string(status: int) -> str:
@@ -346,3 +362,91 @@ def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, writ
         n_slots, _ptr(slot_idx), _ptr(write_pos), _ptr(force_flush), L, _ptr(ring_d),
         _ptr(ring_k), _ptr(ring_g), B, H, K, V, _ptr(o), _ptr(next_write_pos), _stream(dev)))
     return o, next_write_pos
+
+
+def _step_opts(H, lead, K, V, dev, dtype, raw_gate, per_head_gate, qk_l2norm, qk_heads, o_gate,
+               o_norm_w, o_norm_eps, o_gate_act):
+    """Checks the model-layer options and packs them (the tensors must stay
+    alive during the call)."""
+    op = StepOpts()
+    if raw_gate is not None:
+        A_log, dt_bias, lower_bound = raw_gate
+        _need(A_log, "A_log", torch.float32, (H,), dev)
+        if dt_bias is not None:
+            _need(dt_bias, "dt_bias", torch.float32, (H,) if per_head_gate else (H, K), dev)
+        op.gate_mode = 2 if lower_bound < 0 else 1
+        op.A_log = A_log.data_ptr()
+        op.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+        op.lower_bound = float(lower_bound)
+    op.per_head_gate = int(bool(per_head_gate))
+    op.qk_l2norm = int(bool(qk_l2norm))
+    op.qk_heads = int(qk_heads or 0)
+    if o_gate is not None:
+        _need(o_gate, "o_gate", dtype, lead + (H, V), dev)
+        _need(o_norm_w, "o_norm_w", torch.float32, (V,), dev)
+        op.o_gate = o_gate.data_ptr()
+        op.o_norm_w = o_norm_w.data_ptr()
+        op.o_norm_eps = float(o_norm_eps)
+        op.o_gate_act = {"sigmoid": 0, "silu": 1}[o_gate_act]
+    return op
+
+
+def kda_recurrent_decode_ex(q, k, v, g, beta, scale: float, state_pool, slot_idx, *,
+                            raw_gate=None, per_head_gate=False, qk_l2norm=False,
+                            o_gate=None, o_norm_w=None, o_norm_eps: float = 1e-6,
+                            o_gate_act: str = "sigmoid", o=None):
+    """Decode with model-layer options: q, k [B,HK,K]; v [B,H,V]; g [B,H,K]
+    (or [B,H] with per_head_gate), raw a when ``raw_gate`` = (A_log,
+    dt_bias, lower_bound) is given (then beta holds the raw b); ``o_gate``
+    [B,H,V] with ``o_norm_w`` [V] applies the gated RMSNorm to o."""
+    B, HK, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    dev = q.device
+    io = _io_dtype(q)
+    n_slots = state_pool.shape[0]
+    _need(k, "k", q.dtype, (B, HK, K), dev)
+    _need(v, "v", q.dtype, (B, H, V), dev)
+    _need(g, "g", torch.float32, (B, H) if per_head_gate else (B, H, K), dev)
+    _need(beta, "beta", torch.float32, (B, H), dev)
+    _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    op = _step_opts(H, (B,), K, V, dev, q.dtype, raw_gate, per_head_gate, qk_l2norm, HK, o_gate,
+                    o_norm_w, o_norm_eps, o_gate_act)
+    o = torch.empty((B, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (B, H, V), dev)
+    _check("kda_recurrent_decode_ex", lib().kda_recurrent_decode_ex(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale),
+        _ptr(state_pool), n_slots, _ptr(slot_idx), B, H, K, V, _ptr(o), ctypes.byref(op),
+        _stream(dev)))
+    return o
+
+
+def kda_verify_ex(q, k, v, g, beta, scale: float, state_pool, slot_idx, *, raw_gate=None,
+                  per_head_gate=False, qk_l2norm=False, o_gate=None, o_norm_w=None,
+                  o_norm_eps: float = 1e-6, o_gate_act: str = "sigmoid", inter_states=None,
+                  o=None):
+    """Verify with model-layer options (see kda_recurrent_decode_ex); q, k
+    [B,Tv,HK,K], v [B,Tv,H,V].  Returns (o, inter_states)."""
+    B, Tv, HK, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    dev = q.device
+    io = _io_dtype(q)
+    n_slots = state_pool.shape[0]
+    _need(k, "k", q.dtype, (B, Tv, HK, K), dev)
+    _need(v, "v", q.dtype, (B, Tv, H, V), dev)
+    _need(g, "g", torch.float32, (B, Tv, H) if per_head_gate else (B, Tv, H, K), dev)
+    _need(beta, "beta", torch.float32, (B, Tv, H), dev)
+    _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
+    _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
+    op = _step_opts(H, (B, Tv), K, V, dev, q.dtype, raw_gate, per_head_gate, qk_l2norm, HK,
+                    o_gate, o_norm_w, o_norm_eps, o_gate_act)
+    if inter_states is None:
+        inter_states = torch.empty((B, Tv, H, K, V), dtype=torch.float32, device=dev)
+    _need(inter_states, "inter_states", torch.float32, (B, Tv, H, K, V), dev)
+    o = torch.empty((B, Tv, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (B, Tv, H, V), dev)
+    _check("kda_verify_ex", lib().kda_verify_ex(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state_pool),
+        n_slots, _ptr(slot_idx), B, Tv, H, K, V, _ptr(inter_states), _ptr(o),
+        ctypes.byref(op), _stream(dev)))
+    return o, inter_states

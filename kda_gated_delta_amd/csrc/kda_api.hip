@@ -19,6 +19,35 @@ bool io_aligned(kda_dtype io, const void* p) {
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
 
+// Checks the model-layer options and converts them (NULL = the plain step).
+kda_status step_opts(const kda_step_opts* in, kda_dtype io, int32_t H, kda::StepOpts& out) {
+  out = kda::StepOpts{};
+  if (!in) return KDA_OK;
+  if (in->gate_mode < 0 || in->gate_mode > 2) return KDA_ERR_INVALID_ARGUMENT;
+  if (in->gate_mode != 0 && !in->A_log) return KDA_ERR_INVALID_ARGUMENT;
+  if (in->gate_mode == 2 && !(in->lower_bound < 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  if (in->qk_heads < 0 || (in->qk_heads > 0 && H % in->qk_heads != 0))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (in->o_gate) {
+    if (!in->o_norm_w || !aligned16(in->o_norm_w) || !io_aligned(io, in->o_gate))
+      return KDA_ERR_INVALID_ARGUMENT;
+    if (!(in->o_norm_eps >= 0.f) || in->o_gate_act < 0 || in->o_gate_act > 1)
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  out.gate_mode = in->gate_mode;
+  out.A_log = in->A_log;
+  out.dt_bias = in->dt_bias;
+  out.lower_bound = in->gate_mode == 2 ? in->lower_bound : 0.f;
+  out.per_head_gate = in->per_head_gate != 0;
+  out.qk_l2norm = in->qk_l2norm != 0;
+  out.qk_heads = in->qk_heads;
+  out.o_gate = in->o_gate;
+  out.o_norm_w = in->o_norm_w;
+  out.o_norm_eps = in->o_norm_eps;
+  out.o_gate_act = in->o_gate_act;
+  return KDA_OK;
+}
+
 kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const int32_t* cu_seqlens,
                            int32_t N, int64_t T, int32_t H, int32_t K, int32_t V,
@@ -149,6 +178,17 @@ kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,
                                 float* state_pool, int64_t n_slots,
                                 const int32_t* slot_idx, int32_t B, int32_t H,
                                 int32_t K, int32_t V, void* o, void* stream) {
+  return kda_recurrent_decode_ex(io, q, k, v, g, beta, scale, state_pool, n_slots, slot_idx, B,
+                                 H, K, V, o, nullptr, stream);
+}
+
+kda_status kda_recurrent_decode_ex(kda_dtype io, const void* q, const void* k,
+                                   const void* v, const float* g,
+                                   const float* beta, float scale,
+                                   float* state_pool, int64_t n_slots,
+                                   const int32_t* slot_idx, int32_t B, int32_t H,
+                                   int32_t K, int32_t V, void* o,
+                                   const kda_step_opts* opts, void* stream) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
@@ -157,8 +197,10 @@ kda_status kda_recurrent_decode(kda_dtype io, const void* q, const void* k,
     return KDA_ERR_INVALID_ARGUMENT;
   if (!io_aligned(io, v) || !io_aligned(io, o) || !aligned16(state_pool))
     return KDA_ERR_INVALID_ARGUMENT;
+  kda::StepOpts op;
+  if (kda_status st = step_opts(opts, io, H, op)) return st;
   kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
-                    B, 1, H, K, V, nullptr, o};
+                    B, 1, H, K, V, nullptr, o, op};
   return launch_status(kda::run_decode(p, (hipStream_t)stream));
 }
 
@@ -168,6 +210,16 @@ kda_status kda_verify(kda_dtype io, const void* q, const void* k,
                       const int32_t* slot_idx, int32_t B, int32_t Tv,
                       int32_t H, int32_t K, int32_t V, float* inter_states,
                       void* o, void* stream) {
+  return kda_verify_ex(io, q, k, v, g, beta, scale, state_pool, n_slots, slot_idx, B, Tv, H, K,
+                       V, inter_states, o, nullptr, stream);
+}
+
+kda_status kda_verify_ex(kda_dtype io, const void* q, const void* k,
+                         const void* v, const float* g, const float* beta,
+                         float scale, const float* state_pool, int64_t n_slots,
+                         const int32_t* slot_idx, int32_t B, int32_t Tv,
+                         int32_t H, int32_t K, int32_t V, float* inter_states,
+                         void* o, const kda_step_opts* opts, void* stream) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (B < 1 || Tv < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
@@ -177,9 +229,11 @@ kda_status kda_verify(kda_dtype io, const void* q, const void* k,
   if (!io_aligned(io, v) || !io_aligned(io, o) || !aligned16(state_pool) ||
       !aligned16(inter_states))
     return KDA_ERR_INVALID_ARGUMENT;
+  kda::StepOpts op;
+  if (kda_status st = step_opts(opts, io, H, op)) return st;
   kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale,
                     const_cast<float*>(state_pool), slot_idx, B, Tv, H, K, V,
-                    inter_states, o};
+                    inter_states, o, op};
   return launch_status(kda::run_verify(p, (hipStream_t)stream));
 }
 

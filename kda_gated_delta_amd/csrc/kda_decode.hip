@@ -18,6 +18,7 @@
 
 #include "kda.h"
 #include "kda_common.h"
+#include "kda_gate_math.h"
 #include "kda_internal.h"
 
 #include <type_traits>
@@ -139,15 +140,83 @@ __device__ __forceinline__ float4 token_step(Rows<StepShape<K, V>::RPT>& st,
   return fma4(p.qk, d, p.qs);
 }
 
+// ------------------------------------------------------ layer options
+
+// Log decay of key channel c of token row `row` (r * H + h): the activated
+// g, or the gate of the raw a ("Linear attention" tutorial, sections "Gated
+// DeltaNet" and "KDA") with the gate kernel's own functions, so that the
+// result is the value kda_gate_prep would have written.  A per-head gate
+// (the Gated DeltaNet case) decays every channel alike.
+__device__ __forceinline__ float decay_of(const float* __restrict__ g, int64_t row, int c, int K,
+                                          int h, const StepOpts& op) {
+  float x = op.per_head_gate ? g[row] : g[row * K + c];
+  if (op.gate_mode == 0) return x;
+  if (op.dt_bias) x = x + (op.per_head_gate ? op.dt_bias[h] : op.dt_bias[h * K + c]);
+  const float rate = exp_split(op.A_log[h]);
+  return op.gate_mode == 2 ? gate1<true>(x, rate, op.lower_bound)
+                           : gate1<false>(x, rate, op.lower_bound);
+}
+
+// Write strength of a token: beta, or sigmoid of the raw b.
+__device__ __forceinline__ float strength_of(float b, const StepOpts& op) {
+  return op.gate_mode != 0 ? sigmoid_fast(b) : b;
+}
+
+// Reciprocal L2 norms 1 / sqrt(sum x^2 + 1e-6) of the q and k rows of nb
+// tokens (in-kernel normalisation, ReplaySSM analysis section 3.10), one
+// wave per token; written to qn[j], kn[j].  All threads call it.
+template <typename IO, int K, int NW, typename RowOf>
+__device__ __forceinline__ void qk_rnorms(const IO* __restrict__ q, const IO* __restrict__ k,
+                                          RowOf row_of, int nb, float* qn, float* kn) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  for (int j = wv; j < nb; j += NW) {
+    const int64_t row = row_of(j);
+    float sq2 = 0.f, sk2 = 0.f;
+    for (int c = lane; c < K; c += 64) {
+      const float a = to_f32(q[row * K + c]), b = to_f32(k[row * K + c]);
+      sq2 = fmaf(a, a, sq2);
+      sk2 = fmaf(b, b, sk2);
+    }
+    sq2 = xor_sum(sq2, 1);
+    sk2 = xor_sum(sk2, 1);
+    if (lane == 0) {
+      qn[j] = 1.f / sqrtf(sq2 + 1e-6f);
+      kn[j] = 1.f / sqrtf(sk2 + 1e-6f);
+    }
+  }
+}
+
+// Gated RMSNorm of one (token, head) output (the layer's o_norm: RMS over the
+// V columns, times a weight and an activation of the gate z): the CG
+// threads of row group 0 hold o, four columns each, all in wave 0.  Every
+// thread calls it (the sum is a butterfly over aligned groups of CG lanes).
+template <typename IO, int V, int CG>
+__device__ __forceinline__ float4 out_norm(float4 x, bool holder, const IO* __restrict__ z,
+                                           int c0, const StepOpts& op) {
+  float ss = holder ? fmaf(x.x, x.x, fmaf(x.y, x.y, fmaf(x.z, x.z, x.w * x.w))) : 0.f;
+#pragma unroll
+  for (int m = 1; m < CG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  if (!holder) return x;
+  const float f = 1.f / sqrtf(ss / (float)V + op.o_norm_eps);
+  const float4 zz = load4(z + c0), w = load4(op.o_norm_w + c0);
+  auto act = [&](float u) {
+    const float sg = 1.f / (1.f + expf(-u));
+    return op.o_gate_act ? u * sg : sg;
+  };
+  return make_float4(x.x * f * w.x * act(zz.x), x.y * f * w.y * act(zz.y),
+                     x.z * f * w.z * act(zz.z), x.w * f * w.w * act(zz.w));
+}
+
 template <typename IO, int K, int V>
 __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, float* __restrict__ pool,
-    const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o) {
+    const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o, StepOpts op) {
   constexpr int VS = slice_cols<V>(), NS = V / VS;
   typedef StepShape<K, VS> Sh;
   __shared__ float sq[K], sk[K], sa[K];
+  __shared__ float sn[2];
   __shared__ float red[Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
   const int64_t rh = blockIdx.x / NS;  // r * H + h
@@ -163,22 +232,36 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_ke
   float4* s = st.s;
 #pragma unroll
   for (int i = 0; i < Sh::RPT; ++i) s[i] = load4_nt(S + (rg + Sh::RG * i) * V + c0);
+  // q and k rows: grouped heads share them (value head h reads q/k head
+  // h / (H / HK))
+  const int HK = op.qk_heads > 0 ? op.qk_heads : H;
+  const int64_t qk = (int64_t)r * HK + h / (H / HK);
+  float qn = 1.f, kn = 1.f;
+  if (op.qk_l2norm) {
+    qk_rnorms<IO, K, Sh::NW>(q, k, [&](int) { return qk; }, 1, sn, sn + 1);
+    __syncthreads();
+    qn = sn[0];
+    kn = sn[1];
+  }
   for (int c = t; c < K; c += Sh::NT) {
-    sq[c] = to_f32(q[rh * K + c]);
-    sk[c] = to_f32(k[rh * K + c]);
-    sa[c] = expf(g[rh * K + c]);
+    sq[c] = to_f32(q[qk * K + c]) * qn;
+    sk[c] = to_f32(k[qk * K + c]) * kn;
+    sa[c] = expf(decay_of(g, rh, c, K, h, op));
   }
   const float4 vv = load4(v + rh * V + c0);
-  const float b = beta[rh];
+  const float b = strength_of(beta[rh], op);
   __syncthreads();
   const float4 oq = token_step<K, VS>(st, sq, sk, sa, vv, b, red);
-  if (rg == 0) store4(o + rh * V + c0, scale * oq);
+  float4 out = scale * oq;
+  if (op.o_gate != nullptr)
+    out = out_norm<IO, V, Sh::CG>(out, rg == 0, static_cast<const IO*>(op.o_gate) + rh * V, c0, op);
+  if (rg == 0) store4(o + rh * V + c0, out);
 #pragma unroll
   for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
 }
 
 // Draft tokens are staged TVB at a time.
-constexpr int TVB = 8;
+constexpr int TVB = 4;
 
 template <typename IO, int K, int V>
 __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_kernel(
@@ -186,10 +269,12 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale,
     const float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
-    int Tv, int H, float* __restrict__ inter, IO* __restrict__ o) {
+    int Tv, int H, float* __restrict__ inter, IO* __restrict__ o, StepOpts op) {
   constexpr int VS = slice_cols<V>(), NS = V / VS;
   typedef StepShape<K, VS> Sh;
   __shared__ float sq[TVB][K], sk[TVB][K], sa[TVB][K], sb[TVB];
+  __shared__ float sqn[TVB], skn[TVB];
+  __shared__ __align__(16) float sout[TVB][V];
   __shared__ float red[2][Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
   const int rh = blockIdx.x / NS;  // r * H + h
@@ -211,14 +296,24 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
   for (int s0 = 0; s0 < Tv; s0 += TVB) {
     const int nb = (Tv - s0 < TVB) ? Tv - s0 : TVB;
     if (s0 > 0) __syncthreads();  // previous batch fully consumed
+    // q/k rows of the batch's tokens (grouped heads share them)
+    const int HK = op.qk_heads > 0 ? op.qk_heads : H;
+    if (op.qk_l2norm) {
+      qk_rnorms<IO, K, Sh::NW>(
+          q, k, [&](int j) { return ((int64_t)r * Tv + s0 + j) * HK + h / (H / HK); }, nb, sqn,
+          skn);
+      __syncthreads();
+    }
     for (int e = t; e < nb * K; e += Sh::NT) {
       const int j = e / K, c = e % K;
-      const int64_t src = (((int64_t)r * Tv + s0 + j) * H + h) * K + c;
-      sq[j][c] = to_f32(q[src]);
-      sk[j][c] = to_f32(k[src]);
-      sa[j][c] = expf(g[src]);
+      const int64_t row = ((int64_t)r * Tv + s0 + j) * H + h;
+      const int64_t qrow = ((int64_t)r * Tv + s0 + j) * HK + h / (H / HK);
+      const float qn = op.qk_l2norm ? sqn[j] : 1.f, kn = op.qk_l2norm ? skn[j] : 1.f;
+      sq[j][c] = to_f32(q[qrow * K + c]) * qn;
+      sk[j][c] = to_f32(k[qrow * K + c]) * kn;
+      sa[j][c] = expf(decay_of(g, row, c, K, h, op));
     }
-    if (t < nb) sb[t] = beta[((int64_t)r * Tv + s0 + t) * H + h];
+    if (t < nb) sb[t] = strength_of(beta[((int64_t)r * Tv + s0 + t) * H + h], op);
     float4 vv[TVB];
 #pragma unroll
     for (int j = 0; j < TVB; ++j)
@@ -231,10 +326,28 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
         const float4 oq = token_step<K, VS>(st, sq[j], sk[j], sa[j], vv[j], sb[j],
                                             red[step & 1]);
         ++step;
-        if (rg == 0) store4(o + rsh * V + c0, scale * oq);
+        if (rg == 0) {
+          if (op.o_gate != nullptr)  // normalised after the batch
+            *reinterpret_cast<float4*>(&sout[j][c0]) = scale * oq;
+          else
+            store4(o + rsh * V + c0, scale * oq);
+        }
         float* I = inter + rsh * (int64_t)(K * V);
 #pragma unroll
         for (int i = 0; i < Sh::RPT; ++i) store4_nt(I + (rg + Sh::RG * i) * V + c0, s[i]);
+      }
+    }
+    if (op.o_gate != nullptr) {
+      // gated RMSNorm of the batch's outputs, one wave per token
+      __syncthreads();
+      const int lane = t & 63, wv = t >> 6;
+      for (int j = wv; j < nb; j += Sh::NW) {
+        const int64_t rsh = ((int64_t)r * Tv + s0 + j) * H + h;
+        const bool holder = lane < Sh::CG;
+        const float4 x = holder ? *reinterpret_cast<const float4*>(&sout[j][4 * lane]) : f4(0.f);
+        const float4 y = out_norm<IO, V, Sh::CG>(x, holder, static_cast<const IO*>(op.o_gate) + rsh * V,
+                                                 4 * lane, op);
+        if (holder) store4(o + rsh * V + 4 * lane, y);
       }
     }
   }
@@ -498,37 +611,31 @@ hipError_t replay_k(const ReplayArgs& a, hipStream_t st) {
 }
 
 template <typename IO, int K, int V>
-hipError_t launch_decode(const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float scale,
-                         float* pool, const int32_t* slot_idx, int B, int H,
-                         void* o, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   typedef StepShape<K, slice_cols<V>()> Sh;
-  hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)B * H * (V / slice_cols<V>())), dim3(Sh::NT),
-                     0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
-                     scale, pool, slot_idx, H, (IO*)o);
+  hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)a.B * a.H * (V / slice_cols<V>())),
+                     dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
+                     a.g, a.beta, a.scale, a.pool, a.slot_idx, a.H, (IO*)a.o, a.opts);
   return hipGetLastError();
 }
 
 template <typename IO, int K, int V>
-hipError_t launch_verify(const void* q, const void* k, const void* v,
-                         const float* g, const float* beta, float scale,
-                         const float* pool, const int32_t* slot_idx, int B,
-                         int Tv, int H, float* inter, void* o,
-                         hipStream_t stream) {
+hipError_t launch_verify(const DecodeArgs& a, hipStream_t stream) {
   typedef StepShape<K, slice_cols<V>()> Sh;
-  hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)B * H * (V / slice_cols<V>())), dim3(Sh::NT),
-                     0, stream, (const IO*)q, (const IO*)k, (const IO*)v, g, beta,
-                     scale, pool, slot_idx, Tv, H, inter, (IO*)o);
+  hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)a.B * a.H * (V / slice_cols<V>())),
+                     dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
+                     a.g, a.beta, a.scale, a.pool, a.slot_idx, a.Tv, a.H, a.inter, (IO*)a.o,
+                     a.opts);
   return hipGetLastError();
 }
 
 template <typename IO, int K>
 hipError_t decode_v(const DecodeArgs& a, hipStream_t st) {
   switch (a.V) {
-    case 16: return launch_decode<IO, K, 16>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
-    case 32: return launch_decode<IO, K, 32>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
-    case 64: return launch_decode<IO, K, 64>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
-    case 128: return launch_decode<IO, K, 128>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.H, a.o, st);
+    case 16: return launch_decode<IO, K, 16>(a, st);
+    case 32: return launch_decode<IO, K, 32>(a, st);
+    case 64: return launch_decode<IO, K, 64>(a, st);
+    case 128: return launch_decode<IO, K, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }
@@ -547,10 +654,10 @@ hipError_t decode_k(const DecodeArgs& a, hipStream_t st) {
 template <typename IO, int K>
 hipError_t verify_v(const DecodeArgs& a, hipStream_t st) {
   switch (a.V) {
-    case 16: return launch_verify<IO, K, 16>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
-    case 32: return launch_verify<IO, K, 32>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
-    case 64: return launch_verify<IO, K, 64>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
-    case 128: return launch_verify<IO, K, 128>(a.q, a.k, a.v, a.g, a.beta, a.scale, a.pool, a.slot_idx, a.B, a.Tv, a.H, a.inter, a.o, st);
+    case 16: return launch_verify<IO, K, 16>(a, st);
+    case 32: return launch_verify<IO, K, 32>(a, st);
+    case 64: return launch_verify<IO, K, 64>(a, st);
+    case 128: return launch_verify<IO, K, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -16,6 +16,21 @@ struct GateArgs {
   float *g, *beta;
 };
 
+// Model-layer options of decode and verify (kda_step_opts); all zero is the
+// plain step.
+struct StepOpts {
+  int gate_mode;  // 0: g, beta activated; 1: softplus gate, 2: safe gate (raw a, b given)
+  const float *A_log, *dt_bias;
+  float lower_bound;
+  int per_head_gate;  // g (or a) and dt_bias per head: every key channel decays alike
+  int qk_l2norm;      // q, k L2-normalised in the kernel
+  int qk_heads;       // heads of q and k (0: H)
+  const void* o_gate;      // io dtype [.., H, V]: gated RMSNorm of o when not null
+  const float* o_norm_w;   // [V]
+  float o_norm_eps;
+  int o_gate_act;          // 0: sigmoid, 1: silu
+};
+
 struct DecodeArgs {
   bool bf16_io;
   const void *q, *k, *v;
@@ -26,6 +41,7 @@ struct DecodeArgs {
   int B, Tv, H, K, V;
   float* inter;  // verify only
   void* o;
+  StepOpts opts;
 };
 
 struct ReplayArgs {

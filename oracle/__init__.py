@@ -5,8 +5,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``kda_gated_delta_amd``) never imports it, and this package imports nothing
 from there.
 
-The arithmetic lives in ``kda_oracle.c`` (plain C, double precision, token by
-token); this module only marshals numpy arrays into it.  Every array handed
+The recurrence's arithmetic lives in ``kda_oracle.c`` (plain C, double
+precision, token by token); this module marshals numpy arrays into it, and
+holds two row-wise helpers of the layer around the recurrence (``l2norm``,
+``gated_rmsnorm``) as plain float64 numpy.  Every array handed
 in is converted to float64, which is exact for the fp32 and bf16 values the
 GPU consumes.  See ``kda_oracle.c`` for the passages each function follows.
 """
@@ -177,3 +179,21 @@ def verify(q, k, v, g, beta, scale: float, pool, slot_idx,
     if rc != 0:
         raise ValueError("slot index out of range")
     return o, inter
+
+
+def l2norm(x, eps: float = 1e-6):
+    """x / sqrt(sum x^2 + eps) over the last axis, float64: the in-kernel
+    q/k normalisation (ReplaySSM analysis, section 3.10, eps 1e-6)."""
+    x = _f64(x)
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + eps)
+
+
+def gated_rmsnorm(o, z, w, eps: float, act: str = "sigmoid"):
+    """The layer's gated output norm ("Linear attention" tutorial, section
+    "一层 GDN / KDA 的完整数据流"; the KDA form takes a sigmoid of the gate):
+    o over the RMS of its last axis (plus eps), times the weight w and
+    act(z), act = sigmoid or silu (z sigmoid(z)).  float64."""
+    o, z, w = _f64(o), _f64(z), _f64(w)
+    rms = np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return o / rms * w * (sg if act == "sigmoid" else z * sg)

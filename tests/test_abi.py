@@ -185,3 +185,30 @@ def test_prefill_snapshots_validation():
     assert L.kda_chunk_prefill_snapshots(*args(snap=P_MIS)) == INVALID
     assert L.kda_chunk_prefill_snapshots(*args(rows=3)) == INVALID  # 256 / 64 = 4 rows needed
     assert L.kda_chunk_prefill_snapshots(*args(chunk=48, iv=96)) == UNSUPPORTED
+
+
+def test_step_options_validation():
+    L = kda.lib()
+    op = kda.StepOpts()
+
+    def dec(o=op, H=4):
+        return L.kda_recurrent_decode_ex(1, P, P, P, P, P, 1.0, P, 8, P, 2, H, 64, 64, P,
+                                         ctypes.byref(o), None)
+    op.gate_mode = 3
+    assert dec() == INVALID
+    op.gate_mode = 1  # raw gate without A_log
+    assert dec() == INVALID
+    op.A_log = 4096
+    op.gate_mode = 2  # safe gate needs a negative bound
+    assert dec() == INVALID
+    op.gate_mode, op.qk_heads = 0, 3  # 4 value heads are not a multiple of 3
+    assert dec() == INVALID
+    op.qk_heads, op.o_gate = 2, 4096  # output gate without a norm weight
+    assert dec() == INVALID
+    op.o_norm_w, op.o_gate_act = 4096, 2
+    assert dec() == INVALID
+    op.o_gate_act, op.o_norm_eps = 0, -1.0
+    assert dec() == INVALID
+    v = L.kda_verify_ex(1, P, P, P, P, P, 1.0, P, 8, P, 2, 0, 4, 64, 64, P, P,
+                        ctypes.byref(kda.StepOpts()), None)
+    assert v == INVALID  # Tv = 0

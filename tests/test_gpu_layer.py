@@ -1,0 +1,186 @@
+"""Model-layer options of decode and verify (kda_recurrent_decode_ex,
+kda_verify_ex): the gate applied in the kernel from raw inputs, the per-head
+(Gated DeltaNet) gate, grouped q/k heads, in-kernel q/k L2 normalisation and
+the gated RMSNorm of the output.  Options that restate another path exactly
+are checked bit for bit against it; the rest against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import kda_gated_delta_amd as kda
+import kda_synth
+import oracle
+from kda_testutil import TOL, TORCH_IO, assert_io_output, dev, gates_f32, host, rel_err_blocks
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(io, B=6, H=4, K=64, V=64, n_slots=9, seed=0, Tv=None, regime="config"):
+    c = kda_synth.decode_case(B, H, K, V, n_slots, io, seed=seed, regime=regime, Tv=Tv,
+                              n_padding=1)
+    return c
+
+
+def _t(c):
+    io = TORCH_IO[c["io"]]
+    return {x: dev(c[x], io) for x in "qkv"}
+
+
+def test_no_options_is_the_plain_step():
+    for io in ("f32", "bf16"):
+        c = _case(io, seed=1)
+        t = _t(c)
+        g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+        pa, pb = dev(c["pool"]), dev(c["pool"])
+        idx = dev(c["slot_idx"], torch.int32)
+        o1 = kda.kda_recurrent_decode(t["q"], t["k"], t["v"], dev(g), dev(beta), 0.125, pa, idx)
+        o2 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], dev(g), dev(beta), 0.125, pb,
+                                         idx)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(pa, pb)
+
+
+@pytest.mark.parametrize("lb", [0.0, -5.0])
+def test_raw_gate_in_decode_equals_gate_prep_then_decode(lb):
+    c = _case("bf16", K=128, V=128, seed=2)
+    t = _t(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    A_log, dtb = dev(c["A_log"]), dev(c["dt_bias"])
+    g, beta = kda.kda_gate_prep(a, b, A_log, dtb, lower_bound=lb)
+    pa, pb = dev(c["pool"]), dev(c["pool"])
+    idx = dev(c["slot_idx"], torch.int32)
+    o1 = kda.kda_recurrent_decode(t["q"], t["k"], t["v"], g, beta, 0.09, pa, idx)
+    o2 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], a, b, 0.09, pb, idx,
+                                     raw_gate=(A_log, dtb, lb))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(pa, pb)
+
+
+def test_per_head_gate_equals_broadcast_gate():
+    # the Gated DeltaNet gate: one decay per head, shared by every key channel
+    c = _case("bf16", K=64, V=128, seed=3)
+    t = _t(c)
+    B, H, K = c["B"], c["H"], c["K"]
+    r = np.random.default_rng(3)
+    a_h = r.standard_normal((B, H)).astype(np.float32)
+    dtb_h = (0.5 * r.standard_normal(H)).astype(np.float32)
+    A_log = dev(c["A_log"])
+    b = dev(c["b"])
+    idx = dev(c["slot_idx"], torch.int32)
+    # activated per-head g against the same g broadcast over K
+    g_h = -np.abs(a_h)
+    pa, pb = dev(c["pool"]), dev(c["pool"])
+    o1 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], dev(np.repeat(g_h[..., None], K, 2)),
+                                     b, 0.1, pa, idx)
+    o2 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], dev(g_h), b, 0.1, pb, idx,
+                                     per_head_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(pa, pb)
+    # raw per-head gate (a [B,H], dt_bias [H]) against the per-channel raw gate
+    pa, pb = dev(c["pool"]), dev(c["pool"])
+    o1 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], dev(np.repeat(a_h[..., None], K, 2)),
+                                     b, 0.1, pa, idx,
+                                     raw_gate=(A_log, dev(np.repeat(dtb_h[:, None], K, 1)), 0.0))
+    o2 = kda.kda_recurrent_decode_ex(t["q"], t["k"], t["v"], dev(a_h), b, 0.1, pb, idx,
+                                     raw_gate=(A_log, dev(dtb_h), 0.0), per_head_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(pa, pb)
+
+
+def test_grouped_qk_heads_equal_repeated_heads():
+    c = _case("bf16", H=8, K=128, V=64, seed=4)
+    B, H, K = c["B"], c["H"], c["K"]
+    io = TORCH_IO["bf16"]
+    qg, kg = c["q"][:, :2], c["k"][:, :2]  # 2 q/k heads for 8 value heads
+    rep = lambda x: np.repeat(x, 4, axis=1)
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    idx = dev(c["slot_idx"], torch.int32)
+    pa, pb = dev(c["pool"]), dev(c["pool"])
+    o1 = kda.kda_recurrent_decode(dev(rep(qg), io), dev(rep(kg), io), dev(c["v"], io), dev(g),
+                                  dev(beta), 0.1, pa, idx)
+    o2 = kda.kda_recurrent_decode_ex(dev(qg, io), dev(kg, io), dev(c["v"], io), dev(g), dev(beta),
+                                     0.1, pb, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(pa, pb)
+
+
+def _raw_qk(c, seed):
+    """Un-normalised q and k of the case's shape, rounded to its io dtype."""
+    r = np.random.default_rng(seed)
+    q = r.standard_normal(c["q"].shape) * 0.7
+    k = r.standard_normal(c["k"].shape) * 1.3
+    rt = lambda x: torch.from_numpy(x).to(TORCH_IO[c["io"]]).to(torch.float64).numpy()
+    return rt(q), rt(k)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("act", ["sigmoid", "silu"])
+def test_l2norm_and_output_norm_match_oracle(io, act):
+    c = _case(io, K=128, V=128, seed=5, regime="long")
+    B, H, K, V = c["B"], c["H"], c["K"], c["V"]
+    q, k = _raw_qk(c, 5)
+    r = np.random.default_rng(6)
+    z = torch.from_numpy(r.standard_normal((B, H, V))).to(TORCH_IO[io])
+    w = (1.0 + 0.1 * r.standard_normal(V)).astype(np.float32)
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    pool = dev(c["pool"])
+    idx = dev(c["slot_idx"], torch.int32)
+    o = kda.kda_recurrent_decode_ex(dev(q, TORCH_IO[io]), dev(k, TORCH_IO[io]),
+                                    dev(c["v"], TORCH_IO[io]), dev(g), dev(beta), K ** -0.5, pool,
+                                    idx, qk_l2norm=True, o_gate=z.cuda(), o_norm_w=dev(w),
+                                    o_norm_eps=1e-6, o_gate_act=act)
+    torch.cuda.synchronize()
+    o_ref, pool_ref = oracle.decode(oracle.l2norm(q), oracle.l2norm(k), c["v"], g, beta,
+                                    K ** -0.5, c["pool"], c["slot_idx"])
+    o_ref = oracle.gated_rmsnorm(o_ref, z.to(torch.float64).numpy(), w, 1e-6, act)
+    live = c["slot_idx"] >= 0
+    assert_io_output(host(o)[live], o_ref[live], io, 1)
+    np.testing.assert_array_equal(host(o)[~live], 0.0)
+    lv = c["slot_idx"][live]
+    assert rel_err_blocks(host(pool)[lv], pool_ref[lv], 2) <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_verify_with_every_option(io):
+    # raw safe gate, grouped heads, in-kernel L2 norm and the output norm,
+    # against the oracle, and each step against the same options in decode
+    Tv, B, H, HK, K, V = 5, 4, 4, 2, 64, 64
+    c = _case(io, B=B, H=H, K=K, V=V, seed=7, Tv=Tv, regime="long")
+    q, k = _raw_qk(c, 7)
+    q, k = q[:, :, :HK], k[:, :, :HK]
+    r = np.random.default_rng(8)
+    z = r.standard_normal((B, Tv, H, V))
+    z = torch.from_numpy(z).to(TORCH_IO[io])
+    w = (1.0 + 0.1 * r.standard_normal(V)).astype(np.float32)
+    lb = -4.0
+    A_log, dtb = dev(c["A_log"]), dev(c["dt_bias"])
+    io_t = TORCH_IO[io]
+    qd, kd, vd = dev(q, io_t), dev(k, io_t), dev(c["v"], io_t)
+    ad, bd = dev(c["a"]), dev(c["b"])
+    pool = dev(c["pool"])
+    idx = dev(c["slot_idx"], torch.int32)
+    opts = dict(raw_gate=(A_log, dtb, lb), qk_l2norm=True, o_gate=z.cuda(), o_norm_w=dev(w),
+                o_norm_eps=1e-6, o_gate_act="sigmoid")
+    o, inter = kda.kda_verify_ex(qd, kd, vd, ad, bd, K ** -0.5, pool, idx, **opts)
+    torch.cuda.synchronize()
+    # oracle: gates, normalised q/k repeated over the value heads, recurrence, output norm
+    g, beta = oracle.gate(c["a"].reshape(B * Tv, H, K), c["b"].reshape(B * Tv, H), c["A_log"],
+                          c["dt_bias"], lb)
+    g, beta = g.reshape(B, Tv, H, K), beta.reshape(B, Tv, H)
+    rep = lambda x: np.repeat(x, H // HK, axis=2)
+    o_ref, inter_ref = oracle.verify(rep(oracle.l2norm(q)), rep(oracle.l2norm(k)), c["v"], g, beta,
+                                     K ** -0.5, c["pool"], c["slot_idx"])
+    o_ref = oracle.gated_rmsnorm(o_ref, z.to(torch.float64).numpy(), w, 1e-6)
+    live = c["slot_idx"] >= 0
+    assert_io_output(host(o)[live], o_ref[live], io, 1)
+    assert rel_err_blocks(host(inter)[live], inter_ref[live], 2) <= TOL[io]
+    # every step equals the decode with the same options
+    pool2 = dev(c["pool"])
+    for s in range(Tv):
+        sl = lambda x: x[:, s].contiguous()
+        o_d = kda.kda_recurrent_decode_ex(sl(qd), sl(kd), sl(vd), sl(ad), sl(bd), K ** -0.5, pool2,
+                                          idx, raw_gate=(A_log, dtb, lb), qk_l2norm=True,
+                                          o_gate=sl(z.cuda()), o_norm_w=dev(w), o_norm_eps=1e-6)
+        assert torch.equal(o_d, o[:, s]), s
+        lvt = torch.from_numpy(live).cuda()
+        assert torch.equal(pool2[idx[lvt].long()], inter[lvt, s]), s

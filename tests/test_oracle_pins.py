@@ -412,3 +412,46 @@ def test_bad_cu_seqlens_rejected():
     q, k, v, g, beta, cu, h0 = _random_problem(41, [4, 4], 1, 4, 4)
     with pytest.raises(ValueError):
         oracle.prefill(q, k, v, g, beta, [0, 5, 3, 8], 1.0)
+
+
+# ------------------------------------------------- layer helpers (norms)
+
+def test_l2norm_closed_forms():
+    # (3, 4) has norm 5: with eps 0 the result is (0.6, 0.8); eps only
+    # shrinks the norm to 5 / sqrt(25 + eps) and keeps the direction
+    np.testing.assert_allclose(oracle.l2norm(np.array([3.0, 4.0]), eps=0.0), [0.6, 0.8],
+                               rtol=0, atol=1e-15)
+    y = oracle.l2norm(np.array([[3.0, 4.0], [0.0, 2e-3]]), eps=1e-6)
+    np.testing.assert_allclose(np.linalg.norm(y[0]), 5.0 / np.sqrt(25.0 + 1e-6), rtol=1e-15)
+    np.testing.assert_allclose(y[0] / np.linalg.norm(y[0]), [0.6, 0.8], rtol=1e-15)
+    # a small row: |x|^2 = 4e-6, so |y| = 2e-3 / sqrt(5e-6)
+    np.testing.assert_allclose(y[1], [0.0, 2e-3 / np.sqrt(5e-6)], rtol=1e-14)
+    # rows are independent and eps = 0 is scale-free
+    r = np.random.default_rng(4)
+    x = r.standard_normal((5, 16))
+    np.testing.assert_allclose(oracle.l2norm(7.5 * x, eps=0.0), oracle.l2norm(x, eps=0.0),
+                               rtol=1e-14)
+
+
+def test_gated_rmsnorm_closed_forms():
+    w = np.array([1.0, 2.0, 3.0, 4.0])
+    o = np.array([1.0, -1.0, 1.0, -1.0])  # RMS exactly 1
+    z0 = np.zeros(4)
+    # sigmoid(0) = 1/2; silu(0) = 0
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o, z0, w, 0.0), [0.5, -1.0, 1.5, -2.0],
+                               rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(oracle.gated_rmsnorm(o, z0, w, 0.0, act="silu"), 0.0)
+    # o = (2, 0): RMS sqrt(2); z = ln 3 gives sigmoid 3/4 and silu (3/4) ln 3
+    o2, w2, z2 = np.array([2.0, 0.0]), np.array([1.0, 1.0]), np.full(2, np.log(3.0))
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o2, z2, w2, 0.0),
+                               [np.sqrt(2.0) * 0.75, 0.0], rtol=1e-15)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o2, z2, w2, 0.0, act="silu"),
+                               [np.sqrt(2.0) * 0.75 * np.log(3.0), 0.0], rtol=1e-15)
+    # eps enters under the root: RMS^2 = 2 + eps
+    np.testing.assert_allclose(oracle.gated_rmsnorm(o2, z2, w2, 2.0)[0], 2.0 / 2.0 * 0.75,
+                               rtol=1e-15)
+    # invariant to the scale of o when eps = 0
+    r = np.random.default_rng(5)
+    x, z, ww = r.standard_normal((3, 8)), r.standard_normal((3, 8)), r.standard_normal(8)
+    np.testing.assert_allclose(oracle.gated_rmsnorm(40.0 * x, z, ww, 0.0),
+                               oracle.gated_rmsnorm(x, z, ww, 0.0), rtol=1e-13)
