@@ -165,6 +165,45 @@ kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* 
                                        size_t workspace_bytes, void* stream);
 
 /*
+ * Model-layer options of kda_chunk_prefill_ex; NULL or all zero is
+ * kda_chunk_prefill.
+ *   gate_mode, A_log, dt_bias, lower_bound: as in kda_step_opts (the gate
+ *     applied in the kernel from raw a and b, as kda_chunk_prefill_gated).
+ *   per_head_gate: g (or a) is [T, H] and dt_bias [H]: one log decay per
+ *     (token, head) shared by every key channel (the Gated DeltaNet gate,
+ *     tutorial section "Gated DeltaNet"); H must be a multiple of 4.
+ *   qk_heads: heads of q and k (0 = H; H a multiple): value head h reads q
+ *     and k of head h / (H / qk_heads).
+ *   snapshots, snapshot_rows, snapshot_interval: chunk-boundary states as in
+ *     kda_chunk_prefill_snapshots (snapshots NULL = none).
+ */
+typedef struct {
+  int32_t gate_mode;
+  const float* A_log;
+  const float* dt_bias;
+  float lower_bound;
+  int32_t per_head_gate;
+  int32_t qk_heads;
+  float* snapshots;
+  int64_t snapshot_rows;
+  int32_t snapshot_interval;
+} kda_prefill_opts;
+
+/*
+ * kda_chunk_prefill with model-layer options: q, k are [T, qk_heads, K]; g
+ * is [T, H, K] (or [T, H] with per_head_gate), raw a when gate_mode != 0
+ * (then beta holds the raw b).  Workspace, outputs and errors as in
+ * kda_chunk_prefill; with opts NULL the results are bit-identical to it.
+ */
+kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                float scale, const float* h0, float* ht, void* o,
+                                void* workspace, size_t workspace_bytes,
+                                const kda_prefill_opts* opts, void* stream);
+
+/*
  * kda_chunk_prefill_gated with kernel timing marks, for benchmarks and
  * profilers.  Same arguments, work and results as kda_chunk_prefill_gated;
  * in addition it records four caller-created HIP events (hipEvent_t passed

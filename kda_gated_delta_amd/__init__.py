@@ -24,6 +24,15 @@ _IO = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 _lib = None
 
 
+class PrefillOpts(ctypes.Structure):
+    """kda_prefill_opts of include/kda.h (model-layer options of prefill)."""
+    _fields_ = [("gate_mode", ctypes.c_int32), ("A_log", ctypes.c_void_p),
+                ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float),
+                ("per_head_gate", ctypes.c_int32), ("qk_heads", ctypes.c_int32),
+                ("snapshots", ctypes.c_void_p), ("snapshot_rows", ctypes.c_int64),
+                ("snapshot_interval", ctypes.c_int32)]
+
+
 class StepOpts(ctypes.Structure):
     """kda_step_opts of include/kda.h (model-layer options of decode/verify)."""
     _fields_ = [("gate_mode", ctypes.c_int32), ("A_log", ctypes.c_void_p),
@@ -76,6 +85,9 @@ def lib() -> ctypes.CDLL:
     L.kda_verify.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, i32,
                              i32, i32, i32, i32, vp, vp, vp]
     L.kda_verify.restype = ctypes.c_int
+    L.kda_chunk_prefill_ex.argtypes = L.kda_chunk_prefill.argtypes[:-1] + [
+        ctypes.POINTER(PrefillOpts), vp]
+    L.kda_chunk_prefill_ex.restype = ctypes.c_int
     L.kda_recurrent_decode_ex.argtypes = L.kda_recurrent_decode.argtypes[:-1] + [
         ctypes.POINTER(StepOpts), vp]
     L.kda_recurrent_decode_ex.restype = ctypes.c_int
@@ -92,7 +104,7 @@ EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_s
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
             "kda_chunk_prefill_snapshots",
             "kda_recurrent_decode", "kda_verify", "kda_replay_decode",
-            "kda_recurrent_decode_ex", "kda_verify_ex")
+            "kda_recurrent_decode_ex", "kda_verify_ex", "kda_chunk_prefill_ex")
 
 
 def status_string(status: int) -> str:
@@ -450,3 +462,56 @@ def kda_verify_ex(q, k, v, g, beta, scale: float, state_pool, slot_idx, *, raw_g
         n_slots, _ptr(slot_idx), B, Tv, H, K, V, _ptr(inter_states), _ptr(o),
         ctypes.byref(op), _stream(dev)))
     return o, inter_states
+
+
+def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate=None,
+                         per_head_gate=False, h0=None, output_final_state: bool = True,
+                         chunk: int = 64, o=None, ht=None, snapshots=None,
+                         snapshot_interval: int = 0, workspace=None):
+    """Prefill with model-layer options: q, k [T,HK,K]; v [T,H,V]; g [T,H,K]
+    (or [T,H] with per_head_gate), raw a when ``raw_gate`` = (A_log,
+    dt_bias, lower_bound) is given (then beta holds the raw b); snapshots as
+    in kda_chunk_prefill_snapshots.  Returns (o, ht)."""
+    T, HK, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    dev = q.device
+    io = _io_dtype(q)
+    N = cu_seqlens.shape[0] - 1
+    _need(k, "k", q.dtype, (T, HK, K), dev)
+    _need(v, "v", q.dtype, (T, H, V), dev)
+    _need(g, "g", torch.float32, (T, H) if per_head_gate else (T, H, K), dev)
+    _need(beta, "beta", torch.float32, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, (N, H, K, V), dev)
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    if ht is not None:
+        _need(ht, "ht", torch.float32, (N, H, K, V), dev)
+    o = torch.empty((T, H, V), dtype=q.dtype, device=dev) if o is None else o
+    _need(o, "o", q.dtype, (T, H, V), dev)
+    op = PrefillOpts()
+    if raw_gate is not None:
+        A_log, dt_bias, lower_bound = raw_gate
+        _need(A_log, "A_log", torch.float32, (H,), dev)
+        if dt_bias is not None:
+            _need(dt_bias, "dt_bias", torch.float32, (H,) if per_head_gate else (H, K), dev)
+        op.gate_mode = 2 if lower_bound < 0 else 1
+        op.A_log = A_log.data_ptr()
+        op.dt_bias = None if dt_bias is None else dt_bias.data_ptr()
+        op.lower_bound = float(lower_bound)
+    op.per_head_gate = int(bool(per_head_gate))
+    op.qk_heads = HK
+    if snapshots is not None:
+        _need(snapshots, "snapshots", torch.float32, (snapshots.shape[0], H, K, V), dev)
+        op.snapshots = snapshots.data_ptr()
+        op.snapshot_rows = snapshots.shape[0]
+        op.snapshot_interval = int(snapshot_interval)
+    need = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check("kda_chunk_prefill_ex", lib().kda_chunk_prefill_ex(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, K, V,
+        chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace), workspace.numel(),
+        ctypes.byref(op), _stream(dev)))
+    return o, ht

@@ -56,7 +56,7 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            void* const* marks, int gate_mode = 0,
                            const float* A_log = nullptr, const float* dt_bias = nullptr,
                            float lower_bound = 0.f, float* snaps = nullptr,
-                           int snap_interval = 0) {
+                           int snap_interval = 0, int qk_heads = 0, int per_head_gate = 0) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -75,7 +75,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
     return KDA_ERR_INVALID_ARGUMENT;
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
-                     gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval};
+                     gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval,
+                     qk_heads, per_head_gate};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -141,6 +142,35 @@ kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* 
   return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
                          o, workspace, workspace_bytes, stream, nullptr, 0, nullptr, nullptr,
                          0.f, snapshots, snapshot_interval);
+}
+
+kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                float scale, const float* h0, float* ht, void* o,
+                                void* workspace, size_t workspace_bytes,
+                                const kda_prefill_opts* opts, void* stream) {
+  if (!opts)
+    return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0,
+                           ht, o, workspace, workspace_bytes, stream, nullptr);
+  if (opts->gate_mode < 0 || opts->gate_mode > 2) return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->gate_mode == 2 && !(opts->lower_bound < 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->qk_heads < 0 || (opts->qk_heads > 0 && H % opts->qk_heads != 0))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->per_head_gate && H % 4 != 0) return KDA_ERR_UNSUPPORTED;
+  int interval = 0;
+  if (opts->snapshots) {
+    interval = opts->snapshot_interval;
+    if (interval < 1 || chunk < 1 || interval % chunk != 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(opts->snapshots) || T < 0 || opts->snapshot_rows < T / interval)
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, stream, nullptr, opts->gate_mode,
+                         opts->A_log, opts->dt_bias,
+                         opts->gate_mode == 2 ? opts->lower_bound : 0.f, opts->snapshots,
+                         interval, opts->qk_heads, opts->per_head_gate != 0);
 }
 
 kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,

@@ -86,6 +86,8 @@ struct PrefillArgs {
   // sequence after every snap_interval tokens (nullptr for none).
   float* snaps;
   int snap_interval;
+  int qk_heads;       // heads of q and k (0: H)
+  int per_head_gate;  // g (or a) is [T, H] and dt_bias [H]
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

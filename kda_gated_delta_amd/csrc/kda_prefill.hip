@@ -436,7 +436,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
     const ChunkEntry* __restrict__ table, char* __restrict__ recs, int gate_mode,
-    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound) {
+    const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound,
+    int HK, int per_head_gate) {
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
   constexpr int NT = NT_INTRA, NW = NT / 64;
@@ -489,6 +490,14 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     return buffer_rsrc(static_cast<const char*>(base) + ((size_t)ce.start * H + h) * width * esz,
                        (uint32_t)L * (uint32_t)(H * width * esz));
   };
+  // q and k have HK heads: value head h reads head h / (H / HK) (grouped
+  // value heads); rows of [T, HK, D]
+  const int hk = h / (H / HK);
+  auto qk_rows = [&](const void* base) {
+    constexpr int esz = (int)sizeof(IO);
+    return buffer_rsrc(static_cast<const char*>(base) + ((size_t)ce.start * HK + hk) * D * esz,
+                       (uint32_t)L * (uint32_t)(HK * D * esz));
+  };
   // gate_mode 0: g and beta are given.  1 (softplus gate) and 2 (safe gate):
   // g and beta hold the raw inputs a and b, activated here with the gate
   // kernel's own functions (the same values it would have written); beta is
@@ -512,26 +521,46 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     constexpr int K16 = (C * (D / IOV) + NT - 1) / NT;  // 16-byte groups of k, q
     static_assert(NU * D * 4 <= (int)Sm::AA_BYTES, "group totals fit in sAA");
     const int cq = tid % GQ, grp = tid / GQ, c4 = 4 * cq;
-    const auto rG = rows(g, D, 4), rK = rows(k, D, (int)sizeof(IO)), rQ = rows(q, D, (int)sizeof(IO));
+    // A per-head gate (Gated DeltaNet: g [T, H], dt_bias [H]) is one value
+    // per (token, head) that every channel shares.  It is read by the same
+    // 16-byte loads, of the aligned group of four heads that holds h (H is a
+    // multiple of 4), and the head's word is broadcast: no branch separates
+    // the loads, so none of them waits for another.
+    const int hsub = per_head_gate ? (h & 3) : 0;
+    const auto rG = per_head_gate
+        ? buffer_rsrc(g + (size_t)ce.start * H + (h & ~3), (uint32_t)L * (uint32_t)(H * 4))
+        : rows(g, D, 4);
+    const auto rK = qk_rows(k), rQ = qk_rows(q);
     const bool biased = gate_mode != 0 && dt_bias != nullptr;
-    const auto rB = buffer_rsrc(biased ? dt_bias + (size_t)h * D : g, biased ? D * 4 : 0);
+    const auto rB = buffer_rsrc(biased ? dt_bias + (per_head_gate ? (size_t)(h & ~3) : (size_t)h * D) : g,
+                                biased ? (per_head_gate ? 16 : D * 4) : 0);
+    auto pick = [&](const float4 v) {
+      const float x = hsub == 0 ? v.x : (hsub == 1 ? v.y : (hsub == 2 ? v.z : v.w));
+      return per_head_gate ? f4(x) : v;
+    };
     float4 gg[RPT];
     uint4 kk[K16], qq[K16];
+    // byte offset of this thread's first row and the row stride
+    const uint32_t gstride = (uint32_t)(per_head_gate ? H * 4 : H * D * 4);
+    const uint32_t g0 = (uint32_t)(grp * RPT) * gstride + (per_head_gate ? 0u : (uint32_t)c4 * 4);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int t = grp * RPT + i;
-      const uint32_t off = (uint32_t)(t * H * D + c4) * 4;
-      gg[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rG, off, 0, NT_HINT));
-    }
+    for (int i = 0; i < RPT; ++i)
+      gg[i] = __builtin_bit_cast(
+          float4, __builtin_amdgcn_raw_buffer_load_b128(rG, g0 + (uint32_t)i * gstride, 0, NT_HINT));
 #pragma unroll
     for (int i = 0; i < K16; ++i) {
       const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
-      const uint32_t off = (uint32_t)(t * H * D + c) * (uint32_t)sizeof(IO);
+      const uint32_t off = (uint32_t)(t * HK * D + c) * (uint32_t)sizeof(IO);
       kk[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rK, off, 0, NT_HINT));
       qq[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rQ, off, 0, NT_HINT));
     }
     // dt_bias of this thread's channels (zero without one)
-    const float4 db = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)c4 * 4, 0, 0));
+    const float4 db = pick(__builtin_bit_cast(
+        float4, __builtin_amdgcn_raw_buffer_load_b128(rB, per_head_gate ? 0u : (uint32_t)c4 * 4, 0, 0)));
+    if (per_head_gate) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) gg[i] = pick(gg[i]);
+    }
     if (gate_mode != 0) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
@@ -1536,7 +1565,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
                        (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs, a.gate_mode,
-                       a.A_log, a.dt_bias, a.lower_bound);
+                       a.A_log, a.dt_bias, a.lower_bound, a.qk_heads > 0 ? a.qk_heads : a.H,
+                       a.per_head_gate);
   if ((e = mark(2)) != hipSuccess) return e;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;

@@ -212,3 +212,24 @@ def test_step_options_validation():
     v = L.kda_verify_ex(1, P, P, P, P, P, 1.0, P, 8, P, 2, 0, 4, 64, 64, P, P,
                         ctypes.byref(kda.StepOpts()), None)
     assert v == INVALID  # Tv = 0
+
+
+def test_prefill_options_validation():
+    L = kda.lib()
+    WS = ctypes.c_void_p(1 << 20)
+
+    def call(op, H=4):
+        return L.kda_chunk_prefill_ex(1, P, P, P, P, P, P, 2, 256, H, 64, 64, 64, 1.0, None,
+                                      None, P, WS, 1 << 30, ctypes.byref(op), None)
+    op = kda.PrefillOpts()
+    op.per_head_gate = 1
+    assert call(op, H=6) == UNSUPPORTED  # per-head gates need H a multiple of 4
+    op = kda.PrefillOpts()
+    op.qk_heads = 3
+    assert call(op) == INVALID
+    op = kda.PrefillOpts()
+    op.gate_mode = 2  # safe gate without a negative bound
+    assert call(op) == INVALID
+    op = kda.PrefillOpts()
+    op.snapshots, op.snapshot_interval, op.snapshot_rows = 4096, 96, 8
+    assert call(op) == INVALID  # interval not a multiple of the chunk

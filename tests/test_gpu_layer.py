@@ -184,3 +184,81 @@ def test_verify_with_every_option(io):
         assert torch.equal(o_d, o[:, s]), s
         lvt = torch.from_numpy(live).cuda()
         assert torch.equal(pool2[idx[lvt].long()], inter[lvt, s]), s
+
+
+# ------------------------------------------------------------- prefill
+
+def _prefill_case(io, seqlens=(200, 64, 5, 130), H=4, K=64, V=64, seed=11):
+    return kda_synth.prefill_case(list(seqlens), H, K, V, io, seed=seed, regime="long",
+                                  h0_std=0.02)
+
+
+def _pt(c):
+    io = TORCH_IO[c["io"]]
+    return {x: dev(c[x], io) for x in "qkv"}, dev(c["cu"], torch.int32), dev(c["h0"])
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_prefill_per_head_gate_equals_broadcast_gate(io, chunk):
+    c = _prefill_case(io)
+    t, cu, h0 = _pt(c)
+    T, H, K = c["q"].shape
+    r = np.random.default_rng(12)
+    a_h = r.standard_normal((T, H)).astype(np.float32)
+    dtb_h = (0.5 * r.standard_normal(H) - 6.0).astype(np.float32)  # slow decay
+    A_log, b = dev(c["A_log"]), dev(c["b"])
+    g_h = -0.05 * np.abs(a_h)
+    bc = lambda x: dev(np.repeat(x[..., None], K, -1))
+    beta = torch.sigmoid(b)
+    o1, h1 = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], bc(g_h), beta, cu, 0.1, h0=h0,
+                                   chunk=chunk)
+    o2, h2 = kda.kda_chunk_prefill_ex(t["q"], t["k"], t["v"], dev(g_h), beta, cu, 0.1, h0=h0,
+                                      chunk=chunk, per_head_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    # raw per-head gate against the per-channel raw gate of the broadcast inputs
+    o1, h1 = kda.kda_chunk_prefill_ex(t["q"], t["k"], t["v"], bc(a_h), b, cu, 0.1, h0=h0,
+                                      chunk=chunk, raw_gate=(A_log, bc(dtb_h), 0.0))
+    o2, h2 = kda.kda_chunk_prefill_ex(t["q"], t["k"], t["v"], dev(a_h), b, cu, 0.1, h0=h0,
+                                      chunk=chunk, raw_gate=(A_log, dev(dtb_h), 0.0),
+                                      per_head_gate=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    # and the per-head gate against the oracle (the Gated DeltaNet case)
+    g_ref, beta_ref = oracle.gate(np.repeat(a_h[..., None], K, -1), c["b"], c["A_log"],
+                                  np.repeat(dtb_h[:, None], K, 1))
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g_ref, beta_ref, c["cu"], 0.1,
+                                   c["h0"])
+    assert_io_output(host(o2), o_ref, io, 1)
+    assert rel_err_blocks(host(h2), ht_ref, 2) <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_grouped_qk_heads_equal_repeated_heads(io):
+    c = _prefill_case(io, H=8, K=64, V=64, seed=13)
+    t, cu, h0 = _pt(c)
+    iot = TORCH_IO[io]
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    qg, kg = c["q"][:, :2], c["k"][:, :2]  # 2 q/k heads for 8 value heads
+    rep = lambda x: np.repeat(x, 4, axis=1)
+    o1, h1 = kda.kda_chunk_prefill(dev(rep(qg), iot), dev(rep(kg), iot), t["v"], dev(g),
+                                   dev(beta), cu, 0.125, h0=h0)
+    o2, h2 = kda.kda_chunk_prefill_ex(dev(qg, iot), dev(kg, iot), t["v"], dev(g), dev(beta), cu,
+                                      0.125, h0=h0)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def test_prefill_options_snapshots_equal_snapshot_entry_point():
+    c = _prefill_case("bf16", seqlens=(384, 130, 256), seed=14)
+    t, cu, h0 = _pt(c)
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    s1 = torch.zeros((12, 4, 64, 64), device="cuda")
+    s2 = torch.zeros_like(s1)
+    o1, h1, _ = kda.kda_chunk_prefill_snapshots(t["q"], t["k"], t["v"], dev(g), dev(beta), cu,
+                                                0.1, 128, h0=h0, snapshots=s1)
+    o2, h2 = kda.kda_chunk_prefill_ex(t["q"], t["k"], t["v"], dev(g), dev(beta), cu, 0.1, h0=h0,
+                                      snapshots=s2, snapshot_interval=128)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(s1, s2)
