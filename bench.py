@@ -247,6 +247,29 @@ def bench_decode(steps, warmup):
                 gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9)
 
 
+def bench_decode_layer(steps, warmup):
+    """kda_recurrent_decode_ex on decode_256 with every layer option: gate
+    from the raw a and b, in-kernel q/k L2 norm, gated RMSNorm of o."""
+    w = kda_synth.WORKLOADS["decode_256"]
+    c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
+                              seed=w["seed"], dt_bias_std=w["dt_bias_std"],
+                              state_std=w["state_std"])
+    B, H, K, V = w["B"], w["H"], w["K"], w["V"]
+    a, b = _dev(c["a"]), _dev(c["b"])
+    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+    z = torch.randn((B, H, V), device="cuda").to(torch.bfloat16)
+    wn = torch.ones(V, device="cuda")
+    o = torch.empty_like(v)
+    raw = (_dev(c["A_log"]), _dev(c["dt_bias"]), 0.0)
+    fn = lambda: kda.kda_recurrent_decode_ex(q, k, v, a, b, K ** -0.5, pool, idx, raw_gate=raw,
+                                             qk_l2norm=True, o_gate=z, o_norm_w=wn, o=o)
+    ms = _time(fn, max(steps, 20), warmup)
+    nbytes = decode_bytes(B, H, K, V) + B * H * V * 2  # plus the output gate z
+    return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes,
+                gbs=nbytes / (ms * 1e-3) / 1e9)
+
+
 def bench_replay(steps, warmup, L=16):
     """kda_replay_decode on the decode_256 shapes with a ring of L: cursors
     staggered over the rows (row r at r % L, so 1/L of the rows write their
@@ -425,7 +448,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-long", action="store_true", help="skip the 65536-token workload")
-    ap.add_argument("--only", choices=["prefill", "decode", "replay", "verify", "long"],
+    ap.add_argument("--only", choices=["prefill", "decode", "decode_layer", "replay", "verify",
+                                       "long"],
                     default=None,
                     help="time a single workload (for profiler runs)")
     ap.add_argument("--settle", type=float, default=0.2,
@@ -448,6 +472,9 @@ def main():
         return
     if args.only == "decode":
         print(json.dumps(bench_decode(args.steps, args.warmup)))
+        return
+    if args.only == "decode_layer":
+        print(json.dumps(bench_decode_layer(args.steps, args.warmup)))
         return
     if args.only == "replay":
         print(json.dumps(bench_replay(args.steps, args.warmup)))
@@ -506,6 +533,11 @@ def main():
                       "tokens_per_s": d["tokens_per_s"], "ms": d["ms"],
                       "state_gbs": d["state_gbs"], "total_gbs": d["gbs"],
                       "frac_of_hbm_peak": d["gbs"] / HBM_PEAK_GBS}
+    dl = bench_decode_layer(args.steps, args.warmup)
+    line["decode"]["with_layer_options"] = {
+        "what": "raw gate in the kernel, q/k L2 norm, gated RMSNorm of o (kda_recurrent_decode_ex)",
+        "ms": dl["ms"], "tokens_per_s": dl["tokens_per_s"], "total_gbs": dl["gbs"],
+        "frac_of_hbm_peak": dl["gbs"] / HBM_PEAK_GBS}
     rp = bench_replay(args.steps, args.warmup)
     line["replay_decode"] = {"workload": "decode_256 with a 16-entry ring per slot, cursors "
                                          "staggered over the rows (kda_replay_decode)",
