@@ -372,6 +372,23 @@ kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
                              int32_t B, int32_t H, int32_t K, int32_t V, void* o,
                              int32_t* next_write_pos, void* stream);
 
+/*
+ * kda_replay_decode with model-layer options (kda_step_opts): the gate from
+ * raw inputs, the per-head gate and grouped q/k heads (q, k [B, qk_heads,
+ * K]; g [B, H, K] or [B, H]).  The ring keeps the activated per-channel g.
+ * qk_l2norm and o_gate are not supported here (KDA_ERR_UNSUPPORTED).  With
+ * opts NULL the results are bit-identical to kda_replay_decode.
+ */
+kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                float scale, float* state_pool, int64_t n_slots,
+                                const int32_t* slot_idx, const int32_t* write_pos,
+                                const int32_t* force_flush, int32_t ring_len,
+                                float* ring_d, void* ring_k, float* ring_g,
+                                int32_t B, int32_t H, int32_t K, int32_t V, void* o,
+                                int32_t* next_write_pos, const kda_step_opts* opts,
+                                void* stream);
+
 #ifdef __cplusplus
 } /* extern "C" */
 #endif

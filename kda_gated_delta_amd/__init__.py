@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.kda_replay_decode.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, f32, vp, i64, vp, vp, vp,
                                     i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.kda_replay_decode.restype = ctypes.c_int
+    L.kda_replay_decode_ex.argtypes = L.kda_replay_decode.argtypes[:-1] + [
+        ctypes.POINTER(StepOpts), vp]
+    L.kda_replay_decode_ex.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -104,7 +107,8 @@ EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_s
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
             "kda_chunk_prefill_snapshots",
             "kda_recurrent_decode", "kda_verify", "kda_replay_decode",
-            "kda_recurrent_decode_ex", "kda_verify_ex", "kda_chunk_prefill_ex")
+            "kda_recurrent_decode_ex", "kda_verify_ex", "kda_chunk_prefill_ex",
+            "kda_replay_decode_ex")
 
 
 def status_string(status: int) -> str:
@@ -340,21 +344,24 @@ def kda_verify(q, k, v, g, beta, scale: float, state_pool, slot_idx,
 
 
 def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, write_pos,
-                      ring_d, ring_k, ring_g, force_flush=None, o=None, next_write_pos=None):
+                      ring_d, ring_k, ring_g, force_flush=None, o=None, next_write_pos=None,
+                      raw_gate=None, per_head_gate=False):
     """Buffered single-token decode.  ``state_pool`` [n_slots,H,K,V] holds the
     checkpoints; the rings ring_d [n_slots,H,L,V] fp32, ring_k [n_slots,H,L,K]
     (io dtype) and ring_g [n_slots,H,L,K] fp32 hold the steps since them;
-    ``write_pos`` [B] int32 is each row's cursor.  Returns (o [B,H,V],
-    next_write_pos [B] int32)."""
-    B, H, K = q.shape
-    V = v.shape[2]
+    ``write_pos`` [B] int32 is each row's cursor.  ``raw_gate`` = (A_log,
+    dt_bias, lower_bound) applies the gate to the raw a given as g (beta is
+    then the raw b); ``per_head_gate`` takes g [B,H]; q, k may have fewer
+    heads than v (grouped heads).  Returns (o [B,H,V], next_write_pos [B])."""
+    B, HK, K = q.shape
+    H, V = v.shape[1], v.shape[2]
     dev = q.device
     io = _io_dtype(q)
     n_slots = state_pool.shape[0]
     L = ring_d.shape[2]
-    _need(k, "k", q.dtype, (B, H, K), dev)
+    _need(k, "k", q.dtype, (B, HK, K), dev)
     _need(v, "v", q.dtype, (B, H, V), dev)
-    _need(g, "g", torch.float32, (B, H, K), dev)
+    _need(g, "g", torch.float32, (B, H) if per_head_gate else (B, H, K), dev)
     _need(beta, "beta", torch.float32, (B, H), dev)
     _need(state_pool, "state_pool", torch.float32, (n_slots, H, K, V), dev)
     _need(slot_idx, "slot_idx", torch.int32, (B,), dev)
@@ -369,10 +376,16 @@ def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, writ
     if next_write_pos is None:
         next_write_pos = torch.empty((B,), dtype=torch.int32, device=dev)
     _need(next_write_pos, "next_write_pos", torch.int32, (B,), dev)
-    _check("kda_replay_decode", lib().kda_replay_decode(
-        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state_pool),
-        n_slots, _ptr(slot_idx), _ptr(write_pos), _ptr(force_flush), L, _ptr(ring_d),
-        _ptr(ring_k), _ptr(ring_g), B, H, K, V, _ptr(o), _ptr(next_write_pos), _stream(dev)))
+    args = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state_pool),
+            n_slots, _ptr(slot_idx), _ptr(write_pos), _ptr(force_flush), L, _ptr(ring_d),
+            _ptr(ring_k), _ptr(ring_g), B, H, K, V, _ptr(o), _ptr(next_write_pos)]
+    if raw_gate is None and not per_head_gate and HK == H:
+        _check("kda_replay_decode", lib().kda_replay_decode(*args, _stream(dev)))
+    else:
+        op = _step_opts(H, (B,), K, V, dev, q.dtype, raw_gate, per_head_gate, False, HK, None,
+                        None, 0.0, "sigmoid")
+        _check("kda_replay_decode_ex", lib().kda_replay_decode_ex(*args, ctypes.byref(op),
+                                                                  _stream(dev)))
     return o, next_write_pos
 
 

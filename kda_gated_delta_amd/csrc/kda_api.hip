@@ -275,7 +275,21 @@ kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
                              void* ring_k, float* ring_g, int32_t B, int32_t H,
                              int32_t K, int32_t V, void* o, int32_t* next_write_pos,
                              void* stream) {
+  return kda_replay_decode_ex(io, q, k, v, g, beta, scale, state_pool, n_slots, slot_idx,
+                              write_pos, force_flush, ring_len, ring_d, ring_k, ring_g, B, H, K,
+                              V, o, next_write_pos, nullptr, stream);
+}
+
+kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                float scale, float* state_pool, int64_t n_slots,
+                                const int32_t* slot_idx, const int32_t* write_pos,
+                                const int32_t* force_flush, int32_t ring_len, float* ring_d,
+                                void* ring_k, float* ring_g, int32_t B, int32_t H,
+                                int32_t K, int32_t V, void* o, int32_t* next_write_pos,
+                                const kda_step_opts* opts, void* stream) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+  if (opts && (opts->qk_l2norm || opts->o_gate)) return KDA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (ring_len < 1 || ring_len > KDA_RING_MAX) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;
@@ -296,9 +310,11 @@ kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
       if (n0 < f1 && f0 < n1) return KDA_ERR_INVALID_ARGUMENT;
     }
   }
+  kda::StepOpts op;
+  if (kda_status st = step_opts(opts, io, H, op)) return st;
   kda::ReplayArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
                     write_pos, force_flush, ring_len, ring_d, ring_k, ring_g, B, H, K, V, o,
-                    next_write_pos};
+                    next_write_pos, op};
   return launch_status(kda::run_replay(p, (hipStream_t)stream));
 }
 

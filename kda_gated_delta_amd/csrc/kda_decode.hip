@@ -147,14 +147,16 @@ __device__ __forceinline__ float4 token_step(Rows<StepShape<K, V>::RPT>& st,
 // DeltaNet" and "KDA") with the gate kernel's own functions, so that the
 // result is the value kda_gate_prep would have written.  A per-head gate
 // (the Gated DeltaNet case) decays every channel alike.
-__device__ __forceinline__ float decay_of(const float* __restrict__ g, int64_t row, int c, int K,
-                                          int h, const StepOpts& op) {
-  float x = op.per_head_gate ? g[row] : g[row * K + c];
+__device__ __forceinline__ float gate_of(float x, int c, int K, int h, const StepOpts& op) {
   if (op.gate_mode == 0) return x;
   if (op.dt_bias) x = x + (op.per_head_gate ? op.dt_bias[h] : op.dt_bias[h * K + c]);
   const float rate = exp_split(op.A_log[h]);
   return op.gate_mode == 2 ? gate1<true>(x, rate, op.lower_bound)
                            : gate1<false>(x, rate, op.lower_bound);
+}
+__device__ __forceinline__ float decay_of(const float* __restrict__ g, int64_t row, int c, int K,
+                                          int h, const StepOpts& op) {
+  return gate_of(op.per_head_gate ? g[row] : g[row * K + c], c, K, h, op);
 }
 
 // Write strength of a token: beta, or sigmoid of the raw b.
@@ -379,7 +381,7 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
     const int32_t* __restrict__ write_pos, const int32_t* __restrict__ force_flush, int L,
     float* __restrict__ ring_d, IO* __restrict__ ring_k, float* __restrict__ ring_g, int H,
-    IO* __restrict__ o, int32_t* __restrict__ next_pos) {
+    IO* __restrict__ o, int32_t* __restrict__ next_pos, StepOpts op) {
   typedef StepShape<K, V> Sh;
   __shared__ float sq[K], sk[K], sa[K], sg[K];
   __shared__ __align__(16) float swk[RING_MAX][K], sgr[RING_MAX][K], sd[RING_MAX][V];
@@ -434,23 +436,27 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   static_assert(K <= Sh::NT, "one channel per thread");
   float tq, tk, tg;
   {
+    // grouped heads read q/k head h / (H / HK); a per-head gate is one word
+    const int HK = op.qk_heads > 0 ? op.qk_heads : H;
+    const int64_t qk = (int64_t)r * HK + h / (H / HK);
     const uint32_t off = (uint32_t)t * (uint32_t)sizeof(IO);
     if constexpr (sizeof(IO) == 2) {
       tq = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-               buffer_rsrc(q + rh * K, K * 2), off, 0, 0) << 16);
+               buffer_rsrc(q + qk * K, K * 2), off, 0, 0) << 16);
       tk = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
-               buffer_rsrc(k + rh * K, K * 2), off, 0, 0) << 16);
+               buffer_rsrc(k + qk * K, K * 2), off, 0, 0) << 16);
     } else {
       tq = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-               buffer_rsrc(q + rh * K, K * 4), off, 0, 0));
+               buffer_rsrc(q + qk * K, K * 4), off, 0, 0));
       tk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-               buffer_rsrc(k + rh * K, K * 4), off, 0, 0));
+               buffer_rsrc(k + qk * K, K * 4), off, 0, 0));
     }
     tg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-             buffer_rsrc(g + rh * K, K * 4), (uint32_t)t * 4, 0, 0));
+             op.per_head_gate ? buffer_rsrc(g + rh, 4) : buffer_rsrc(g + rh * K, K * 4),
+             op.per_head_gate ? 0u : (uint32_t)t * 4, 0, 0));
   }
   const float4 vv = load4(v + rh * V + c0);
-  const float b = beta[rh];
+  const float b = strength_of(beta[rh], op);
   Rows<Sh::RPT> st;
   float4* s = st.s;
   __builtin_amdgcn_sched_barrier(0);  // keep the checkpoint's loads last
@@ -485,6 +491,10 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     if (j < RING_MAX) *reinterpret_cast<float4*>(&sd[j][c]) = dr[i];
   }
   __syncthreads();
+  if (op.gate_mode != 0) {  // the gate from the raw a, in place
+    if (t < K) sg[t] = gate_of(sg[t], t, K, h, op);
+    __syncthreads();
+  }
   // Decay weights per key channel, newest entry first: w_j k_j in place of
   // k_j, then A.  The NG = NT / K thread groups of a channel take EPG
   // consecutive entries each; a group starts from the sum of the current g
@@ -572,7 +582,7 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
     if (t < K) {  // k was read as io values: converting back is exact
       ring_k[(e0 + pos) * K + t] = from_f32<IO>(tk);
-      ring_g[(e0 + pos) * K + t] = tg;
+      ring_g[(e0 + pos) * K + t] = sg[t];
     }
   }
   if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = flush ? 0 : pos + 1;
@@ -584,7 +594,7 @@ hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((replay_kernel<IO, K, V>), dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0,
                      stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
                      a.scale, a.pool, a.slot_idx, a.write_pos, a.force_flush, a.L, a.ring_d,
-                     (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos);
+                     (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos, a.opts);
   return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ struct ReplayArgs {
   int B, H, K, V;
   void* o;
   int32_t* next_pos;
+  StepOpts opts;  // gate options and grouped heads (no L2 norm, no output norm)
 };
 
 struct PrefillArgs {

@@ -233,3 +233,21 @@ def test_prefill_options_validation():
     op = kda.PrefillOpts()
     op.snapshots, op.snapshot_interval, op.snapshot_rows = 4096, 96, 8
     assert call(op) == INVALID  # interval not a multiple of the chunk
+
+
+def test_replay_options_validation():
+    L = kda.lib()
+    W, N, F = ctypes.c_void_p(8192), ctypes.c_void_p(8192 + 64), ctypes.c_void_p(8192 + 128)
+    op = kda.StepOpts()
+    op.qk_l2norm = 1
+
+    def call(o):
+        return L.kda_replay_decode_ex(1, P, P, P, P, P, 1.0, P, 8, P, W, F, 16, P, P, P, 4, 2,
+                                      128, 128, P, N, ctypes.byref(o), None)
+    assert call(op) == UNSUPPORTED
+    op = kda.StepOpts()
+    op.o_gate, op.o_norm_w = 4096, 4096
+    assert call(op) == UNSUPPORTED
+    op = kda.StepOpts()
+    op.gate_mode = 1  # no A_log
+    assert call(op) == INVALID

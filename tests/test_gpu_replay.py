@@ -176,3 +176,39 @@ def test_cursor_outside_ring_touches_nothing():
         s = c["slot_idx"][r]
         np.testing.assert_array_equal(pool[s], c["pool"][s])
     assert torch.isnan(rd[c["slot_idx"][1]]).all() and torch.isnan(rd[c["slot_idx"][2]]).all()
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_replay_options_equal_prepared_inputs(io):
+    # raw per-head gate (Gated DeltaNet form) and grouped q/k heads against
+    # the same steps with kda_gate_prep's per-channel g and repeated heads
+    B, H, HK, K, V, L, steps = 6, 8, 2, 64, 64, 4, 9
+    c = _case(B, H, K, V, 9, io, seed=70, steps=steps, regime="long", n_padding=1)
+    r = np.random.default_rng(71)
+    a_h = r.standard_normal((B, steps, H)).astype(np.float32)
+    dtb_h = (0.5 * r.standard_normal(H) - 6.0).astype(np.float32)
+    A_log = dev(c["A_log"])
+    iot = TORCH_IO[io]
+    idx = dev(c["slot_idx"], torch.int32)
+    pool_a, pool_b = dev(c["pool"]), dev(c["pool"])
+    ra, rb = _rings(c, L), _rings(c, L)
+    pos_a = pos_b = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for s in range(steps):
+        q = dev(c["q"][:, s, :HK], iot)
+        k = dev(c["k"][:, s, :HK], iot)
+        v = dev(c["v"][:, s], iot)
+        b = dev(c["b"][:, s])
+        force = dev(np.array([s == 5] + [False] * (B - 1), dtype=np.int32), torch.int32)
+        a_bc = dev(np.repeat(a_h[:, s, :, None], K, -1))
+        g_ch, beta = kda.kda_gate_prep(a_bc, b, A_log, dev(np.repeat(dtb_h[:, None], K, 1)))
+        rep = lambda x: x.repeat_interleave(H // HK, dim=1).contiguous()
+        o_a, pos_a = kda.kda_replay_decode(rep(q), rep(k), v, g_ch, beta, 0.1, pool_a, idx, pos_a,
+                                           *ra, force_flush=force)
+        o_b, pos_b = kda.kda_replay_decode(q, k, v, dev(a_h[:, s]), b, 0.1, pool_b, idx, pos_b,
+                                           *rb, force_flush=force,
+                                           raw_gate=(A_log, dev(dtb_h), 0.0), per_head_gate=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b), s
+        assert torch.equal(pos_a, pos_b) and torch.equal(pool_a, pool_b), s
+    for x, y in zip(ra, rb):
+        assert torch.equal(torch.nan_to_num(x, nan=7.0), torch.nan_to_num(y, nan=7.0))
