@@ -374,7 +374,7 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
 // bit-identical to it.
 constexpr int RING_MAX = KDA_RING_MAX;
 
-template <typename IO, int K, int V>
+template <typename IO, int K, int V, bool OPT>
 __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_per_eu(StepShape<K, V>::NT == 1024 ? 8 : 1))) void replay_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, float scale,
@@ -385,7 +385,8 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   typedef StepShape<K, V> Sh;
   __shared__ float sq[K], sk[K], sa[K], sg[K];
   __shared__ __align__(16) float swk[RING_MAX][K], sgr[RING_MAX][K], sd[RING_MAX][V];
-  __shared__ float sck[RING_MAX], scq[RING_MAX], sdump[3];
+  __shared__ float sck[RING_MAX], scq[RING_MAX];
+  __shared__ float sdump[3];
   __shared__ float spart[Sh::NT / K][K];
   __shared__ float red[Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
@@ -410,6 +411,14 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   // there (reads past it return zero without touching memory), then the
   // checkpoint.  Staging the small ones in LDS then waits for them alone,
   // and the ring arithmetic below runs while the checkpoint is in flight.
+  // option-dependent addresses first, so that the loads below form one
+  // straight block: grouped heads read q/k head h / (H / HK), a per-head
+  // gate is one word
+  // (OPT: the kernel instance that reads the options; the other one is the
+  // plain step, with no option code at all)
+  const int HK = OPT && op.qk_heads > 0 ? op.qk_heads : H;
+  const int64_t qk = OPT ? (int64_t)r * HK + h / (H / HK) : rh;
+  const bool ph = OPT && op.per_head_gate;
   constexpr int RK = (RING_MAX * K / 4 + Sh::NT - 1) / Sh::NT;  // 4-channel groups
   constexpr int RD = (RING_MAX * V / 4 + Sh::NT - 1) / Sh::NT;  // 4-column groups
   typedef typename std::conditional<sizeof(IO) == 2, uint2, uint4>::type RawK;
@@ -436,9 +445,6 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   static_assert(K <= Sh::NT, "one channel per thread");
   float tq, tk, tg;
   {
-    // grouped heads read q/k head h / (H / HK); a per-head gate is one word
-    const int HK = op.qk_heads > 0 ? op.qk_heads : H;
-    const int64_t qk = (int64_t)r * HK + h / (H / HK);
     const uint32_t off = (uint32_t)t * (uint32_t)sizeof(IO);
     if constexpr (sizeof(IO) == 2) {
       tq = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(
@@ -451,12 +457,13 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
       tk = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                buffer_rsrc(k + qk * K, K * 4), off, 0, 0));
     }
+    // (a per-head gate is one word, which every channel reads)
     tg = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-             op.per_head_gate ? buffer_rsrc(g + rh, 4) : buffer_rsrc(g + rh * K, K * 4),
-             op.per_head_gate ? 0u : (uint32_t)t * 4, 0, 0));
+             ph ? buffer_rsrc(g + rh, 4) : buffer_rsrc(g + rh * K, K * 4),
+             ph ? 0u : (uint32_t)t * 4, 0, 0));
   }
   const float4 vv = load4(v + rh * V + c0);
-  const float b = strength_of(beta[rh], op);
+  const float braw = beta[rh];
   Rows<Sh::RPT> st;
   float4* s = st.s;
   __builtin_amdgcn_sched_barrier(0);  // keep the checkpoint's loads last
@@ -491,10 +498,11 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     if (j < RING_MAX) *reinterpret_cast<float4*>(&sd[j][c]) = dr[i];
   }
   __syncthreads();
-  if (op.gate_mode != 0) {  // the gate from the raw a, in place
+  if (OPT && op.gate_mode != 0) {  // the gate from the raw a, in place
     if (t < K) sg[t] = gate_of(sg[t], t, K, h, op);
     __syncthreads();
   }
+  const float b = OPT ? strength_of(braw, op) : braw;
   // Decay weights per key channel, newest entry first: w_j k_j in place of
   // k_j, then A.  The NG = NT / K thread groups of a channel take EPG
   // consecutive entries each; a group starts from the sum of the current g
@@ -580,9 +588,9 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
   } else {
     if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
-    if (t < K) {  // k was read as io values: converting back is exact
+    if (t < K) {  // k was read as io values: converting back is exact; g as activated
       ring_k[(e0 + pos) * K + t] = from_f32<IO>(tk);
-      ring_g[(e0 + pos) * K + t] = sg[t];
+      ring_g[(e0 + pos) * K + t] = OPT ? sg[t] : tg;
     }
   }
   if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = flush ? 0 : pos + 1;
@@ -591,8 +599,10 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
 template <typename IO, int K, int V>
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
   typedef StepShape<K, V> Sh;
-  hipLaunchKernelGGL((replay_kernel<IO, K, V>), dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0,
-                     stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
+  const bool opt = a.opts.gate_mode != 0 || a.opts.per_head_gate != 0 ||
+                   (a.opts.qk_heads > 0 && a.opts.qk_heads != a.H);
+  hipLaunchKernelGGL((opt ? replay_kernel<IO, K, V, true> : replay_kernel<IO, K, V, false>),
+                     dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
                      a.scale, a.pool, a.slot_idx, a.write_pos, a.force_flush, a.L, a.ring_d,
                      (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos, a.opts);
   return hipGetLastError();
