@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 import kda_gated_delta_amd as kda  # noqa: E402
 import kda_synth  # noqa: E402
+from kda_gated_delta_amd import ceilings  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16, published
@@ -365,6 +366,50 @@ def bench_long(steps, warmup):
                 bytes=prefill_bytes(T, 1, H, K, V))
 
 
+def _event_ms(fn, reps: int = 5) -> float:
+    """Median milliseconds of one call of fn, each call between HIP events on
+    the current stream (after two untimed calls)."""
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
+def measure_ceilings(nbytes: int = 2 << 30):
+    """Rates that plain hand-written kernels (libkda_probe) reach on this GPU:
+    HBM streams over `nbytes` per buffer in the access patterns of the paths
+    (separate read + write, in-place read-modify-write, read only, write
+    only), and loops of independent bf16 matrix-core products in the two MFMA
+    shapes (32x32x16, and 16x16x32: the shape the prefill kernels use)."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    out = {}
+    traffic = {"copy": 2 * nbytes, "rmw": 2 * nbytes, "read": nbytes, "write": nbytes}
+    for mode, moved in traffic.items():
+        ms = _event_ms(lambda: ceilings.hbm(mode, src if mode in ("copy", "read") else None,
+                                            dst, nbytes))
+        out[f"hbm_{mode}_gbs"] = moved / (ms * 1e-3) / 1e9
+    del src, dst
+    blocks, iters = 512, 20000
+    res = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
+    for shape in ("32x32x16", "16x16x32"):
+        ms = _event_ms(lambda: ceilings.mfma_bf16(shape, blocks, iters, res))
+        out[f"bf16_mfma_{shape}_tflops"] = ceilings.mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+    out["what"] = (f"libkda_probe kernels timed in this run: HBM streams over {nbytes >> 30} GiB "
+                   "per buffer (copy and rmw count read + write bytes; one 1024-thread "
+                   "workgroup per 16 KiB, non-temporal); 512 workgroups of independent bf16 "
+                   "MFMA chains per shape")
+    return out
+
+
 KERNEL_SYMBOL = {"intra": "intra_kernel", "state": "state_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_varlen_7680_traffic.md")
 PREFILL_SOURCE = os.path.join(ROOT, "kda_gated_delta_amd", "csrc", "kda_prefill.hip")
@@ -450,7 +495,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-long", action="store_true", help="skip the 65536-token workload")
     ap.add_argument("--only", choices=["prefill", "decode", "decode_layer", "replay", "verify",
-                                       "long"],
+                                       "long", "ceilings"],
                     default=None,
                     help="time a single workload (for profiler runs)")
     ap.add_argument("--settle", type=float, default=0.2,
@@ -485,6 +530,9 @@ def main():
         return
     if args.only == "long":
         print(json.dumps(bench_long(args.steps, args.warmup)))
+        return
+    if args.only == "ceilings":
+        print(json.dumps(measure_ceilings()))
         return
 
     p = bench_prefill(args.steps, args.warmup)
@@ -559,6 +607,17 @@ def main():
                         "tokens_per_s_segmented": lg["tokens_per_s_segmented"],
                         "tokens_per_s_full": lg["tokens_per_s_full"],
                         "ms_segmented": lg["ms_segmented"], "ms_full": lg["ms_full"]}
+    cl = measure_ceilings()
+    line["measured_ceilings"] = cl
+    # each path against the measured stream of its access pattern: the decode
+    # pool update is an in-place read-modify-write; verify, the buffered
+    # decode and the prefill kernels read some buffers and write others
+    line["roofline"]["frac_of_measured"] = line["roofline"]["achieved"] / (
+        cl["hbm_copy_gbs"] if line["roofline"]["unit"] == "GB/s" else cl["bf16_mfma_32x32x16_tflops"])
+    line["prefill"]["frac_of_measured_copy"] = achieved / cl["hbm_copy_gbs"]
+    line["decode"]["frac_of_measured_rmw"] = d["gbs"] / cl["hbm_rmw_gbs"]
+    line["replay_decode"]["frac_of_measured_copy"] = rp["gbs"] / cl["hbm_copy_gbs"]
+    line["verify"]["frac_of_measured_copy"] = vr["gbs"] / cl["hbm_copy_gbs"]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(p["inputs"], w)
     print(json.dumps(line))

@@ -1,4 +1,5 @@
-"""Builds libkda.so (all HIP sources under csrc/) for gfx950, in-tree.
+"""Builds libkda.so (all HIP sources under csrc/) and libkda_probe.so (the
+measured-ceiling kernels under probe/) for gfx950, in-tree.
 
 hipcc compiles every translation unit for gfx950 only, with packed-fp32
 instructions disabled, and links them into one shared library next to this
@@ -19,6 +20,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkda.so")
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libkda_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -38,17 +41,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = ["hipcc", f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(jobs: int = 4) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip")))
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[:len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     return LIB
 
 
