@@ -176,6 +176,11 @@ kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* 
  *     and k of head h / (H / qk_heads).
  *   snapshots, snapshot_rows, snapshot_interval: chunk-boundary states as in
  *     kda_chunk_prefill_snapshots (snapshots NULL = none).
+ *   qk_l2norm: q and k are L2-normalised in the kernel, x / sqrt(|x|^2 +
+ *     1e-6) per (token, q/k head) (ReplaySSM analysis, section 3.10), as
+ *     kda_step_opts.qk_l2norm does for decode and verify.  The factor
+ *     1 / sqrt(|x|^2 + 1e-6) of each row scales the products that row enters;
+ *     q and k themselves are never rounded again.
  */
 typedef struct {
   int32_t gate_mode;
@@ -187,6 +192,7 @@ typedef struct {
   float* snapshots;
   int64_t snapshot_rows;
   int32_t snapshot_interval;
+  int32_t qk_l2norm;
 } kda_prefill_opts;
 
 /*

@@ -30,7 +30,7 @@ class PrefillOpts(ctypes.Structure):
                 ("dt_bias", ctypes.c_void_p), ("lower_bound", ctypes.c_float),
                 ("per_head_gate", ctypes.c_int32), ("qk_heads", ctypes.c_int32),
                 ("snapshots", ctypes.c_void_p), ("snapshot_rows", ctypes.c_int64),
-                ("snapshot_interval", ctypes.c_int32)]
+                ("snapshot_interval", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32)]
 
 
 class StepOpts(ctypes.Structure):
@@ -480,11 +480,13 @@ def kda_verify_ex(q, k, v, g, beta, scale: float, state_pool, slot_idx, *, raw_g
 def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate=None,
                          per_head_gate=False, h0=None, output_final_state: bool = True,
                          chunk: int = 64, o=None, ht=None, snapshots=None,
-                         snapshot_interval: int = 0, workspace=None):
+                         snapshot_interval: int = 0, qk_l2norm: bool = False,
+                         workspace=None):
     """Prefill with model-layer options: q, k [T,HK,K]; v [T,H,V]; g [T,H,K]
     (or [T,H] with per_head_gate), raw a when ``raw_gate`` = (A_log,
     dt_bias, lower_bound) is given (then beta holds the raw b); snapshots as
-    in kda_chunk_prefill_snapshots.  Returns (o, ht)."""
+    in kda_chunk_prefill_snapshots; ``qk_l2norm``: q and k L2-normalised in
+    the kernel.  Returns (o, ht)."""
     T, HK, K = q.shape
     H, V = v.shape[1], v.shape[2]
     dev = q.device
@@ -515,6 +517,7 @@ def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate
         op.lower_bound = float(lower_bound)
     op.per_head_gate = int(bool(per_head_gate))
     op.qk_heads = HK
+    op.qk_l2norm = int(bool(qk_l2norm))
     if snapshots is not None:
         _need(snapshots, "snapshots", torch.float32, (snapshots.shape[0], H, K, V), dev)
         op.snapshots = snapshots.data_ptr()

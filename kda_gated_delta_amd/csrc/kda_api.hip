@@ -56,7 +56,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            void* const* marks, int gate_mode = 0,
                            const float* A_log = nullptr, const float* dt_bias = nullptr,
                            float lower_bound = 0.f, float* snaps = nullptr,
-                           int snap_interval = 0, int qk_heads = 0, int per_head_gate = 0) {
+                           int snap_interval = 0, int qk_heads = 0, int per_head_gate = 0,
+                           int qk_l2norm = 0) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -76,7 +77,7 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
                      gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval,
-                     qk_heads, per_head_gate};
+                     qk_heads, per_head_gate, qk_l2norm};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -170,7 +171,8 @@ kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
                          o, workspace, workspace_bytes, stream, nullptr, opts->gate_mode,
                          opts->A_log, opts->dt_bias,
                          opts->gate_mode == 2 ? opts->lower_bound : 0.f, opts->snapshots,
-                         interval, opts->qk_heads, opts->per_head_gate != 0);
+                         interval, opts->qk_heads, opts->per_head_gate != 0,
+                         opts->qk_l2norm != 0);
 }
 
 kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,

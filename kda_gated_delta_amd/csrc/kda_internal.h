@@ -89,6 +89,7 @@ struct PrefillArgs {
   int snap_interval;
   int qk_heads;       // heads of q and k (0: H)
   int per_head_gate;  // g (or a) is [T, H] and dt_bias [H]
+  int qk_l2norm;      // q, k L2-normalised in the kernel
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

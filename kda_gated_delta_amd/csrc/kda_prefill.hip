@@ -350,9 +350,15 @@ __device__ __forceinline__ int swz(int r, int c) {
   return r * N + ((((unsigned)c / GR) ^ (unsigned)r) & (NG - 1)) * GR + ((unsigned)c % GR);
 }
 
+constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
+
 template <typename IO, int D, int C>
 struct IntraSmem {
   static constexpr int NB = C / 16, KTC = (C + 31) / 32;
+  // row groups of the cumulative-sum staging (step 1): NT_INTRA / (D / 4)
+  // groups of RPT rows, NU of which hold rows
+  static constexpr int NGR = NT_INTRA / (D / 4), RPT = (C + NGR - 1) / NGR;
+  static constexpr int NU = (C + RPT - 1) / RPT;
   static constexpr size_t cmax(size_t x, size_t y) { return x > y ? x : y; }
   // sG [C][D] fp32: G (groups of 8), then K e^G and V (plain)
   static constexpr size_t G_BYTES = (size_t)C * D * 4;
@@ -363,14 +369,14 @@ struct IntraSmem {
                                          (size_t)6 * 256 * 4);
   // sQ [C][D] io (groups of 8): q; then beta
   static constexpr size_t Q_BYTES = cmax((size_t)C * D * sizeof(IO), (size_t)C * 4);
-  // sAA [C][C] fp32 (plain): A transposed in the strict upper triangle and
-  // Aq in the lower one, Aq's triangle then reused for X; finally the 32-row
-  // staging of W ([32][D] fp32, groups of 8)
-  static constexpr size_t AA_BYTES = cmax((size_t)C * C * 4, (size_t)32 * D * 4);
+  // sAA [C][C] fp32 (plain): first the NU row-group totals of step 1 and,
+  // past them, the inverse norms of q and k rows; then A transposed in the
+  // strict upper triangle and Aq in the lower one, Aq's triangle then reused
+  // for X; finally the 32-row staging of W ([32][D] fp32, groups of 8)
+  static constexpr size_t AA_BYTES =
+      cmax(cmax((size_t)C * C * 4, (size_t)32 * D * 4), (size_t)(NU * D + 2 * C) * 4);
   static constexpr size_t TOTAL = G_BYTES + K_BYTES + Q_BYTES + AA_BYTES;
 };
-
-constexpr int NT_INTRA = 512;  // eight waves: two per SIMD
 
 // Cache policy of the intra kernel's streams (inputs read once, records
 // written once and read by the next kernel): the non-temporal hint.
@@ -402,6 +408,24 @@ __device__ __forceinline__ void offdiag_group(int idx, int& I, int& J0, int& nJ)
 // exponential (v_exp_f32) of the difference of two stored values.
 constexpr float LOG2E = 1.4426950408889634f;
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum of squares of one 16-byte group of io elements (raw bits).
+template <typename IO>
+__device__ __forceinline__ float sumsq16(const uint4 x) {
+  float s = 0.f;
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(IO) == 2) {  // bf16 pairs: element 2i in the low half of word i
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+      s = fmaf(lo, lo, fmaf(hi, hi, s));
+    } else {
+      const float f = __uint_as_float(w[i]);
+      s = fmaf(f, f, s);
+    }
+  }
+  return s;
+}
 
 // Lane-broadcast helpers (DPP, no LDS): row_newbcast:n gives every lane of a
 // 16-lane row the value of lane n of that row; quad_perm[0,0,0,0] gives every
@@ -437,7 +461,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
     const ChunkEntry* __restrict__ table, char* __restrict__ recs, int gate_mode,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound,
-    int HK, int per_head_gate) {
+    int HK, int per_head_gate, int qk_l2norm) {
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
   constexpr int NT = NT_INTRA, NW = NT / 64;
@@ -506,6 +530,16 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   const float braw = __builtin_bit_cast(
       float, __builtin_amdgcn_raw_buffer_load_b32(rows(beta, 1, 4), (uint32_t)(tid * H * 4), 0, 0));
 
+  // In-kernel L2 norm of q and k (option): 1 / sqrt(|row|^2 + 1e-6) of every
+  // q and k row of the chunk, lane t of each wave holding row t's.  A row
+  // enters every product linearly, so these factors scale the products'
+  // results (A, Aq, the in-sub-block sums) and the state pass's operands
+  // (scale Q e^G, K e^{G_C-G}, K e^G and through it W); q and k stay as given.
+  // rq_of / rk_of must run with every lane of the wave active.
+  float rq_all = 1.f, rk_all = 1.f;
+  auto rq_of = [&](int t) { return __shfl(rq_all, t, 64); };
+  auto rk_of = [&](int t) { return __shfl(rk_all, t, 64); };
+
   // ---- 1. stage g, k, q (rows t >= L are zero) with the chunk-local
   // inclusive cumulative sum of g folded in.  A thread holds RPT consecutive
   // rows of one four-channel group of g and scans them in registers; the
@@ -519,7 +553,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     constexpr int RPT = (C + NGR - 1) / NGR;     // rows per thread
     constexpr int NU = (C + RPT - 1) / RPT;      // row groups that hold rows
     constexpr int K16 = (C * (D / IOV) + NT - 1) / NT;  // 16-byte groups of k, q
-    static_assert(NU * D * 4 <= (int)Sm::AA_BYTES, "group totals fit in sAA");
+    static_assert(NU == Sm::NU && (NU * D + 2 * C) * 4 <= (int)Sm::AA_BYTES,
+                  "group totals and row norms fit in sAA");
     const int cq = tid % GQ, grp = tid / GQ, c4 = 4 * cq;
     // A per-head gate (Gated DeltaNet: g [T, H], dt_bias [H]) is one value
     // per (token, head) that every channel shares.  It is read by the same
@@ -582,6 +617,26 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       gg[i] = acc;
     }
     if (grp < NU) *reinterpret_cast<float4*>(sAA + grp * D + c4) = acc;
+    float* sNrm = sAA + NU * D;  // [q rows, k rows] of inverse norms
+    if (qk_l2norm) {
+      // a row's GPR 16-byte groups sit in GPR consecutive lanes of one wave:
+      // their sums of squares meet by a butterfly over those lanes
+      constexpr int GPR = D / IOV;
+#pragma unroll
+      for (int i = 0; i < K16; ++i) {
+        const int e = tid + i * NT;
+        float sq = sumsq16<IO>(qq[i]), sk = sumsq16<IO>(kk[i]);
+#pragma unroll
+        for (int m = GPR / 2; m >= 1; m >>= 1) {
+          sq += __shfl_xor(sq, m, 64);
+          sk += __shfl_xor(sk, m, 64);
+        }
+        if (e < C * GPR && e % GPR == 0) {
+          sNrm[e / GPR] = 1.f / sqrtf(sq + 1e-6f);
+          sNrm[C + e / GPR] = 1.f / sqrtf(sk + 1e-6f);
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < K16; ++i) {
       const int e = tid + i * NT, t = e / (D / IOV), c = (e % (D / IOV)) * IOV;
@@ -591,6 +646,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       }
     }
     __syncthreads();
+    if (qk_l2norm && l < C) {
+      rq_all = sNrm[l];
+      rk_all = sNrm[C + l];
+    }
     if (grp < NU) {
       float4 offs = f4(0.f);
       for (int g2 = 0; g2 < grp; ++g2) offs = offs + *reinterpret_cast<const float4*>(sAA + g2 * D + c4);
@@ -636,7 +695,16 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   //    sub-block s = 1..3 against the columns before r'), one tile each.
   //    Pairs inside one sub-block (and Aq's diagonal) follow in 3b.
   {
-    auto store_tile = [&](int I, int J, const f32x4& accA, const f32x4& accQ, bool diag) {
+    auto store_tile = [&](int I, int J, f32x4 accA, f32x4 accQ, bool diag) {
+      if (qk_l2norm) {  // rows t = 16 I + 4 lg + i, column j = 16 J + lr
+        const float rkj = rk_of(16 * J + lr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * I + 4 * lg + i;
+          accA[i] *= rk_of(t) * rkj;
+          accQ[i] *= rq_of(t) * rkj;
+        }
+      }
       // keep, on the diagonal, rows of a later sub-block than the column only
       const bool keep = !diag || (lg > (lr >> 2));
       if (keep) {
@@ -799,6 +867,13 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const int a2 = 1 + (m >= 1) + (m >= 3), b2 = m - a2 * (a2 - 1) / 2;
     const int idx = r < 6 ? iA(t0 + b2, t0 + a2)
                           : (r < 12 ? iA(t0 + a2, t0 + b2) : iA(t0 + r - 12, t0 + r - 12));
+    if (qk_l2norm) {  // row rt, column rj of the sum this lane holds
+      // every shuffle runs on all lanes (a lane-dependent choice of which one
+      // to run would leave source lanes inactive, and those read as zero)
+      const int rt = r < 12 ? t0 + a2 : t0 + r - 12, rj = r < 12 ? t0 + b2 : rt;
+      const float rkt = rk_of(rt), rqt = rq_of(rt), rkj = rk_of(rj);
+      v[0] *= (r < 6 ? rkt : rqt) * rkj;
+    }
     sAA[idx] = v[0];
   }
   __syncthreads();
@@ -818,8 +893,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     float x[8], g8[8];
     row_io8(sQ, t, c0, x);
     row_g8(t, c0, g8);
+    const float sc = qk_l2norm ? scale * rq_of(t) : scale;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) x[j] = scale * x[j] * ex2(g8[j]);
+    for (int j = 0; j < 8; ++j) x[j] = sc * x[j] * ex2(g8[j]);
     put_frag(Gm::Q_OFF + (uint32_t)tile * FRAG_BYTES, split8(x));
   }
   // (K e^{G_C - G})^T as A fragments [MTD][KTC]: rows = channels
@@ -839,6 +915,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     for (int j = 0; j < 8; ++j) {
       const int idx = base + j * D + (((X ^ j) & (NG - 1)) << 3);
       x[j] = t0 + j < C ? to_f32(sK[idx]) * ex2(glast - sG[idx]) : 0.f;
+    }
+    if (qk_l2norm) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] *= rk_of(min(t0 + j, C - 1));
     }
     put_frag(Gm::KT_OFF + (uint32_t)tile * FRAG_BYTES, split8(x));
   }
@@ -870,11 +950,13 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll
     for (int i = 0; i < G4; ++i) {
       const int e = tid + i * NT, t = e / (D / 4), c = (e % (D / 4)) * 4;
+      const float rk = qk_l2norm ? rk_of(min(t, C - 1)) : 1.f;
       if (e < C * (D / 4)) {
         const float4 kk = load4(sK + iG(t, c));
         const float4 gg = *reinterpret_cast<const float4*>(sG + iG(t, c));
         ke[i] = make_float4(kk.x * ex2(gg.x), kk.y * ex2(gg.y), kk.z * ex2(gg.z),
                             kk.w * ex2(gg.w));
+        if (qk_l2norm) ke[i] = rk * ke[i];
       }
     }
     __syncthreads();
@@ -1566,7 +1648,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
                        (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs, a.gate_mode,
                        a.A_log, a.dt_bias, a.lower_bound, a.qk_heads > 0 ? a.qk_heads : a.H,
-                       a.per_head_gate);
+                       a.per_head_gate, a.qk_l2norm);
   if ((e = mark(2)) != hipSuccess) return e;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;

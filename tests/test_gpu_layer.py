@@ -262,3 +262,66 @@ def test_prefill_options_snapshots_equal_snapshot_entry_point():
                                       snapshots=s2, snapshot_interval=128)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(h1, h2) and torch.equal(s1, s2)
+
+
+# ---------------------------------------------- in-kernel L2 norm in prefill
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("D,chunk", [(128, 64), (64, 32), (32, 64), (16, 16)])
+def test_prefill_l2norm_matches_oracle(io, D, chunk):
+    """Un-normalised q and k, normalised in the kernel: the oracle runs on
+    l2norm(q), l2norm(k) (fp64, eps 1e-6)."""
+    c = _prefill_case(io, seqlens=(200, 64, 5, 130), K=D, V=D, seed=21)
+    q, k = _raw_qk(c, 21)
+    iot = TORCH_IO[io]
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    o, ht = kda.kda_chunk_prefill_ex(dev(q, iot), dev(k, iot), dev(c["v"], iot), dev(g),
+                                     dev(beta), dev(c["cu"], torch.int32), D ** -0.5,
+                                     h0=dev(c["h0"]), chunk=chunk, qk_l2norm=True)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.prefill(oracle.l2norm(q), oracle.l2norm(k), c["v"], g, beta,
+                                   c["cu"], D ** -0.5, c["h0"])
+    assert_io_output(host(o), o_ref, io, 1)
+    assert rel_err_blocks(host(ht), ht_ref, 2) <= TOL[io]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_prefill_l2norm_with_grouped_heads_and_raw_gate(io):
+    """Every prefill option at once: 2 q/k heads for 8 value heads, the
+    softplus gate from raw a and b, and the in-kernel L2 norm."""
+    c = _prefill_case(io, seqlens=(150, 1, 64, 97), H=8, K=64, V=64, seed=22)
+    q, k = _raw_qk(c, 22)
+    qg, kg = q[:, :2], k[:, :2]
+    iot = TORCH_IO[io]
+    o, ht = kda.kda_chunk_prefill_ex(dev(qg, iot), dev(kg, iot), dev(c["v"], iot),
+                                     dev(c["a"]), dev(c["b"]), dev(c["cu"], torch.int32), 0.125,
+                                     h0=dev(c["h0"]), chunk=32, qk_l2norm=True,
+                                     raw_gate=(dev(c["A_log"]), dev(c["dt_bias"]), 0.0))
+    torch.cuda.synchronize()
+    g_ref, b_ref = oracle.gate(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    rep = lambda x: np.repeat(oracle.l2norm(x), 4, axis=1)
+    o_ref, ht_ref = oracle.prefill(rep(qg), rep(kg), c["v"], g_ref, b_ref, c["cu"], 0.125,
+                                   c["h0"])
+    assert_io_output(host(o), o_ref, io, 1)
+    assert rel_err_blocks(host(ht), ht_ref, 2) <= TOL[io]
+
+
+def test_prefill_l2norm_varlen_workload_sampled_heads():
+    """The varlen batch's shape ({512, 1024, 2048, 4096}, H = 32, K = V = 128,
+    bf16, chunk 64, slow decay) with raw q and k, checked on three heads."""
+    w = kda_synth.WORKLOADS["varlen_prefill_7680"]
+    c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], "bf16", seed=23,
+                               regime="long", dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
+    q, k = _raw_qk(c, 23)
+    g, beta = gates_f32(c["a"], c["b"], c["A_log"], c["dt_bias"])
+    bf = torch.bfloat16
+    o, ht = kda.kda_chunk_prefill_ex(dev(q, bf), dev(k, bf), dev(c["v"], bf), dev(g), dev(beta),
+                                     dev(c["cu"], torch.int32), w["K"] ** -0.5,
+                                     h0=dev(c["h0"]), chunk=w["chunk"], qk_l2norm=True)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    sub = lambda x: np.ascontiguousarray(x[:, heads])
+    o_ref, ht_ref = oracle.prefill(oracle.l2norm(sub(q)), oracle.l2norm(sub(k)), sub(c["v"]),
+                                   sub(g), sub(beta), c["cu"], w["K"] ** -0.5, sub(c["h0"]))
+    assert_io_output(host(o)[:, heads], o_ref, "bf16", 1)
+    assert rel_err_blocks(host(ht)[:, heads], ht_ref, 2) <= TOL["bf16"]
