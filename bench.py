@@ -71,6 +71,32 @@ def _time(fn, steps: int, warmup: int, settle_s: float | None = None) -> float:
 
 # ------------------------------------------------------------ byte models
 
+_FLUSH = None
+
+
+def _time_flushed(fn, reps: int = 20) -> float:
+    """Median milliseconds of single calls of fn, each timed alone between
+    HIP events after a write and then a read of a 512 MiB scratch buffer
+    (twice the 256 MB last-level cache): no input of fn is served from that
+    cache, and the read leaves no dirty lines whose write-back would fall in
+    the timed call."""
+    global _FLUSH
+    if _FLUSH is None:
+        _FLUSH = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+    fn()
+    times = []
+    for _ in range(reps):
+        _FLUSH.fill_(1.0)
+        _FLUSH.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    return float(np.median(times))
+
+
 def prefill_bytes(T, N, H, K, V, io_bytes=2):
     """Algorithmic HBM bytes of one prefill call: q, k, v, o in the io dtype,
     g fp32, beta fp32 per token-head; h0 read and ht written per sequence."""
@@ -242,11 +268,13 @@ def bench_decode(steps, warmup):
     o = torch.empty_like(v)
     fn = lambda: kda.kda_recurrent_decode(q, k, v, g, beta, w["K"] ** -0.5, pool, idx, o=o)
     ms = _time(fn, max(steps, 20), warmup)
+    ms_flushed = _time_flushed(fn)
     B, H, K, V = w["B"], w["H"], w["K"], w["V"]
     nbytes = decode_bytes(B, H, K, V)
     state = 2 * B * H * K * V * 4
     return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9)
+                gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9,
+                ms_flushed=ms_flushed, gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9)
 
 
 def bench_decode_layer(steps, warmup):
@@ -323,9 +351,11 @@ def bench_verify(steps, warmup):
     o = torch.empty_like(v)
     fn = lambda: kda.kda_verify(q, k, v, g, beta, K ** -0.5, pool, idx, inter_states=inter, o=o)
     ms = _time(fn, max(steps, 20), warmup)
+    ms_flushed = _time_flushed(fn)
     nbytes = verify_bytes(B, Tv, H, K, V)
     return dict(ms=ms, tokens_per_s=B * Tv / (ms * 1e-3), bytes=nbytes,
-                gbs=nbytes / (ms * 1e-3) / 1e9)
+                gbs=nbytes / (ms * 1e-3) / 1e9, ms_flushed=ms_flushed,
+                gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9)
 
 
 def bench_long(steps, warmup):
@@ -579,9 +609,14 @@ def main():
     }
     d = bench_decode(args.steps, args.warmup)
     line["decode"] = {"workload": "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",
-                      "tokens_per_s": d["tokens_per_s"], "ms": d["ms"],
-                      "state_gbs": d["state_gbs"], "total_gbs": d["gbs"],
-                      "frac_of_hbm_peak": d["gbs"] / HBM_PEAK_GBS}
+                      "timing": "median of single calls, each after a 512 MiB write and read "
+                                "that empty the last-level cache",
+                      "tokens_per_s": 256 / (d["ms_flushed"] * 1e-3), "ms": d["ms_flushed"],
+                      "state_gbs": d["state_gbs"] * d["ms"] / d["ms_flushed"],
+                      "total_gbs": d["gbs_flushed"],
+                      "frac_of_hbm_peak": d["gbs_flushed"] / HBM_PEAK_GBS,
+                      "back_to_back": {"ms": d["ms"], "tokens_per_s": d["tokens_per_s"],
+                                       "total_gbs": d["gbs"]}}
     dl = bench_decode_layer(args.steps, args.warmup)
     line["decode"]["with_layer_options"] = {
         "what": "raw gate in the kernel, q/k L2 norm, gated RMSNorm of o (kda_recurrent_decode_ex)",
@@ -598,8 +633,14 @@ def main():
                              "speedup_vs_decode": d["ms"] / rp["ms"]}
     vr = bench_verify(args.steps, args.warmup)
     line["verify"] = {"workload": "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool",
-                      "tokens_per_s": vr["tokens_per_s"], "ms": vr["ms"],
-                      "total_gbs": vr["gbs"], "frac_of_hbm_peak": vr["gbs"] / HBM_PEAK_GBS}
+                      "timing": "median of single calls, each after a 512 MiB write and read "
+                                "that empty the last-level cache (the 134 MB of pool a call "
+                                "reads would otherwise stay cached between calls)",
+                      "tokens_per_s": 512 / (vr["ms_flushed"] * 1e-3), "ms": vr["ms_flushed"],
+                      "total_gbs": vr["gbs_flushed"],
+                      "frac_of_hbm_peak": vr["gbs_flushed"] / HBM_PEAK_GBS,
+                      "back_to_back": {"ms": vr["ms"], "tokens_per_s": vr["tokens_per_s"],
+                                       "total_gbs": vr["gbs"]}}
     if not args.no_long:
         lg = bench_long(args.steps, args.warmup)
         line["long"] = {"workload": "long_prefill_65536: 16 carried 4096-token segments "
@@ -615,9 +656,9 @@ def main():
     line["roofline"]["frac_of_measured"] = line["roofline"]["achieved"] / (
         cl["hbm_copy_gbs"] if line["roofline"]["unit"] == "GB/s" else cl["bf16_mfma_32x32x16_tflops"])
     line["prefill"]["frac_of_measured_copy"] = achieved / cl["hbm_copy_gbs"]
-    line["decode"]["frac_of_measured_rmw"] = d["gbs"] / cl["hbm_rmw_gbs"]
+    line["decode"]["frac_of_measured_rmw"] = d["gbs_flushed"] / cl["hbm_rmw_gbs"]
     line["replay_decode"]["frac_of_measured_copy"] = rp["gbs"] / cl["hbm_copy_gbs"]
-    line["verify"]["frac_of_measured_copy"] = vr["gbs"] / cl["hbm_copy_gbs"]
+    line["verify"]["frac_of_measured_copy"] = vr["gbs_flushed"] / cl["hbm_copy_gbs"]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(p["inputs"], w)
     print(json.dumps(line))
