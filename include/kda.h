@@ -380,10 +380,12 @@ kda_status kda_replay_decode(kda_dtype io, const void* q, const void* k,
 
 /*
  * kda_replay_decode with model-layer options (kda_step_opts): the gate from
- * raw inputs, the per-head gate and grouped q/k heads (q, k [B, qk_heads,
- * K]; g [B, H, K] or [B, H]).  The ring keeps the activated per-channel g.
- * qk_l2norm and o_gate are not supported here (KDA_ERR_UNSUPPORTED).  With
- * opts NULL the results are bit-identical to kda_replay_decode.
+ * raw inputs, the per-head gate, grouped q/k heads (q, k [B, qk_heads, K];
+ * g [B, H, K] or [B, H]), the in-kernel q/k L2 norm and the gated RMSNorm of
+ * o (o_gate [B, H, V]).  The ring keeps the activated per-channel g and k
+ * as given (with qk_l2norm each entry's k row is normalised again when it is
+ * replayed).  With opts NULL the results are bit-identical to
+ * kda_replay_decode.
  */
 kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
                                 const void* v, const float* g, const float* beta,

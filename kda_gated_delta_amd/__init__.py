@@ -345,14 +345,17 @@ def kda_verify(q, k, v, g, beta, scale: float, state_pool, slot_idx,
 
 def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, write_pos,
                       ring_d, ring_k, ring_g, force_flush=None, o=None, next_write_pos=None,
-                      raw_gate=None, per_head_gate=False):
+                      raw_gate=None, per_head_gate=False, qk_l2norm=False, o_gate=None,
+                      o_norm_w=None, o_norm_eps: float = 1e-6, o_gate_act: str = "sigmoid"):
     """Buffered single-token decode.  ``state_pool`` [n_slots,H,K,V] holds the
     checkpoints; the rings ring_d [n_slots,H,L,V] fp32, ring_k [n_slots,H,L,K]
     (io dtype) and ring_g [n_slots,H,L,K] fp32 hold the steps since them;
     ``write_pos`` [B] int32 is each row's cursor.  ``raw_gate`` = (A_log,
     dt_bias, lower_bound) applies the gate to the raw a given as g (beta is
     then the raw b); ``per_head_gate`` takes g [B,H]; q, k may have fewer
-    heads than v (grouped heads).  Returns (o [B,H,V], next_write_pos [B])."""
+    heads than v (grouped heads); ``qk_l2norm`` and ``o_gate`` (with
+    ``o_norm_w``) as in kda_recurrent_decode_ex.  Returns (o [B,H,V],
+    next_write_pos [B])."""
     B, HK, K = q.shape
     H, V = v.shape[1], v.shape[2]
     dev = q.device
@@ -379,11 +382,11 @@ def kda_replay_decode(q, k, v, g, beta, scale: float, state_pool, slot_idx, writ
     args = [io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), float(scale), _ptr(state_pool),
             n_slots, _ptr(slot_idx), _ptr(write_pos), _ptr(force_flush), L, _ptr(ring_d),
             _ptr(ring_k), _ptr(ring_g), B, H, K, V, _ptr(o), _ptr(next_write_pos)]
-    if raw_gate is None and not per_head_gate and HK == H:
+    if raw_gate is None and not per_head_gate and HK == H and not qk_l2norm and o_gate is None:
         _check("kda_replay_decode", lib().kda_replay_decode(*args, _stream(dev)))
     else:
-        op = _step_opts(H, (B,), K, V, dev, q.dtype, raw_gate, per_head_gate, False, HK, None,
-                        None, 0.0, "sigmoid")
+        op = _step_opts(H, (B,), K, V, dev, q.dtype, raw_gate, per_head_gate, qk_l2norm, HK,
+                        o_gate, o_norm_w, o_norm_eps, o_gate_act)
         _check("kda_replay_decode_ex", lib().kda_replay_decode_ex(*args, ctypes.byref(op),
                                                                   _stream(dev)))
     return o, next_write_pos

@@ -291,7 +291,6 @@ kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
                                 int32_t K, int32_t V, void* o, int32_t* next_write_pos,
                                 const kda_step_opts* opts, void* stream) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-  if (opts && (opts->qk_l2norm || opts->o_gate)) return KDA_ERR_UNSUPPORTED;
   if (B < 1 || H < 1 || n_slots < 1) return KDA_ERR_INVALID_ARGUMENT;
   if (ring_len < 1 || ring_len > KDA_RING_MAX) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V)) return KDA_ERR_UNSUPPORTED;

@@ -386,6 +386,7 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   __shared__ float sq[K], sk[K], sa[K], sg[K];
   __shared__ __align__(16) float swk[RING_MAX][K], sgr[RING_MAX][K], sd[RING_MAX][V];
   __shared__ float sck[RING_MAX], scq[RING_MAX];
+  __shared__ float snq[2], snr[RING_MAX];  // L2 norm option: token q, k; ring k rows
   __shared__ float sdump[3];
   __shared__ float spart[Sh::NT / K][K];
   __shared__ float red[Sh::RED];
@@ -502,6 +503,30 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     if (t < K) sg[t] = gate_of(sg[t], t, K, h, op);
     __syncthreads();
   }
+  if (OPT && op.qk_l2norm) {
+    // The token's q and k by the decode kernel's own norms.  The ring keeps
+    // raw k rows (exact in the io dtype); each entry's row is normalised
+    // here again, before its decay weight multiplies it: entry j's LPE
+    // lanes sum its squares, every LPE-th channel each.
+    qk_rnorms<IO, K, Sh::NW>(q, k, [&](int) { return qk; }, 1, snq, snq + 1);
+    constexpr int LPE = Sh::NT / RING_MAX, CPL = K / LPE;
+    const int j = t / LPE, pl = t % LPE;
+    float ss = 0.f;
+    if (j < m) {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) ss = fmaf(swk[j][pl + LPE * i], swk[j][pl + LPE * i], ss);
+    }
+#pragma unroll
+    for (int x = 1; x < LPE; x <<= 1) ss += __shfl_xor(ss, x, 64);
+    if (pl == 0 && j < m) snr[j] = 1.f / sqrtf(ss + 1e-6f);
+    __syncthreads();
+    if (t < K) {
+      sq[t] *= snq[0];
+      sk[t] *= snq[1];
+    }
+    for (int e = t; e < m * K; e += Sh::NT) swk[e / K][e % K] *= snr[e / K];
+    __syncthreads();
+  }
   const float b = OPT ? strength_of(braw, op) : braw;
   // Decay weights per key channel, newest entry first: w_j k_j in place of
   // k_j, then A.  The NG = NT / K thread groups of a channel take EPG
@@ -575,7 +600,10 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   p = reduce_rows<K, V>(p, red);
   const float4 d = b * (vv - p.vh);
   const float4 oq = fma4(p.qk, d, p.qs);
-  if (rg == 0) store4(o + rh * V + c0, scale * oq);
+  float4 out = scale * oq;
+  if (OPT && op.o_gate != nullptr)  // the layer's gated RMSNorm, as in decode
+    out = out_norm<IO, V, Sh::CG>(out, rg == 0, static_cast<const IO*>(op.o_gate) + rh * V, c0, op);
+  if (rg == 0) store4(o + rh * V + c0, out);
   if (flush) {
 #pragma unroll
     for (int i = 0; i < Sh::RPT; ++i) s[i] = fma4(sk[rg + Sh::RG * i], d, s[i]);
@@ -588,7 +616,7 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
   } else {
     if (rg == 0) store4(ring_d + (e0 + pos) * V + c0, d);
-    if (t < K) {  // k was read as io values: converting back is exact; g as activated
+    if (t < K) {  // k as read (raw: exact in io), g as activated
       ring_k[(e0 + pos) * K + t] = from_f32<IO>(tk);
       ring_g[(e0 + pos) * K + t] = OPT ? sg[t] : tg;
     }
@@ -600,7 +628,8 @@ template <typename IO, int K, int V>
 hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
   typedef StepShape<K, V> Sh;
   const bool opt = a.opts.gate_mode != 0 || a.opts.per_head_gate != 0 ||
-                   (a.opts.qk_heads > 0 && a.opts.qk_heads != a.H);
+                   (a.opts.qk_heads > 0 && a.opts.qk_heads != a.H) || a.opts.qk_l2norm != 0 ||
+                   a.opts.o_gate != nullptr;
   hipLaunchKernelGGL((opt ? replay_kernel<IO, K, V, true> : replay_kernel<IO, K, V, false>),
                      dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
                      a.scale, a.pool, a.slot_idx, a.write_pos, a.force_flush, a.L, a.ring_d,

@@ -238,16 +238,21 @@ def test_prefill_options_validation():
 def test_replay_options_validation():
     L = kda.lib()
     W, N, F = ctypes.c_void_p(8192), ctypes.c_void_p(8192 + 64), ctypes.c_void_p(8192 + 128)
-    op = kda.StepOpts()
-    op.qk_l2norm = 1
 
     def call(o):
         return L.kda_replay_decode_ex(1, P, P, P, P, P, 1.0, P, 8, P, W, F, 16, P, P, P, 4, 2,
                                       128, 128, P, N, ctypes.byref(o), None)
-    assert call(op) == UNSUPPORTED
+    # the output norm's arguments are checked as for decode and verify
     op = kda.StepOpts()
-    op.o_gate, op.o_norm_w = 4096, 4096
-    assert call(op) == UNSUPPORTED
+    op.qk_l2norm = 1
+    op.o_gate = 4096  # no weight
+    assert call(op) == INVALID
+    op.o_norm_w = 4096 + 4  # misaligned weight
+    assert call(op) == INVALID
+    op.o_norm_w, op.o_gate_act = 4096, 2  # unknown activation
+    assert call(op) == INVALID
+    op.o_gate_act, op.o_norm_eps = 0, -1.0
+    assert call(op) == INVALID
     op = kda.StepOpts()
     op.gate_mode = 1  # no A_log
     assert call(op) == INVALID

@@ -212,3 +212,81 @@ def test_replay_options_equal_prepared_inputs(io):
         assert torch.equal(pos_a, pos_b) and torch.equal(pool_a, pool_b), s
     for x, y in zip(ra, rb):
         assert torch.equal(torch.nan_to_num(x, nan=7.0), torch.nan_to_num(y, nan=7.0))
+
+
+# --------------------------------------------------- L2 norm and output norm
+
+def _raw_qk(c, seed):
+    """Un-normalised q and k of the case's shape, rounded to its io dtype."""
+    r = np.random.default_rng(seed)
+    rt = lambda x: torch.from_numpy(x).to(TORCH_IO[c["io"]]).to(torch.float64).numpy()
+    return rt(r.standard_normal(c["q"].shape) * 0.7), rt(r.standard_normal(c["k"].shape) * 1.3)
+
+
+def _norm_opts(c, seed):
+    B, steps, H, V = c["B"], c["q"].shape[1], c["H"], c["V"]
+    r = np.random.default_rng(seed)
+    z = torch.from_numpy(r.standard_normal((B, steps, H, V))).to(TORCH_IO[c["io"]])
+    w = (1.0 + 0.1 * r.standard_normal(V)).astype(np.float32)
+    return z, w
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_ring_of_one_with_norms_is_the_plain_decode_with_norms(io):
+    """Ring length 1 (every call flushes, nothing is replayed) with the q/k L2
+    norm and the gated RMSNorm equals kda_recurrent_decode_ex with the same
+    options, bit for bit, o and pool, over several steps."""
+    c = _case(6, 4, 128, 128, 9, io, seed=71, steps=4, n_padding=1)
+    q_raw, k_raw = _raw_qk(c, 71)
+    z, w = _norm_opts(c, 72)
+    iot = TORCH_IO[io]
+    pool_a, pool_b = dev(c["pool"]), dev(c["pool"])
+    idx = dev(c["slot_idx"], torch.int32)
+    rd, rk, rg = _rings(c, 1)
+    pos = torch.zeros(c["B"], dtype=torch.int32, device="cuda")
+    for s in range(4):
+        q, k = dev(q_raw[:, s], iot), dev(k_raw[:, s], iot)
+        _, _, v, g, beta = _step_inputs(c, s)
+        zz = z[:, s].contiguous().cuda()
+        o_a = kda.kda_recurrent_decode_ex(q, k, v, g, beta, _scale(128), pool_a, idx,
+                                          qk_l2norm=True, o_gate=zz, o_norm_w=dev(w),
+                                          o_gate_act="silu")
+        o_b, pos = kda.kda_replay_decode(q, k, v, g, beta, _scale(128), pool_b, idx, pos,
+                                         rd, rk, rg, qk_l2norm=True, o_gate=zz,
+                                         o_norm_w=dev(w), o_gate_act="silu")
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b) and torch.equal(pool_a, pool_b), s
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("L", [4, 16])
+def test_ring_steps_with_norms_match_oracle(io, L):
+    """Raw q and k normalised in the kernel, ring entries replayed from raw k
+    rows, and the gated RMSNorm of o, against the oracle's decode on
+    l2norm(q), l2norm(k) followed by its gated_rmsnorm; slow decay so that
+    the replayed terms carry the state."""
+    c = _case(5, 4, 128, 128, 9, io, seed=73 + L, steps=2 * L + 3, regime="long", n_padding=1)
+    steps, B, K = 2 * L + 3, c["B"], c["K"]
+    q_raw, k_raw = _raw_qk(c, 74)
+    z, w = _norm_opts(c, 75)
+    iot = TORCH_IO[io]
+    pool_d, idx_d = dev(c["pool"]), dev(c["slot_idx"], torch.int32)
+    live = c["slot_idx"] >= 0
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    rd, rk, rg = _rings(c, L)
+    pool_ref = c["pool"].astype(np.float64)
+    for s in range(steps):
+        _, _, v, g, beta = _step_inputs(c, s)
+        force = np.zeros(B, dtype=np.int32)
+        if s == L // 2:
+            force[1] = 1  # one row flushed early: its cursor runs apart
+        o, pos = kda.kda_replay_decode(dev(q_raw[:, s], iot), dev(k_raw[:, s], iot), v, g, beta,
+                                       _scale(K), pool_d, idx_d, pos, rd, rk, rg,
+                                       force_flush=dev(force, torch.int32), qk_l2norm=True,
+                                       o_gate=z[:, s].contiguous().cuda(), o_norm_w=dev(w))
+        o_ref, pool_ref = oracle.decode(oracle.l2norm(q_raw[:, s]), oracle.l2norm(k_raw[:, s]),
+                                        c["v"][:, s], c["g"][:, s], c["beta"][:, s], _scale(K),
+                                        pool_ref, c["slot_idx"])
+        o_ref = oracle.gated_rmsnorm(o_ref, z[:, s].to(torch.float64).numpy(), w, 1e-6)
+        torch.cuda.synchronize()
+        assert_io_output(host(o)[live], o_ref[live], io, 1)
