@@ -33,7 +33,17 @@
  *   - Errors are returned, never thrown.  Host-side validation covers null
  *     pointers, alignment, sizes and supported shapes; on any error nothing
  *     is enqueued.  Values that live in device memory (cu_seqlens, slot
- *     indices) are the caller's contract and are not read by the host.
+ *     indices, ring cursors) are the caller's contract and are not read by
+ *     the host.  The kernels still keep every access in bounds: cu_seqlens
+ *     are clamped into [0, T], and a live slot index at or past n_slots (or
+ *     a ring cursor outside the ring) gives o = NaN for that row and touches
+ *     no state.
+ *   - Debug checks: when the environment variable KDA_CHECK is "1" (read at
+ *     every call), each call copies those device arrays to the host (waiting
+ *     for the stream) and returns KDA_ERR_INVALID_ARGUMENT, with nothing
+ *     enqueued, unless cu_seqlens starts at 0, ends at T and never
+ *     decreases; every live slot is below n_slots and appears once; and every
+ *     ring cursor lies in [0, ring_len).
  *   - Supported head sizes: K, V in {16, 32, 64, 128}.
  */
 #ifndef KDA_H_

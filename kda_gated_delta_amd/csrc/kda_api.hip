@@ -3,6 +3,10 @@
 // synchronises or keeps state; every launch goes to the caller's stream.
 
 #include "kda.h"
+
+#include <algorithm>
+#include <cstdlib>
+#include <vector>
 #include "kda_internal.h"
 
 namespace {
@@ -18,6 +22,58 @@ bool io_aligned(kda_dtype io, const void* p) {
 }
 
 kda_status launch_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_LAUNCH; }
+
+// Debug checks of the device-resident preconditions, on when the environment
+// variable KDA_CHECK is "1" (read at every call): the index arrays are copied
+// to the host, which waits for the stream, and checked before anything is
+// enqueued.  Off (the default), nothing is read back and nothing waits.
+bool debug_checks() {
+  const char* e = std::getenv("KDA_CHECK");
+  return e != nullptr && e[0] == '1' && e[1] == '\0';
+}
+
+kda_status read_back(const int32_t* src, size_t n, hipStream_t st, std::vector<int32_t>& dst) {
+  dst.resize(n);
+  if (hipMemcpyAsync(dst.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return KDA_ERR_LAUNCH;
+  return KDA_OK;
+}
+
+// cu_seqlens: cu[0] = 0, cu[N] = T, non-decreasing.
+kda_status check_cu(const int32_t* cu, int32_t N, int64_t T, hipStream_t st) {
+  std::vector<int32_t> h;
+  if (kda_status s = read_back(cu, (size_t)N + 1, st, h)) return s;
+  if (h[0] != 0 || h[N] != T) return KDA_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < N; ++i)
+    if (h[i + 1] < h[i]) return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
+
+// slot_idx: every live (non-negative) slot below n_slots, no slot twice.
+kda_status check_slots(const int32_t* idx, int32_t B, int64_t n_slots, hipStream_t st) {
+  std::vector<int32_t> h;
+  if (kda_status s = read_back(idx, (size_t)B, st, h)) return s;
+  std::vector<int32_t> live;
+  for (int32_t x : h) {
+    if (x < 0) continue;
+    if (x >= n_slots) return KDA_ERR_INVALID_ARGUMENT;
+    live.push_back(x);
+  }
+  std::sort(live.begin(), live.end());
+  return std::adjacent_find(live.begin(), live.end()) == live.end() ? KDA_OK
+                                                                    : KDA_ERR_INVALID_ARGUMENT;
+}
+
+// write_pos of the buffered decode: every cursor in [0, ring_len).
+kda_status check_cursors(const int32_t* pos, int32_t B, int32_t L, hipStream_t st) {
+  std::vector<int32_t> h;
+  if (kda_status s = read_back(pos, (size_t)B, st, h)) return s;
+  for (int32_t x : h)
+    if (x < 0 || x >= L) return KDA_ERR_INVALID_ARGUMENT;
+  return KDA_OK;
+}
 
 // Checks the model-layer options and converts them (NULL = the plain step).
 kda_status step_opts(const kda_step_opts* in, kda_dtype io, int32_t H, kda::StepOpts& out) {
@@ -74,6 +130,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
     return KDA_ERR_WORKSPACE;
   if (gate_mode != 0 && T > 0 && (!A_log || (dt_bias && !aligned16(dt_bias))))
     return KDA_ERR_INVALID_ARGUMENT;
+  if (debug_checks())
+    if (kda_status st = check_cu(cu_seqlens, N, T, (hipStream_t)stream)) return st;
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
                      gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval,
@@ -231,8 +289,10 @@ kda_status kda_recurrent_decode_ex(kda_dtype io, const void* q, const void* k,
     return KDA_ERR_INVALID_ARGUMENT;
   kda::StepOpts op;
   if (kda_status st = step_opts(opts, io, H, op)) return st;
+  if (debug_checks())
+    if (kda_status st = check_slots(slot_idx, B, n_slots, (hipStream_t)stream)) return st;
   kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
-                    B, 1, H, K, V, nullptr, o, op};
+                    B, 1, H, K, V, nullptr, o, op, n_slots};
   return launch_status(kda::run_decode(p, (hipStream_t)stream));
 }
 
@@ -263,9 +323,11 @@ kda_status kda_verify_ex(kda_dtype io, const void* q, const void* k,
     return KDA_ERR_INVALID_ARGUMENT;
   kda::StepOpts op;
   if (kda_status st = step_opts(opts, io, H, op)) return st;
+  if (debug_checks())
+    if (kda_status st = check_slots(slot_idx, B, n_slots, (hipStream_t)stream)) return st;
   kda::DecodeArgs p{io == KDA_BF16, q, k, v, g, beta, scale,
                     const_cast<float*>(state_pool), slot_idx, B, Tv, H, K, V,
-                    inter_states, o, op};
+                    inter_states, o, op, n_slots};
   return launch_status(kda::run_verify(p, (hipStream_t)stream));
 }
 
@@ -313,9 +375,13 @@ kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
   }
   kda::StepOpts op;
   if (kda_status st = step_opts(opts, io, H, op)) return st;
+  if (debug_checks()) {
+    if (kda_status st = check_slots(slot_idx, B, n_slots, (hipStream_t)stream)) return st;
+    if (kda_status st = check_cursors(write_pos, B, ring_len, (hipStream_t)stream)) return st;
+  }
   kda::ReplayArgs p{io == KDA_BF16, q, k, v, g, beta, scale, state_pool, slot_idx,
                     write_pos, force_flush, ring_len, ring_d, ring_k, ring_g, B, H, K, V, o,
-                    next_write_pos, op};
+                    next_write_pos, op, n_slots};
   return launch_status(kda::run_replay(p, (hipStream_t)stream));
 }
 

@@ -214,7 +214,8 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_ke
     const IO* __restrict__ q, const IO* __restrict__ k,
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale, float* __restrict__ pool,
-    const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o, StepOpts op) {
+    const int32_t* __restrict__ slot_idx, int H, IO* __restrict__ o, StepOpts op,
+    int64_t n_slots) {
   constexpr int VS = slice_cols<V>(), NS = V / VS;
   typedef StepShape<K, VS> Sh;
   __shared__ float sq[K], sk[K], sa[K];
@@ -225,8 +226,10 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_ke
   const int r = (int)(rh / H), h = (int)(rh % H);
   const int c0 = (blockIdx.x % NS) * VS + 4 * cg;  // this thread's first state column
   const int64_t slot = slot_idx[r];
-  if (slot < 0) {
-    if (rg == 0) store4(o + rh * V + c0, f4(0.f));
+  if (slot < 0 || slot >= n_slots) {
+    // padding row: o = 0; a slot past the pool: o = NaN (a caller error made
+    // visible).  Neither touches the pool.
+    if (rg == 0) store4(o + rh * V + c0, f4(slot < 0 ? 0.f : __builtin_nanf("")));
     return;
   }
   float* S = pool + (slot * H + h) * (int64_t)(K * V);
@@ -271,7 +274,7 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
     const IO* __restrict__ v, const float* __restrict__ g,
     const float* __restrict__ beta, float scale,
     const float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
-    int Tv, int H, float* __restrict__ inter, IO* __restrict__ o, StepOpts op) {
+    int Tv, int H, float* __restrict__ inter, IO* __restrict__ o, StepOpts op, int64_t n_slots) {
   constexpr int VS = slice_cols<V>(), NS = V / VS;
   typedef StepShape<K, VS> Sh;
   __shared__ float sq[TVB][K], sk[TVB][K], sa[TVB][K], sb[TVB];
@@ -283,10 +286,12 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
   const int r = rh / H, h = rh % H;
   const int c0 = (blockIdx.x % NS) * VS + 4 * cg;  // this thread's first state column
   const int64_t slot = slot_idx[r];
-  if (slot < 0) {
+  if (slot < 0 || slot >= n_slots) {
+    // padding row: o = 0; a slot past the pool: o = NaN.  inter stays unwritten.
     if (rg == 0)
       for (int s = 0; s < Tv; ++s)
-        store4(o + (((int64_t)r * Tv + s) * H + h) * V + c0, f4(0.f));
+        store4(o + (((int64_t)r * Tv + s) * H + h) * V + c0,
+               f4(slot < 0 ? 0.f : __builtin_nanf("")));
     return;
   }
   const float* S0 = pool + (slot * H + h) * (int64_t)(K * V);
@@ -381,7 +386,7 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
     float* __restrict__ pool, const int32_t* __restrict__ slot_idx,
     const int32_t* __restrict__ write_pos, const int32_t* __restrict__ force_flush, int L,
     float* __restrict__ ring_d, IO* __restrict__ ring_k, float* __restrict__ ring_g, int H,
-    IO* __restrict__ o, int32_t* __restrict__ next_pos, StepOpts op) {
+    IO* __restrict__ o, int32_t* __restrict__ next_pos, StepOpts op, int64_t n_slots) {
   typedef StepShape<K, V> Sh;
   __shared__ float sq[K], sk[K], sa[K], sg[K];
   __shared__ __align__(16) float swk[RING_MAX][K], sgr[RING_MAX][K], sd[RING_MAX][V];
@@ -396,9 +401,10 @@ __global__ __launch_bounds__((StepShape<K, V>::NT)) __attribute__((amdgpu_waves_
   const int c0 = 4 * cg;
   const int64_t slot = slot_idx[r];
   const int pos = write_pos[r];
-  if (slot < 0 || pos < 0 || pos >= L) {
-    // padding row: o = 0; a cursor outside the ring: o = NaN (a caller
-    // error made visible).  Neither touches the pool or the ring.
+  if (slot < 0 || slot >= n_slots || pos < 0 || pos >= L) {
+    // padding row: o = 0; a slot past the pool or a cursor outside the
+    // ring: o = NaN (a caller error made visible).  None touches the pool
+    // or the ring.
     if (rg == 0) store4(o + rh * V + c0, f4(slot < 0 ? 0.f : __builtin_nanf("")));
     if (h == 0 && t == 0 && next_pos != nullptr) next_pos[r] = pos;
     return;
@@ -633,7 +639,7 @@ hipError_t launch_replay(const ReplayArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((opt ? replay_kernel<IO, K, V, true> : replay_kernel<IO, K, V, false>),
                      dim3((unsigned)a.B * a.H), dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v, a.g, a.beta,
                      a.scale, a.pool, a.slot_idx, a.write_pos, a.force_flush, a.L, a.ring_d,
-                     (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos, a.opts);
+                     (IO*)a.ring_k, a.ring_g, a.H, (IO*)a.o, a.next_pos, a.opts, a.n_slots);
   return hipGetLastError();
 }
 
@@ -664,7 +670,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   typedef StepShape<K, slice_cols<V>()> Sh;
   hipLaunchKernelGGL((decode_kernel<IO, K, V>), dim3((unsigned)a.B * a.H * (V / slice_cols<V>())),
                      dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
-                     a.g, a.beta, a.scale, a.pool, a.slot_idx, a.H, (IO*)a.o, a.opts);
+                     a.g, a.beta, a.scale, a.pool, a.slot_idx, a.H, (IO*)a.o, a.opts, a.n_slots);
   return hipGetLastError();
 }
 
@@ -674,7 +680,7 @@ hipError_t launch_verify(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((verify_kernel<IO, K, V>), dim3((unsigned)a.B * a.H * (V / slice_cols<V>())),
                      dim3(Sh::NT), 0, stream, (const IO*)a.q, (const IO*)a.k, (const IO*)a.v,
                      a.g, a.beta, a.scale, a.pool, a.slot_idx, a.Tv, a.H, a.inter, (IO*)a.o,
-                     a.opts);
+                     a.opts, a.n_slots);
   return hipGetLastError();
 }
 

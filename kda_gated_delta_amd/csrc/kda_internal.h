@@ -42,6 +42,7 @@ struct DecodeArgs {
   float* inter;  // verify only
   void* o;
   StepOpts opts;
+  int64_t n_slots;  // live slots must be below it (checked in the kernels)
 };
 
 struct ReplayArgs {
@@ -59,6 +60,7 @@ struct ReplayArgs {
   void* o;
   int32_t* next_pos;
   StepOpts opts;  // gate options and grouped heads (no L2 norm, no output norm)
+  int64_t n_slots;
 };
 
 struct PrefillArgs {

@@ -180,3 +180,106 @@ def test_verify_shapes_long_memory(KV):
     K, V = KV
     c = kda_synth.decode_case(4, 3, K, V, n_slots=5, io="f32", seed=7, Tv=6, regime="long")
     _check_verify(c)
+
+
+# ------------------------------------------- caller errors in device arrays
+
+def _step_case(io="bf16", B=5, n_slots=6, Tv=None):
+    c = kda_synth.decode_case(B, 2, 64, 64, n_slots, io, seed=91, Tv=Tv)
+    lead = (B,) if Tv is None else (B * Tv,)
+    g, beta = gates_f32(c["a"].reshape(lead + (2, 64)), c["b"].reshape(lead + (2,)),
+                        c["A_log"], c["dt_bias"])
+    shp = (B,) if Tv is None else (B, Tv)
+    c["g"], c["beta"] = g.reshape(shp + (2, 64)), beta.reshape(shp + (2,))
+    return c
+
+
+def test_slot_past_the_pool_gives_nan_and_touches_nothing():
+    """A live slot index >= n_slots is caught by the kernels' own bounds:
+    that row's o is NaN, no state is read or written, and the other rows are
+    computed as usual (decode, verify and the buffered decode)."""
+    io = TORCH_IO["bf16"]
+    c = _step_case()
+    idx = c["slot_idx"].copy()
+    idx[2] = c["n_slots"]  # one past the pool
+    q, k, v = (dev(c[x], io) for x in "qkv")
+    g, beta = dev(c["g"]), dev(c["beta"])
+    pool = dev(c["pool"])
+    o = kda.kda_recurrent_decode(q, k, v, g, beta, 0.125, pool, dev(idx, torch.int32))
+    ref_pool = dev(c["pool"])
+    o_ok = kda.kda_recurrent_decode(q, k, v, g, beta, 0.125, ref_pool,
+                                    dev(c["slot_idx"], torch.int32))
+    torch.cuda.synchronize()
+    assert torch.isnan(o[2]).all()
+    keep = [0, 1, 3, 4]
+    assert torch.equal(o[keep], o_ok[keep])
+    # the pool differs from the valid call only in the slot row 2 would have used
+    s2 = int(c["slot_idx"][2])
+    others = [s for s in range(c["n_slots"]) if s != s2]
+    assert torch.equal(pool[others], ref_pool[others])
+    assert torch.equal(pool[s2], dev(c["pool"])[s2])
+    # verify: o NaN for the row, inter left as it was, pool untouched
+    cv = _step_case(Tv=3)
+    inter = torch.full((5, 3, 2, 64, 64), 7.0, device="cuda")
+    pv = dev(cv["pool"])
+    ov, inter = kda.kda_verify(*(dev(cv[x], io) for x in "qkv"), dev(cv["g"]), dev(cv["beta"]),
+                               0.125, pv, dev(idx, torch.int32), inter_states=inter)
+    torch.cuda.synchronize()
+    assert torch.isnan(ov[2]).all() and (inter[2] == 7.0).all()
+    assert torch.equal(pv, dev(cv["pool"]))
+    # buffered decode: o NaN, cursor kept, pool and ring untouched
+    ring = (torch.zeros((6, 2, 4, 64), device="cuda"),
+            torch.zeros((6, 2, 4, 64), dtype=io, device="cuda"),
+            torch.zeros((6, 2, 4, 64), device="cuda"))
+    pos = torch.tensor([0, 1, 2, 3, 0], dtype=torch.int32, device="cuda")
+    pr = dev(c["pool"])
+    orp, nxt = kda.kda_replay_decode(q, k, v, g, beta, 0.125, pr, dev(idx, torch.int32), pos,
+                                     *ring)
+    torch.cuda.synchronize()
+    assert torch.isnan(orp[2]).all() and int(nxt[2]) == 2
+    assert torch.equal(pr[s2], dev(c["pool"])[s2])
+
+
+def test_debug_checks_reject_bad_device_arrays(monkeypatch):
+    """KDA_CHECK=1: bad cu_seqlens, slots past the pool, duplicate live slots
+    and ring cursors outside the ring are rejected before anything runs; good
+    arrays give the same results as without the checks."""
+    io = TORCH_IO["bf16"]
+    c = _step_case()
+    q, k, v = (dev(c[x], io) for x in "qkv")
+    g, beta = dev(c["g"]), dev(c["beta"])
+    pool = dev(c["pool"])
+    good = dev(c["slot_idx"], torch.int32)
+    o_ref = kda.kda_recurrent_decode(q, k, v, g, beta, 0.125, dev(c["pool"]), good)
+    monkeypatch.setenv("KDA_CHECK", "1")
+    for bad in ([0, 1, 6, 2, 3], [0, 1, 1, 2, 3]):  # past the pool; slot 1 twice
+        with pytest.raises(kda.KdaError) as e:
+            kda.kda_recurrent_decode(q, k, v, g, beta, 0.125, pool,
+                                     torch.tensor(bad, dtype=torch.int32, device="cuda"))
+        assert e.value.status == 1
+        with pytest.raises(kda.KdaError):
+            kda.kda_verify(q[:, None], k[:, None], v[:, None], g[:, None], beta[:, None], 0.125,
+                           pool, torch.tensor(bad, dtype=torch.int32, device="cuda"))
+    assert torch.equal(pool, dev(c["pool"]))  # nothing ran
+    o = kda.kda_recurrent_decode(q, k, v, g, beta, 0.125, pool, good)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    ring = (torch.zeros((6, 2, 4, 64), device="cuda"),
+            torch.zeros((6, 2, 4, 64), dtype=io, device="cuda"),
+            torch.zeros((6, 2, 4, 64), device="cuda"))
+    with pytest.raises(kda.KdaError):
+        kda.kda_replay_decode(q, k, v, g, beta, 0.125, pool, good,
+                              torch.tensor([0, 1, 4, 0, 0], dtype=torch.int32, device="cuda"),
+                              *ring)
+    # prefill: cu must start at 0, end at T and never decrease
+    pc = kda_synth.prefill_case([20, 12], 2, 64, 64, "bf16", seed=92)
+    gp, bp = gates_f32(pc["a"], pc["b"], pc["A_log"], pc["dt_bias"])
+    args = [dev(pc[x], io) for x in "qkv"] + [dev(gp), dev(bp)]
+    for cu in ([0, 20, 31], [1, 20, 32], [0, 21, 20]):
+        with pytest.raises(kda.KdaError):
+            kda.kda_chunk_prefill(*args, torch.tensor(cu, dtype=torch.int32, device="cuda"), 0.125)
+    o1, h1 = kda.kda_chunk_prefill(*args, dev(pc["cu"], torch.int32), 0.125)
+    monkeypatch.delenv("KDA_CHECK")
+    o2, h2 = kda.kda_chunk_prefill(*args, dev(pc["cu"], torch.int32), 0.125)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
