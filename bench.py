@@ -503,6 +503,13 @@ def cpu_baseline(inputs, workload):
     oracle.prefill(c["q"], c["k"], c["v"], g.astype(np.float32), beta.astype(np.float32),
                    c["cu"], workload["K"] ** -0.5, c["h0"], nthreads=nthreads)
     dt = time.time() - t0
+    # one thread on one head of the same batch: the per-core rate
+    sub = lambda x: np.ascontiguousarray(x[:, :1])
+    g1, b1 = sub(g).astype(np.float32), sub(beta).astype(np.float32)
+    t1 = time.time()
+    oracle.prefill(sub(c["q"]), sub(c["k"]), sub(c["v"]), g1, b1, c["cu"], workload["K"] ** -0.5,
+                   np.ascontiguousarray(c["h0"][:, :1]), nthreads=1)
+    dt1 = time.time() - t1
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -514,7 +521,10 @@ def cpu_baseline(inputs, workload):
         pass
     return dict(value=c["T"] / dt, unit="tokens/s", cores=nthreads, kind="oracle",
                 sample=f"whole varlen prefill batch ({c['T']} tokens x {workload['H']} heads, "
-                       f"gate + token-serial fp64 recurrence), {dt:.1f} s wall, CPU: {cpu}")
+                       f"gate + token-serial fp64 recurrence), {dt:.1f} s wall, CPU: {cpu}",
+                single_thread={"value": c["T"] / (dt1 * workload["H"]), "unit": "tokens/s",
+                               "sample": f"one head of the same batch on one thread, "
+                                         f"{dt1:.2f} s, scaled to {workload['H']} heads"})
 
 
 def main():
