@@ -74,6 +74,18 @@ def _time(fn, steps: int, warmup: int, settle_s: float | None = None) -> float:
 _FLUSH = None
 
 
+def _fresh_memory():
+    """Returns torch's cached device blocks to the driver before a workload
+    allocates its own buffers, so that each workload's buffers are fresh
+    allocations.  Without it, a buffered-decode run that followed the other
+    workloads in one process, on a GPU that other processes had just used,
+    was measured 7-8x slower (0.84-0.90 ms against 0.112 ms in every other
+    arrangement) with unchanged kernels: the timing of its scattered
+    per-slot reads depended on where the allocation history put them."""
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def _time_flushed(fn, reps: int = 20) -> float:
     """Median milliseconds of single calls of fn, each timed alone between
     HIP events after a write and then a read of a 512 MiB scratch buffer
@@ -617,6 +629,7 @@ def main():
                                      if (r := measured_counters(n)) else None)
                                  for n in ("intra_kernel", "state_kernel")}},
     }
+    _fresh_memory()
     d = bench_decode(args.steps, args.warmup)
     line["decode"] = {"workload": "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",
                       "timing": "median of single calls, each after a 512 MiB write and read "
@@ -627,11 +640,13 @@ def main():
                       "frac_of_hbm_peak": d["gbs_flushed"] / HBM_PEAK_GBS,
                       "back_to_back": {"ms": d["ms"], "tokens_per_s": d["tokens_per_s"],
                                        "total_gbs": d["gbs"]}}
+    _fresh_memory()
     dl = bench_decode_layer(args.steps, args.warmup)
     line["decode"]["with_layer_options"] = {
         "what": "raw gate in the kernel, q/k L2 norm, gated RMSNorm of o (kda_recurrent_decode_ex)",
         "ms": dl["ms"], "tokens_per_s": dl["tokens_per_s"], "total_gbs": dl["gbs"],
         "frac_of_hbm_peak": dl["gbs"] / HBM_PEAK_GBS}
+    _fresh_memory()
     rp = bench_replay(args.steps, args.warmup)
     line["replay_decode"] = {"workload": "decode_256 with a 16-entry ring per slot, cursors "
                                          "staggered over the rows (kda_replay_decode)",
@@ -641,6 +656,7 @@ def main():
                              "mean_ring_entries": rp["mean_ring_entries"],
                              "flush_frac": rp["flush_frac"],
                              "speedup_vs_decode": d["ms"] / rp["ms"]}
+    _fresh_memory()
     vr = bench_verify(args.steps, args.warmup)
     line["verify"] = {"workload": "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool",
                       "timing": "median of single calls, each after a 512 MiB write and read "
@@ -652,12 +668,14 @@ def main():
                       "back_to_back": {"ms": vr["ms"], "tokens_per_s": vr["tokens_per_s"],
                                        "total_gbs": vr["gbs"]}}
     if not args.no_long:
+        _fresh_memory()
         lg = bench_long(args.steps, args.warmup)
         line["long"] = {"workload": "long_prefill_65536: 16 carried 4096-token segments "
                                     "and one full run",
                         "tokens_per_s_segmented": lg["tokens_per_s_segmented"],
                         "tokens_per_s_full": lg["tokens_per_s_full"],
                         "ms_segmented": lg["ms_segmented"], "ms_full": lg["ms_full"]}
+    _fresh_memory()
     cl = measure_ceilings()
     line["measured_ceilings"] = cl
     # each path against the measured stream of its access pattern: the decode
