@@ -455,7 +455,10 @@ __device__ __forceinline__ void butterfly_step(float (&v)[16], int upper) {
 // LDS use (bf16 io, C = 64, D = 128: 80 KB, two workgroups per CU): see
 // IntraSmem.  Every input is staged once; the work units read their rows
 // from LDS into registers and take reference rows by lane broadcast.
-template <typename IO, int D, int C>
+// GATED: the instance that applies the gate to raw inputs (gate_mode 1 or
+// 2); the other one is compiled without the gate code, and the two show up
+// as separate kernels in a profile.
+template <typename IO, int D, int C, bool GATED>
 __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
@@ -522,6 +525,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     return buffer_rsrc(static_cast<const char*>(base) + ((size_t)ce.start * HK + hk) * D * esz,
                        (uint32_t)L * (uint32_t)(HK * D * esz));
   };
+  if (!GATED) gate_mode = 0;
   // gate_mode 0: g and beta are given.  1 (softplus gate) and 2 (safe gate):
   // g and beta hold the raw inputs a and b, activated here with the gate
   // kernel's own functions (the same values it would have written); beta is
@@ -1643,12 +1647,14 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
                      C, ws.ncb, table, off, order);
   if ((e = mark(1)) != hipSuccess) return e;
-  if (a.T > 0)
-    hipLaunchKernelGGL((intra_kernel<IO, D, C>), dim3((unsigned)(ws.ncb * a.H)),
+  if (a.T > 0) {
+    auto intra = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
+    hipLaunchKernelGGL(intra, dim3((unsigned)(ws.ncb * a.H)),
                        dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
                        (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs, a.gate_mode,
                        a.A_log, a.dt_bias, a.lower_bound, a.qk_heads > 0 ? a.qk_heads : a.H,
                        a.per_head_gate, a.qk_l2norm);
+  }
   if ((e = mark(2)) != hipSuccess) return e;
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
