@@ -444,7 +444,7 @@ def measure_ceilings(nbytes: int = 2 << 30):
     res = torch.empty(4 * blocks, dtype=torch.float32, device="cuda")
     for shape in ("32x32x16", "16x16x32"):
         ms = _event_ms(lambda: ceilings.mfma_bf16(shape, blocks, iters, res))
-        out[f"bf16_mfma_{shape}_tflops"] = ceilings.mfma_flops(blocks, iters) / (ms * 1e-3) / 1e12
+        out[f"bf16_mfma_{shape}_tflops"] = ceilings.mfma_flops(shape, blocks, iters) / (ms * 1e-3) / 1e12
     out["what"] = (f"libkda_probe kernels timed in this run: HBM streams over {nbytes >> 30} GiB "
                    "per buffer (copy and rmw count read + write bytes; one 1024-thread "
                    "workgroup per 16 KiB, non-temporal); 512 workgroups of independent bf16 "

@@ -34,8 +34,11 @@
  *     pointers, alignment, sizes and supported shapes; on any error nothing
  *     is enqueued.  Values that live in device memory (cu_seqlens, slot
  *     indices, ring cursors) are the caller's contract and are not read by
- *     the host.  The kernels still keep every access in bounds: cu_seqlens
- *     are clamped into [0, T], and a live slot index at or past n_slots (or
+ *     the host.  The kernels still keep every access in bounds whatever
+ *     those arrays hold.  Sequence ranges are made disjoint: with c'_m =
+ *     cu_seqlens[m] clamped into [0, T], sequence n covers tokens
+ *     max(c'_0 .. c'_n) .. max(c'_0 .. c'_{n+1}) - 1 (for a valid array,
+ *     exactly cu[n] .. cu[n+1]-1).  A live slot index at or past n_slots (or
  *     a ring cursor outside the ring) gives o = NaN for that row and touches
  *     no state.
  *   - Debug checks: when the environment variable KDA_CHECK is "1" (read at
@@ -44,7 +47,11 @@
  *     enqueued, unless cu_seqlens starts at 0, ends at T and never
  *     decreases; every live slot is below n_slots and appears once; and every
  *     ring cursor lies in [0, ring_len).
- *   - Supported head sizes: K, V in {16, 32, 64, 128}.
+ *   - Supported head sizes: K, V in {16, 32, 64, 128}.  The prefill entry
+ *     points also require K == V (the head layout of the pages' models,
+ *     where the q/k head size equals the value head size); they return
+ *     KDA_ERR_UNSUPPORTED otherwise.  Decode, verify and the buffered decode
+ *     take any K, V of the set.
  */
 #ifndef KDA_H_
 #define KDA_H_
@@ -91,15 +98,20 @@ kda_status kda_gate_prep(const float* a, const float* b, const float* A_log,
 /*
  * Bytes of device workspace kda_chunk_prefill needs for a packed batch of
  * T tokens in N sequences (an upper bound that holds for every split of T
- * into N lengths).  Returns 0 for unsupported arguments.
+ * into N lengths), written to *bytes.  Returns KDA_ERR_INVALID_ARGUMENT for
+ * T < 0, N < 1, H < 1 or a NULL `bytes`, and KDA_ERR_UNSUPPORTED for a shape
+ * the prefill does not build (K, V outside {16, 32, 64, 128}, K != V, chunk
+ * outside {16, 32, 64}); *bytes is then left untouched.
  */
-size_t kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
-                                        int32_t K, int32_t V, int32_t chunk);
+kda_status kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
+                                            int32_t K, int32_t V, int32_t chunk,
+                                            size_t* bytes);
 
 /*
  * Chunkwise varlen prefill (tutorial, section "两种计算形态"; the WY/UT form
  * of the unrolled delta rule, section "矩阵（并行）形式").
- *   q, k    [T, H, K] io dtype;  v [T, H, V] io dtype
+ *   q, k    [T, H, K] io dtype;  v [T, H, V] io dtype; K == V
+ *     (KDA_ERR_UNSUPPORTED otherwise)
  *   g       [T, H, K] fp32 activated log decay;  beta [T, H] fp32
  *   cu_seqlens [N + 1] int32 (device): sequence n owns tokens
  *     cu[n] .. cu[n+1]-1; must satisfy cu[0] = 0 <= cu[1] <= ... <= cu[N] = T.
@@ -218,27 +230,6 @@ kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
                                 float scale, const float* h0, float* ht, void* o,
                                 void* workspace, size_t workspace_bytes,
                                 const kda_prefill_opts* opts, void* stream);
-
-/*
- * kda_chunk_prefill_gated with kernel timing marks, for benchmarks and
- * profilers.  Same arguments, work and results as kda_chunk_prefill_gated;
- * in addition it records four caller-created HIP events (hipEvent_t passed
- * as void*) on `stream`: marks[0] before the chunk-table kernel, marks[1]
- * before the intra-chunk kernel, marks[2] before the inter-chunk state kernel
- * and marks[3] after it, so that the elapsed time between consecutive marks
- * is one kernel's duration.  A NULL `marks` or a NULL entry returns
- * KDA_ERR_INVALID_ARGUMENT with nothing enqueued; a failed event record
- * returns KDA_ERR_LAUNCH.
- */
-kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
-                                    const void* v, const float* a, const float* b,
-                                    const float* A_log, const float* dt_bias,
-                                    float lower_bound, const int32_t* cu_seqlens,
-                                    int32_t N, int64_t T, int32_t H, int32_t K,
-                                    int32_t V, int32_t chunk, float scale,
-                                    const float* h0, float* ht, void* o,
-                                    void* workspace, size_t workspace_bytes,
-                                    void* stream, void* const* marks);
 
 /*
  * Single-token decode on a slot-indexed state pool, updated in place

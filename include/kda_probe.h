@@ -38,13 +38,14 @@ extern "C" {
 int kda_probe_hbm(int mode, const void* src, void* dst, size_t bytes, void* stream);
 
 /* Dense bf16 matrix-core loop: `blocks` workgroups of 256 threads (four
- * waves), each wave issuing `iters` rounds of independent products:
- *   shape 0: four v_mfma_f32_32x32x16_bf16 (32768 flops each) per round;
- *   shape 1: eight v_mfma_f32_16x16x32_bf16 (16384 flops each) per round.
- * Either way a round is 131072 flops per wave, so the total work is
- * blocks * 4 * iters * 131072 flops.  One fp32 per wave (the sum over its
- * lanes of every accumulator entry) goes to out[0 .. 4 * blocks - 1], so that
- * no product is dead code.  blocks in [1, 65536], iters in [1, 1 << 24]. */
+ * waves), each wave issuing `iters` rounds of eight independent products:
+ *   shape 0: eight v_mfma_f32_32x32x16_bf16 (32768 flops each) per round,
+ *            262144 flops per wave and round;
+ *   shape 1: eight v_mfma_f32_16x16x32_bf16 (16384 flops each) per round,
+ *            131072 flops per wave and round.
+ * The total work is blocks * 4 * iters times that.  One fp32 per wave (the
+ * sum over its lanes of every accumulator entry) goes to out[0 .. 4 * blocks
+ * - 1], so that no product is dead code.  blocks in [1, 65536], iters in [1, 1 << 24]. */
 int kda_probe_mfma_bf16(int shape, int32_t blocks, int32_t iters, float* out, void* stream);
 
 #ifdef __cplusplus

@@ -64,8 +64,9 @@ def lib() -> ctypes.CDLL:
     L.kda_status_string.restype = ctypes.c_char_p
     L.kda_gate_prep.argtypes = [vp, vp, vp, vp, i64, i32, i32, f32, vp, vp, vp]
     L.kda_gate_prep.restype = ctypes.c_int
-    L.kda_chunk_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32]
-    L.kda_chunk_prefill_workspace_size.restype = sz
+    L.kda_chunk_prefill_workspace_size.argtypes = [i64, i32, i32, i32, i32, i32,
+                                                   ctypes.POINTER(sz)]
+    L.kda_chunk_prefill_workspace_size.restype = ctypes.c_int
     L.kda_chunk_prefill.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, vp, i32, i64,
                                     i32, i32, i32, i32, f32, vp, vp, vp, vp, sz, vp]
     L.kda_chunk_prefill.restype = ctypes.c_int
@@ -103,6 +104,7 @@ def lib() -> ctypes.CDLL:
     return L
 
 
+# every entry point declared in include/kda.h and include/kda_profile.h
 EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_size",
             "kda_chunk_prefill", "kda_chunk_prefill_marked", "kda_chunk_prefill_gated",
             "kda_chunk_prefill_snapshots",
@@ -168,7 +170,12 @@ def kda_gate_prep(a, b, A_log, dt_bias=None, lower_bound: float = 0.0,
 
 def kda_chunk_prefill_workspace_size(T: int, N: int, H: int, K: int, V: int,
                                      chunk: int = 64) -> int:
-    return int(lib().kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk))
+    """Bytes of workspace kda_chunk_prefill needs (raises KdaError for a
+    shape the prefill does not build)."""
+    n = ctypes.c_size_t(0)
+    _check("kda_chunk_prefill_workspace_size",
+           lib().kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk, ctypes.byref(n)))
+    return int(n.value)
 
 
 def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,
@@ -480,16 +487,10 @@ def kda_verify_ex(q, k, v, g, beta, scale: float, state_pool, slot_idx, *, raw_g
     return o, inter_states
 
 
-def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate=None,
-                         per_head_gate=False, h0=None, output_final_state: bool = True,
-                         chunk: int = 64, o=None, ht=None, snapshots=None,
-                         snapshot_interval: int = 0, qk_l2norm: bool = False,
-                         workspace=None):
-    """Prefill with model-layer options: q, k [T,HK,K]; v [T,H,V]; g [T,H,K]
-    (or [T,H] with per_head_gate), raw a when ``raw_gate`` = (A_log,
-    dt_bias, lower_bound) is given (then beta holds the raw b); snapshots as
-    in kda_chunk_prefill_snapshots; ``qk_l2norm``: q and k L2-normalised in
-    the kernel.  Returns (o, ht)."""
+def _prefill_ex_args(q, k, v, g, beta, cu_seqlens, raw_gate, per_head_gate, h0, ht, o,
+                     snapshots, snapshot_interval, qk_l2norm):
+    """Checks the tensors of a prefill with options; returns (PrefillOpts,
+    T, N, H, K, V, io)."""
     T, HK, K = q.shape
     H, V = v.shape[1], v.shape[2]
     dev = q.device
@@ -502,11 +503,8 @@ def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     if h0 is not None:
         _need(h0, "h0", torch.float32, (N, H, K, V), dev)
-    if ht is None and output_final_state:
-        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, (N, H, K, V), dev)
-    o = torch.empty((T, H, V), dtype=q.dtype, device=dev) if o is None else o
     _need(o, "o", q.dtype, (T, H, V), dev)
     op = PrefillOpts()
     if raw_gate is not None:
@@ -526,6 +524,27 @@ def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate
         op.snapshots = snapshots.data_ptr()
         op.snapshot_rows = snapshots.shape[0]
         op.snapshot_interval = int(snapshot_interval)
+    return op, T, N, H, K, V, io
+
+
+def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate=None,
+                         per_head_gate=False, h0=None, output_final_state: bool = True,
+                         chunk: int = 64, o=None, ht=None, snapshots=None,
+                         snapshot_interval: int = 0, qk_l2norm: bool = False,
+                         workspace=None):
+    """Prefill with model-layer options: q, k [T,HK,K]; v [T,H,V]; g [T,H,K]
+    (or [T,H] with per_head_gate), raw a when ``raw_gate`` = (A_log,
+    dt_bias, lower_bound) is given (then beta holds the raw b); snapshots as
+    in kda_chunk_prefill_snapshots; ``qk_l2norm``: q and k L2-normalised in
+    the kernel.  Returns (o, ht)."""
+    T, H, V = q.shape[0], v.shape[1], v.shape[2]
+    K, N, dev = q.shape[2], cu_seqlens.shape[0] - 1, q.device
+    if ht is None and output_final_state:
+        ht = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    o = torch.empty((T, H, V), dtype=q.dtype, device=dev) if o is None else o
+    op, T, N, H, K, V, io = _prefill_ex_args(q, k, v, g, beta, cu_seqlens, raw_gate,
+                                             per_head_gate, h0, ht, o, snapshots,
+                                             snapshot_interval, qk_l2norm)
     need = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

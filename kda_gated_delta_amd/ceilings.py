@@ -74,7 +74,9 @@ def mfma_bf16(shape: str, blocks: int, iters: int, out) -> None:
         raise RuntimeError(f"kda_probe_mfma_bf16 failed with status {st}")
 
 
-def mfma_flops(blocks: int, iters: int) -> int:
-    """Flops of one kda_probe_mfma_bf16 launch (either shape): four waves per
-    workgroup, 131072 flops per wave per round."""
-    return blocks * 4 * iters * 131072
+def mfma_flops(shape: str, blocks: int, iters: int) -> int:
+    """Flops of one kda_probe_mfma_bf16 launch: four waves per workgroup,
+    eight products per wave and round (32x32x16: 32768 flops each,
+    16x16x32: 16384)."""
+    per = 32768 if MFMA_SHAPES[shape] == 0 else 16384
+    return blocks * 4 * iters * 8 * per

@@ -3,6 +3,7 @@
 // synchronises or keeps state; every launch goes to the caller's stream.
 
 #include "kda.h"
+#include "kda_profile.h"
 
 #include <algorithm>
 #include <cstdlib>
@@ -112,8 +113,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            void* const* marks, int gate_mode = 0,
                            const float* A_log = nullptr, const float* dt_bias = nullptr,
                            float lower_bound = 0.f, float* snaps = nullptr,
-                           int snap_interval = 0, int qk_heads = 0, int per_head_gate = 0,
-                           int qk_l2norm = 0) {
+                           int snap_interval = 0, int64_t snap_rows = 0, int qk_heads = 0,
+                           int per_head_gate = 0, int qk_l2norm = 0) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -135,7 +136,7 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
                      gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval,
-                     qk_heads, per_head_gate, qk_l2norm};
+                     snap_rows, qk_heads, per_head_gate, qk_l2norm};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -168,11 +169,14 @@ kda_status kda_gate_prep(const float* a, const float* b, const float* A_log,
   return launch_status(kda::run_gate(p, (hipStream_t)stream));
 }
 
-size_t kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
-                                        int32_t K, int32_t V, int32_t chunk) {
-  if (T < 0 || N < 1 || H < 1 || !head_dim_ok(K) || K != V) return 0;
-  if (chunk != 16 && chunk != 32 && chunk != 64) return 0;
-  return kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
+kda_status kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
+                                            int32_t K, int32_t V, int32_t chunk,
+                                            size_t* bytes) {
+  if (T < 0 || N < 1 || H < 1 || !bytes) return KDA_ERR_INVALID_ARGUMENT;
+  if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
+  if (chunk != 16 && chunk != 32 && chunk != 64) return KDA_ERR_UNSUPPORTED;
+  *bytes = kda::prefill_workspace_bytes(T, N, H, K, V, chunk);
+  return KDA_OK;
 }
 
 kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
@@ -200,7 +204,7 @@ kda_status kda_chunk_prefill_snapshots(kda_dtype io, const void* q, const void* 
     return KDA_ERR_INVALID_ARGUMENT;
   return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
                          o, workspace, workspace_bytes, stream, nullptr, 0, nullptr, nullptr,
-                         0.f, snapshots, snapshot_interval);
+                         0.f, snapshots, snapshot_interval, snapshot_rows);
 }
 
 kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
@@ -229,7 +233,8 @@ kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
                          o, workspace, workspace_bytes, stream, nullptr, opts->gate_mode,
                          opts->A_log, opts->dt_bias,
                          opts->gate_mode == 2 ? opts->lower_bound : 0.f, opts->snapshots,
-                         interval, opts->qk_heads, opts->per_head_gate != 0,
+                         interval, opts->snapshots ? opts->snapshot_rows : 0, opts->qk_heads,
+                         opts->per_head_gate != 0,
                          opts->qk_l2norm != 0);
 }
 

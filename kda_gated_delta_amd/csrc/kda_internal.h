@@ -89,6 +89,7 @@ struct PrefillArgs {
   // sequence after every snap_interval tokens (nullptr for none).
   float* snaps;
   int snap_interval;
+  int64_t snap_rows;  // rows of snaps; rows at or past it are never written
   int qk_heads;       // heads of q and k (0: H)
   int per_head_gate;  // g (or a) is [T, H] and dt_bias [H]
   int qk_l2norm;      // q, k L2-normalised in the kernel

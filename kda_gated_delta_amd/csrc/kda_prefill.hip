@@ -184,9 +184,16 @@ struct Geom {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-// Header of the workspace: chunk table [NCB] and per-sequence chunk offsets.
+// Per-sequence plan entry: the clamped token range lo .. hi-1, the first
+// chunk of the sequence in the chunk table, and the first snapshot row.
+struct SeqInfo {
+  int lo, hi, chunk_first, snap_base;
+};
+
+// Header of the workspace: chunk table [NCB], per-sequence entries [N] and
+// the state pass's sequence order [N].
 struct WsLayout {
-  size_t table_off, off_off, order_off, rec_off;
+  size_t table_off, seq_off, order_off, rec_off;
   int64_t ncb;
 };
 
@@ -194,8 +201,8 @@ WsLayout ws_layout(int64_t T, int N, int C) {
   WsLayout w;
   w.ncb = (T + C - 1) / C + N;
   w.table_off = 0;
-  w.off_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
-  w.order_off = w.off_off + round256((size_t)(N + 1) * sizeof(int));
+  w.seq_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
+  w.order_off = w.seq_off + round256((size_t)N * sizeof(SeqInfo));
   w.rec_off = w.order_off + round256((size_t)N * sizeof(int));
   return w;
 }
@@ -213,104 +220,84 @@ size_t rec_bytes(int D, int C) {
 
 // ------------------------------------------------------------------- plan
 
-// Token range lo .. hi-1 of sequence n, with the bounds clamped to
-// 0 <= lo <= hi <= T (the plan and the snapshot rows both use this).
-__device__ __forceinline__ void seq_bounds(const int32_t* __restrict__ cu, int n, int64_t T,
-                                           int& lo, int& hi) {
-  const int64_t a = cu[n], b = cu[n + 1];
-  lo = (int)(a < 0 ? 0 : (a > T ? T : a));
-  hi = (int)(b < lo ? lo : (b > T ? T : b));
+// Inclusive scan over the NTHREADS threads of a workgroup (Hillis-Steele in
+// LDS); `op` is max or +.  Every thread must call it.
+template <typename Op>
+__device__ __forceinline__ int block_scan(int x, int* scratch, Op op) {
+  const int t = threadIdx.x;
+  scratch[t] = x;
+  __syncthreads();
+  for (int s = 1; s < NTHREADS; s <<= 1) {
+    const int y = t >= s ? scratch[t - s] : x;
+    __syncthreads();
+    if (t >= s) x = op(x, y);
+    scratch[t] = x;
+    __syncthreads();
+  }
+  return x;
 }
 
-// Chunk table of the packed batch: sequence n owns chunks
-// off[n] .. off[n+1]-1; entries past the last chunk get len = 0.  Sequence
-// bounds are clamped to 0 <= lo <= hi <= T.
+// Chunk table of the packed batch.  Sequence bounds are made disjoint and
+// monotone whatever cu_seqlens holds: with c'_m = min(max(cu[m], 0), T) and
+// p_n = max(c'_0 .. c'_n), sequence n owns tokens p_n .. p_{n+1}-1.  For a
+// valid cu_seqlens (cu[0] = 0 <= cu[1] <= .. <= cu[N] = T) that is exactly
+// cu[n] .. cu[n+1]-1; for any other array the ranges still partition a part
+// of [0, T), so the chunks never outnumber the workspace's ceil(T/C) + N.
+// Sequence n owns chunks seqs[n].chunk_first .. + ceil((hi - lo) / C) - 1;
+// table entries past the last chunk get len = 0.  With snapshots, sequence n
+// owns the rows from seqs[n].snap_base on, floor((hi - lo) / snap_interval)
+// of them.
 __global__ __launch_bounds__(NTHREADS) void plan_kernel(
-    const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb,
-    ChunkEntry* __restrict__ table, int* __restrict__ off, int* __restrict__ order) {
-  __shared__ int scan[NTHREADS];
-  __shared__ int carry;
+    const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb, int snap_interval,
+    ChunkEntry* __restrict__ table, SeqInfo* __restrict__ seqs, int* __restrict__ order) {
+  __shared__ int scratch[NTHREADS];
+  __shared__ int carry_max, carry_chunks, carry_snaps;
   __shared__ int bcount[33], bbase[33];
-  __shared__ int s_lo[NTHREADS], s_hi[NTHREADS];
   const int t = threadIdx.x;
-  // Clamped bounds and chunk count of sequence n.  A batch of at most
-  // NTHREADS sequences reads cu_seqlens once (thread t keeps sequence t);
-  // larger ones re-read it in each pass.
-  auto bounds = [&](int n, int& lo, int& hi) { seq_bounds(cu, n, T, lo, hi); };
-  const bool small = N <= NTHREADS;
-  int my_lo = 0, my_hi = 0;
-  if (small && t < N) bounds(t, my_lo, my_hi);
-  auto seq = [&](int n, int& lo, int& hi) {
-    if (small) {
-      lo = my_lo;
-      hi = my_hi;
-    } else {
-      bounds(n, lo, hi);
-    }
-  };
+  auto clampT = [&](int64_t x) { return (int)(x < 0 ? 0 : (x > T ? T : x)); };
   auto bucket_of = [](int nch) { return nch <= 0 ? 0 : 32 - __clz(nch); };
-  if (t == 0) carry = 0;
+  auto imax = [](int a, int b) { return a > b ? a : b; };
+  auto iadd = [](int a, int b) { return a + b; };
+  if (t == 0) {
+    carry_max = clampT(cu[0]);
+    carry_chunks = 0;
+    carry_snaps = 0;
+  }
   if (t < 33) bcount[t] = 0;
   __syncthreads();
   for (int base = 0; base < N; base += NTHREADS) {
     const int n = base + t;
-    int lo = 0, hi = 0, nch = 0;
+    const int cm = carry_max, cc = carry_chunks, cs = carry_snaps;
+    // hi of sequence n = p_{n+1}; lo = hi of sequence n-1 (p_n)
+    const int hi = imax(cm, block_scan(n < N ? clampT(cu[n + 1]) : 0, scratch, imax));
+    const int lo = t == 0 ? cm : imax(cm, scratch[t - 1]);
+    const int len = n < N ? hi - lo : 0;
+    const int nch = (len + C - 1) / C;
+    const int nsn = snap_interval > 0 ? len / snap_interval : 0;
+    __syncthreads();
+    const int first = cc + block_scan(nch, scratch, iadd) - nch;
+    __syncthreads();
+    const int sfirst = cs + block_scan(nsn, scratch, iadd) - nsn;
     if (n < N) {
-      seq(n, lo, hi);
-      nch = (hi - lo + C - 1) / C;
+      SeqInfo e;
+      e.lo = lo;
+      e.hi = hi;
+      e.chunk_first = first;
+      e.snap_base = sfirst;
+      seqs[n] = e;
       atomicAdd(&bcount[bucket_of(nch)], 1);
     }
-    scan[t] = nch;
     __syncthreads();
-    for (int s = 1; s < NTHREADS; s <<= 1) {  // inclusive Hillis-Steele scan
-      const int x = t >= s ? scan[t - s] : 0;
-      __syncthreads();
-      scan[t] += x;
-      __syncthreads();
+    if (t == NTHREADS - 1) {
+      carry_max = hi > cm ? hi : cm;
+      carry_chunks = first + nch;
+      carry_snaps = sfirst + nsn;
     }
-    const int first = carry + scan[t] - nch;
-    if (n < N) {
-      off[n] = first;
-      if (!small) {
-        for (int j = 0; j < nch && first + j < ncb; ++j) {
-          ChunkEntry e;
-          e.seq = n;
-          e.start = lo + j * C;
-          e.len = (hi - e.start < C) ? hi - e.start : C;
-          e.pad = 0;
-          table[first + j] = e;
-        }
-      }
-    }
-    if (small) {
-      // all threads fill the table: entry i belongs to the sequence whose
-      // chunk range holds it (a search over the inclusive scan in LDS)
-      if (n < N) {
-        s_lo[t] = lo;
-        s_hi[t] = hi;
-      }
-      __syncthreads();
-      const int total = scan[N - 1];
-      for (int i = t; i < total && i < ncb; i += NTHREADS) {
-        int a = 0, b = N - 1;  // first m with scan[m] > i
-        while (a < b) {
-          const int m = (a + b) >> 1;
-          if (scan[m] > i) b = m; else a = m + 1;
-        }
-        const int first_a = scan[a] - ((s_hi[a] - s_lo[a] + C - 1) / C);
-        ChunkEntry e;
-        e.seq = a;
-        e.start = s_lo[a] + (i - first_a) * C;
-        e.len = (s_hi[a] - e.start < C) ? s_hi[a] - e.start : C;
-        e.pad = 0;
-        table[i] = e;
-      }
-    }
-    __syncthreads();
-    if (t == NTHREADS - 1) carry += scan[t];
     __syncthreads();
   }
-  if (t == 0) off[N] = carry;
+  const int total = carry_chunks;  // <= ncb (see above)
+  __threadfence_block();
+  __syncthreads();
   // Longest sequences first: order[] lists the sequences by descending
   // power-of-two bucket of their chunk count, so the state pass starts the
   // longest serial chains first.
@@ -323,16 +310,29 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   }
   __syncthreads();
   for (int n = t; n < N; n += NTHREADS) {
-    int lo, hi;
-    seq(n, lo, hi);
-    order[atomicAdd(&bbase[bucket_of((hi - lo + C - 1) / C)], 1)] = n;
+    const SeqInfo e = seqs[n];
+    order[atomicAdd(&bbase[bucket_of((e.hi - e.lo + C - 1) / C)], 1)] = n;
   }
-  for (int64_t i = carry + t; i < ncb; i += NTHREADS) {
+  // entry i belongs to the last sequence whose first chunk is <= i (a
+  // binary search over the monotone chunk_first; empty sequences share
+  // their successor's first chunk and lose the search)
+  for (int64_t i = t; i < ncb; i += NTHREADS) {
     ChunkEntry e;
     e.seq = 0;
     e.start = 0;
     e.len = 0;
     e.pad = 0;
+    if (i < total) {
+      int a = 0, b = N - 1;  // last m with chunk_first <= i
+      while (a < b) {
+        const int m = (a + b + 1) >> 1;
+        if (seqs[m].chunk_first <= i) a = m; else b = m - 1;
+      }
+      const SeqInfo s = seqs[a];
+      e.seq = a;
+      e.start = s.lo + ((int)i - s.chunk_first) * C;
+      e.len = (s.hi - e.start < C) ? s.hi - e.start : C;
+    }
     table[i] = e;
   }
 }
@@ -1279,10 +1279,10 @@ struct StateOps {
 
 template <typename IO, int D, int C, int VT>
 __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
-    const ChunkEntry* __restrict__ table, const int* __restrict__ off,
+    const ChunkEntry* __restrict__ table, const SeqInfo* __restrict__ seqs,
     const int* __restrict__ order, const char* __restrict__ recs, int ncb, int N, int H,
     const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o,
-    const int32_t* __restrict__ cu, int64_t T, float* __restrict__ snaps, int snap_interval) {
+    float* __restrict__ snaps, int64_t snap_rows, int snap_interval) {
   typedef Geom<D, C> Gm;
   typedef StateSmem<IO, D, C, VT> Sm;
   typedef StateOps<D, C, VT> Ops;
@@ -1334,33 +1334,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     }
   }
 
-  const int c_first = __builtin_amdgcn_readfirstlane(off[n]);
-  const int c_last = __builtin_amdgcn_readfirstlane(off[n + 1]);
-  // token range of the sequence; chunk c covers tokens from seq_start +
-  // (c - c_first) C, at most C of them, up to seq_end
-  int seq_start = 0, seq_end = 0;
-  if (c_first < c_last) {
-    seq_start = __builtin_amdgcn_readfirstlane(table[c_first].start);
-    seq_end = __builtin_amdgcn_readfirstlane(table[c_last - 1].start + table[c_last - 1].len);
-  }
-  // Snapshot rows of this sequence follow those of sequences 0 .. n-1:
-  // sum over them of floor(length / snap_interval).
-  int snap_base = 0;
-  if (snaps != nullptr) {
-    __shared__ int s_snap[NTHREADS / 64];
-    int acc = 0;
-    for (int i = tid; i < n; i += NTHREADS) {
-      int lo, hi;
-      seq_bounds(cu, i, T, lo, hi);
-      acc += (hi - lo) / snap_interval;
-    }
-    for (int x = 1; x < 64; x <<= 1) acc += __shfl_xor(acc, x, 64);
-    if (l == 0) s_snap[w] = acc;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < NTHREADS / 64; ++i) snap_base += s_snap[i];
-    snap_base = __builtin_amdgcn_readfirstlane(snap_base);
-  }
+  // the sequence's chunks and tokens, from the plan (disjoint clamped ranges,
+  // so c_last never passes the workspace's chunk count)
+  const SeqInfo si = seqs[n];
+  const int seq_start = __builtin_amdgcn_readfirstlane(si.lo);
+  const int seq_end = __builtin_amdgcn_readfirstlane(si.hi);
+  const int c_first = __builtin_amdgcn_readfirstlane(si.chunk_first);
+  const int c_last = min(ncb, c_first + (seq_end - seq_start + C - 1) / C);
+  // snapshot rows of this sequence follow those of sequences 0 .. n-1
+  const int snap_base = __builtin_amdgcn_readfirstlane(si.snap_base);
   // Every operand of a chunk is loaded unconditionally (including Aq tiles
   // above the diagonal, which are never multiplied), so the loads form one
   // straight block.
@@ -1575,8 +1557,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     // ends a whole multiple of snap_interval tokens into the sequence
     if (snaps != nullptr) {
       const int end_tok = (ch - c_first + 1) * C;
-      if (end_tok <= seq_end - seq_start && end_tok % snap_interval == 0) {
-        float* P = snaps + ((int64_t)(snap_base + end_tok / snap_interval - 1) * H + h) * D * D;
+      const int64_t row = (int64_t)snap_base + end_tok / snap_interval - 1;
+      if (end_tok <= seq_end - seq_start && end_tok % snap_interval == 0 && row < snap_rows) {
+        float* P = snaps + (row * H + h) * D * D;
 #pragma unroll
         for (int i = 0; i < MS; ++i) {
           const int ms = w + 4 * i;
@@ -1636,7 +1619,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const WsLayout ws = ws_layout(a.T, a.N, C);
   char* base = reinterpret_cast<char*>(a.ws);
   ChunkEntry* table = reinterpret_cast<ChunkEntry*>(base + ws.table_off);
-  int* off = reinterpret_cast<int*>(base + ws.off_off);
+  SeqInfo* seqs = reinterpret_cast<SeqInfo*>(base + ws.seq_off);
   int* order = reinterpret_cast<int*>(base + ws.order_off);
   char* recs = base + ws.rec_off;
   auto mark = [&](int i) -> hipError_t {
@@ -1645,7 +1628,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
-                     C, ws.ncb, table, off, order);
+                     C, ws.ncb, a.snaps != nullptr ? a.snap_interval : 0, table, seqs, order);
   if ((e = mark(1)) != hipSuccess) return e;
   if (a.T > 0) {
     auto intra = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
@@ -1659,8 +1642,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const int units = a.N * a.H;
   const int groups = (units + 7) / 8;
   hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
-                     dim3(NTHREADS), 0, st, table, off, order, recs, (int)ws.ncb, a.N, a.H,
-                     a.h0, a.ht, (IO*)a.o, a.cu_seqlens, a.T, a.snaps, a.snap_interval);
+                     dim3(NTHREADS), 0, st, table, seqs, order, recs, (int)ws.ncb, a.N, a.H,
+                     a.h0, a.ht, (IO*)a.o, a.snaps, a.snap_rows, a.snap_interval);
   if ((e = mark(3)) != hipSuccess) return e;
   (void)sizeof(Gm);
   return hipGetLastError();

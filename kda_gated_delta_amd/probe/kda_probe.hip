@@ -48,7 +48,6 @@ __global__ __launch_bounds__(NT) void stream_kernel(const f32x4* __restrict__ sr
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int CHAINS = 4;  // independent accumulators per wave
 
 // Operands fixed per lane: A and B fragments of 8 bf16 each (lane l, value
 // 0.001 * ((l + j) & 7) and 0.001 * ((3 l + j) & 7) for j = 0..7).
@@ -61,38 +60,42 @@ __device__ __forceinline__ void probe_operands(bf16x8& a, bf16x8& b) {
   }
 }
 
-// Each wave: `iters` rounds of CHAINS independent products of one shape;
-// the accumulators carry the dependence.  One fp32 per wave goes out (the
-// sum over its lanes of all accumulator entries).
+// One MFMA accumulating in place.  Written as inline assembly so that the
+// loop below is nothing but the MFMAs: with the compiler builtins, hipcc
+// moves every accumulator between register files in each iteration of such
+// a loop, and the probe then measures those moves.  Consecutive products
+// write different accumulators (a dependent pair is eight products apart),
+// so no wait states are needed between them.
+#define KDA_MFMA_16(acc) \
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+#define KDA_MFMA_32(acc) \
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
+
+// Each wave: `iters` rounds of eight independent products of one shape; the
+// accumulators carry the dependence.  One fp32 per wave goes out: the sum
+// over its lanes of every accumulator entry.
 template <bool BIG>
 __global__ __launch_bounds__(NTM) void mfma_kernel(int iters, float* __restrict__ out) {
   bf16x8 a, b;
   probe_operands(a, b);
   float s = 0.f;
   if constexpr (BIG) {
-    f32x16 acc[CHAINS];
-#pragma unroll
-    for (int c = 0; c < CHAINS; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
+    f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {}, c4 = {}, c5 = {}, c6 = {}, c7 = {};
     for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      KDA_MFMA_32(c0); KDA_MFMA_32(c1); KDA_MFMA_32(c2); KDA_MFMA_32(c3);
+      KDA_MFMA_32(c4); KDA_MFMA_32(c5); KDA_MFMA_32(c6); KDA_MFMA_32(c7);
     }
+    const f32x16 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
 #pragma unroll
-    for (int c = 0; c < CHAINS; ++c)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s += acc[c][e];
+    for (int e = 0; e < 16; ++e) s += t[e];
   } else {
-    f32x4 acc[2 * CHAINS];
-#pragma unroll
-    for (int c = 0; c < 2 * CHAINS; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 c0 = {}, c1 = {}, c2 = {}, c3 = {}, c4 = {}, c5 = {}, c6 = {}, c7 = {};
     for (int it = 0; it < iters; ++it) {
-#pragma unroll
-      for (int c = 0; c < 2 * CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+      KDA_MFMA_16(c0); KDA_MFMA_16(c1); KDA_MFMA_16(c2); KDA_MFMA_16(c3);
+      KDA_MFMA_16(c4); KDA_MFMA_16(c5); KDA_MFMA_16(c6); KDA_MFMA_16(c7);
     }
-#pragma unroll
-    for (int c = 0; c < 2 * CHAINS; ++c) s += (acc[c][0] + acc[c][1]) + (acc[c][2] + acc[c][3]);
+    const f32x4 t = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+    s = (t[0] + t[1]) + (t[2] + t[3]);
   }
   for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m, 64);
   if ((threadIdx.x & 63) == 0) out[blockIdx.x * (NTM / 64) + (threadIdx.x >> 6)] = s;

@@ -14,15 +14,18 @@ import pytest
 import kda_gated_delta_amd as kda
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kda.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in ("kda.h", "kda_profile.h")]
 
 OK, INVALID, UNSUPPORTED, LAUNCH, WORKSPACE = 0, 1, 2, 3, 4
 
 
 def _declared():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names |= set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -89,8 +92,16 @@ def test_prefill_validation_and_workspace():
     # monotone in T and N
     assert kda.kda_chunk_prefill_workspace_size(7681, 4, 32, 128, 128, 64) >= ws
     assert kda.kda_chunk_prefill_workspace_size(7680, 5, 32, 128, 128, 64) >= ws
-    assert kda.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 16, 48) == 0
-    assert kda.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 32, 16) == 0
+    n = ctypes.c_size_t(12345)
+    assert L.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 16, 48, ctypes.byref(n)) == UNSUPPORTED
+    assert L.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 32, 16, ctypes.byref(n)) == UNSUPPORTED
+    assert L.kda_chunk_prefill_workspace_size(64, 1, 2, 24, 24, 16, ctypes.byref(n)) == UNSUPPORTED
+    assert L.kda_chunk_prefill_workspace_size(-1, 1, 2, 16, 16, 16, ctypes.byref(n)) == INVALID
+    assert L.kda_chunk_prefill_workspace_size(64, 0, 2, 16, 16, 16, ctypes.byref(n)) == INVALID
+    assert L.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 16, 16, None) == INVALID
+    assert n.value == 12345  # untouched on error
+    with pytest.raises(kda.KdaError):
+        kda.kda_chunk_prefill_workspace_size(64, 1, 2, 16, 32, 16)
 
     def call(**kw):
         return L.kda_chunk_prefill(
@@ -256,3 +267,4 @@ def test_replay_options_validation():
     op = kda.StepOpts()
     op.gate_mode = 1  # no A_log
     assert call(op) == INVALID
+

@@ -249,3 +249,34 @@ def test_gated_prefill_equals_gate_prep_then_prefill(lower_bound, with_bias, D, 
     o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g32, b32, c["cu"], scale, c["h0"])
     assert_io_output(host(o2), o_ref, "bf16", 1)
     assert rel_err_blocks(host(ht2), ht_ref, 2) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cu_bad,T", [([0, 200, 0, 200], 200),
+                                      ([0, 150, 40, 300, 200, 300], 300),
+                                      ([-7, 120, 999, 50, 300], 300)])
+def test_malformed_cu_seqlens_stay_in_bounds(cu_bad, T):
+    """cu_seqlens that decrease or leave [0, T] (no KDA_CHECK): the kernels
+    take the disjoint clamped ranges (tests/test_plan_bounds.py), so the call
+    equals the same call on that clamped array bit for bit, and matches the
+    oracle there; snapshot rows stay within T // interval."""
+    N = len(cu_bad) - 1
+    p = np.maximum.accumulate(np.clip(np.asarray(cu_bad, dtype=np.int64), 0, T))
+    assert p[0] == 0 and p[-1] == T
+    c = kda_synth.prefill_case(list(np.diff(p)), 2, 64, 64, "bf16", seed=N, regime="long",
+                               h0_std=0.1)
+    t, g, beta = _inputs(c)
+    bad = torch.tensor(cu_bad, dtype=torch.int32, device="cuda")
+    outs = []
+    for cu in (bad, t["cu"]):
+        # rows past the batch's total are left untouched: start from zeros
+        snaps = torch.zeros((T // 64, 2, 64, 64), device="cuda")
+        o, ht, snaps = kda.kda_chunk_prefill_snapshots(
+            t["q"], t["k"], t["v"], t["g"], t["beta"], cu, 0.125, 64, h0=t["h0"], chunk=32,
+            snapshots=snaps)
+        outs.append((o, ht, snaps))
+    torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, p, 0.125, c["h0"])
+    assert_io_output(host(outs[1][0]), o_ref, "bf16", 1)
+    assert rel_err_blocks(host(outs[1][1]), ht_ref, 2) <= TOL["bf16"]

@@ -75,7 +75,7 @@ def test_probe_streams_move_every_byte(nbytes):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("shape,rows,chains", [("32x32x16", 32, 4), ("16x16x32", 16, 8)])
+@pytest.mark.parametrize("shape,rows,chains", [("32x32x16", 32, 8), ("16x16x32", 16, 8)])
 def test_probe_mfma_loop_computes_its_products(shape, rows, chains):
     blocks, iters = 3, 5
     out = torch.zeros(4 * blocks, device="cuda")
