@@ -68,7 +68,9 @@ typedef enum {
   KDA_ERR_INVALID_ARGUMENT = 1, /* null pointer, misalignment, bad size   */
   KDA_ERR_UNSUPPORTED = 2,      /* shape or dtype outside the built set   */
   KDA_ERR_LAUNCH = 3,           /* the HIP runtime refused a launch       */
-  KDA_ERR_WORKSPACE = 4         /* workspace missing or too small         */
+  KDA_ERR_WORKSPACE = 4,        /* workspace missing or too small         */
+  KDA_ERR_SCRATCH_LIMIT = 5     /* the call needs more scratch than the
+                                   library's static scratch array holds   */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype; /* dtype of q, k, v, o */
@@ -230,6 +232,33 @@ kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
                                 float scale, const float* h0, float* ht, void* o,
                                 void* workspace, size_t workspace_bytes,
                                 const kda_prefill_opts* opts, void* stream);
+
+/* Bytes of the static scratch array behind kda_chunk_prefill_noalloc. */
+#define KDA_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/*
+ * kda_chunk_prefill_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The workspace is a static device array
+ * of KDA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until
+ * the process ends; this call allocates nothing.  Every other argument, the
+ * results (bit-identical to kda_chunk_prefill_ex with any workspace) and the
+ * errors are those of kda_chunk_prefill_ex, plus:
+ *   KDA_ERR_SCRATCH_LIMIT when kda_chunk_prefill_workspace_size(T, N, H, K,
+ *     V, chunk) exceeds KDA_NOALLOC_SCRATCH_BYTES (nothing is enqueued).  At
+ *     H = 32, K = V = 128, chunk 64 that allows about 3500 tokens in one
+ *     sequence; fewer heads or shorter sequences fit more.
+ *   KDA_ERR_LAUNCH when the array's device address cannot be looked up.
+ * All calls on one GPU share its array: two calls whose work overlaps on
+ * that GPU (on different streams, or from different host threads without
+ * ordering) race on it.  Calls ordered on one stream are safe.
+ */
+kda_status kda_chunk_prefill_noalloc(kda_dtype io, const void* q, const void* k,
+                                     const void* v, const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                     int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                     float scale, const float* h0, float* ht, void* o,
+                                     const kda_prefill_opts* opts, void* stream);
 
 /*
  * Single-token decode on a slot-indexed state pool, updated in place

@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
     L.kda_chunk_prefill_ex.argtypes = L.kda_chunk_prefill.argtypes[:-1] + [
         ctypes.POINTER(PrefillOpts), vp]
     L.kda_chunk_prefill_ex.restype = ctypes.c_int
+    L.kda_chunk_prefill_noalloc.argtypes = L.kda_chunk_prefill.argtypes[:-3] + [
+        ctypes.POINTER(PrefillOpts), vp]
+    L.kda_chunk_prefill_noalloc.restype = ctypes.c_int
     L.kda_recurrent_decode_ex.argtypes = L.kda_recurrent_decode.argtypes[:-1] + [
         ctypes.POINTER(StepOpts), vp]
     L.kda_recurrent_decode_ex.restype = ctypes.c_int
@@ -110,7 +113,11 @@ EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_s
             "kda_chunk_prefill_snapshots",
             "kda_recurrent_decode", "kda_verify", "kda_replay_decode",
             "kda_recurrent_decode_ex", "kda_verify_ex", "kda_chunk_prefill_ex",
-            "kda_replay_decode_ex")
+            "kda_replay_decode_ex", "kda_chunk_prefill_noalloc")
+
+# Bytes of the static scratch array behind kda_chunk_prefill_noalloc
+# (KDA_NOALLOC_SCRATCH_BYTES of include/kda.h).
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 def status_string(status: int) -> str:
@@ -552,4 +559,22 @@ def kda_chunk_prefill_ex(q, k, v, g, beta, cu_seqlens, scale: float, *, raw_gate
         io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, K, V,
         chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), _ptr(workspace), workspace.numel(),
         ctypes.byref(op), _stream(dev)))
+    return o, ht
+
+
+def kda_chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, scale: float, o, *, ht=None,
+                              raw_gate=None, per_head_gate=False, h0=None, chunk: int = 64,
+                              snapshots=None, snapshot_interval: int = 0,
+                              qk_l2norm: bool = False):
+    """kda_chunk_prefill_ex on the library's static scratch: allocates
+    nothing.  The caller passes every output: ``o`` [T,H,V] and, to receive
+    the final states, ``ht`` [N,H,K,V] (None: not written).  Raises KdaError
+    with KDA_ERR_SCRATCH_LIMIT when the batch needs more workspace than
+    KDA_NOALLOC_SCRATCH_BYTES.  Returns (o, ht)."""
+    op, T, N, H, K, V, io = _prefill_ex_args(q, k, v, g, beta, cu_seqlens, raw_gate,
+                                             per_head_gate, h0, ht, o, snapshots,
+                                             snapshot_interval, qk_l2norm)
+    _check("kda_chunk_prefill_noalloc", lib().kda_chunk_prefill_noalloc(
+        io, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), N, T, H, K, V,
+        chunk, float(scale), _ptr(h0), _ptr(ht), _ptr(o), ctypes.byref(op), _stream(q.device)))
     return o, ht

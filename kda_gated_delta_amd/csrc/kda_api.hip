@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <mutex>
 #include <vector>
 #include "kda_internal.h"
 
@@ -140,6 +141,39 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------ static scratch
+
+// The prefill workspace of kda_chunk_prefill_noalloc, for callers that cannot
+// allocate: one array per GPU the library runs on, held until the process
+// ends.  In host code `scratch` only names the symbol; its device address on
+// each GPU comes from hipGetSymbolAddress (scratch_on), and only that address
+// is ever passed to a kernel.
+static __device__ __align__(256) char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the GPU that runs `stream` (looked up once
+// per device, with that device current), or nullptr if the lookup fails.
+void* scratch_on(hipStream_t stream) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  hipDevice_t dev = cur;
+  if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (scratch_ptr[dev] == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return nullptr;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -151,6 +185,7 @@ const char* kda_status_string(kda_status s) {
     case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
     case KDA_ERR_LAUNCH: return "KDA_ERR_LAUNCH";
     case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_SCRATCH_LIMIT: return "KDA_ERR_SCRATCH_LIMIT";
   }
   return "KDA_ERR_UNKNOWN";
 }
@@ -388,6 +423,21 @@ kda_status kda_replay_decode_ex(kda_dtype io, const void* q, const void* k,
                     write_pos, force_flush, ring_len, ring_d, ring_k, ring_g, B, H, K, V, o,
                     next_write_pos, op, n_slots};
   return launch_status(kda::run_replay(p, (hipStream_t)stream));
+}
+
+kda_status kda_chunk_prefill_noalloc(kda_dtype io, const void* q, const void* k,
+                                     const void* v, const float* g, const float* beta,
+                                     const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                     int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                     float scale, const float* h0, float* ht, void* o,
+                                     const kda_prefill_opts* opts, void* stream) {
+  size_t need = 0;
+  if (kda_status st = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk, &need)) return st;
+  if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
+  void* ws = scratch_on((hipStream_t)stream);
+  if (ws == nullptr) return KDA_ERR_LAUNCH;
+  return kda_chunk_prefill_ex(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0,
+                              ht, o, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, opts, stream);
 }
 
 }  // extern "C"

@@ -16,7 +16,7 @@ import kda_gated_delta_amd as kda
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = [os.path.join(ROOT, "include", h) for h in ("kda.h", "kda_profile.h")]
 
-OK, INVALID, UNSUPPORTED, LAUNCH, WORKSPACE = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, LAUNCH, WORKSPACE, SCRATCH_LIMIT = 0, 1, 2, 3, 4, 5
 
 
 def _declared():
@@ -42,6 +42,7 @@ def test_status_strings():
     assert kda.status_string(UNSUPPORTED) == "KDA_ERR_UNSUPPORTED"
     assert kda.status_string(LAUNCH) == "KDA_ERR_LAUNCH"
     assert kda.status_string(WORKSPACE) == "KDA_ERR_WORKSPACE"
+    assert kda.status_string(SCRATCH_LIMIT) == "KDA_ERR_SCRATCH_LIMIT"
     assert kda.status_string(99) == "KDA_ERR_UNKNOWN"
 
 
@@ -268,3 +269,21 @@ def test_replay_options_validation():
     op.gate_mode = 1  # no A_log
     assert call(op) == INVALID
 
+
+def test_noalloc_prefill_validation():
+    """kda_chunk_prefill_noalloc refuses on the host: the prefill's own
+    argument errors, and a batch whose workspace exceeds the static scratch
+    (KDA_ERR_SCRATCH_LIMIT), both before any HIP call."""
+    L = kda.lib()
+
+    def call(**kw):
+        return L.kda_chunk_prefill_noalloc(
+            kw.get("io", 1), P, P, P, P, P, P, kw.get("N", 1), kw.get("T", 64), kw.get("H", 2),
+            kw.get("K", 128), kw.get("V", 128), kw.get("chunk", 64), 1.0, None, P, P, None, None)
+    assert call(chunk=48) == UNSUPPORTED
+    assert call(K=64, V=128) == UNSUPPORTED
+    assert call(N=0) == INVALID
+    assert call(T=-1) == INVALID
+    assert call(T=1 << 20, H=32) == SCRATCH_LIMIT
+    ws = kda.kda_chunk_prefill_workspace_size(8192, 1, 32, 128, 128, 64)
+    assert ws > kda.NOALLOC_SCRATCH_BYTES and call(T=8192, H=32) == SCRATCH_LIMIT
