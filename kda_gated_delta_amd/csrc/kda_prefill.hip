@@ -185,25 +185,92 @@ struct Geom {
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
 // Per-sequence plan entry: the clamped token range lo .. hi-1, the first
-// chunk of the sequence in the chunk table, and the first snapshot row.
+// chunk of the sequence in the chunk table, the first snapshot row, and,
+// when the sequence is cut into segments, its first start-state slot and
+// first map slot.
 struct SeqInfo {
-  int lo, hi, chunk_first, snap_base;
+  int lo, hi, chunk_first, snap_base, start_slot, map_slot, pad0, pad1;
 };
 
-// Header of the workspace: chunk table [NCB], per-sequence entries [N] and
-// the state pass's sequence order [N].
+// A work unit of the state pass: the chunks c_begin .. c_end-1 of sequence
+// `seq`, in one of three roles.
+//  - first segment (or the whole sequence): from h0 (or zeros); writes ht
+//    when it is the whole sequence, else its final state into start slot
+//    `slot` (the next segment's start);
+//  - map of a middle segment: the affine map S -> M S + B of its chunks,
+//    computed as the state pass over the K + V columns of [M | B] from
+//    [I | 0] with no read-out, into map slot `slot`;
+//  - later segment: from start slot `slot`; writes ht when it is the last.
+// A chunk is the affine map S -> (Diag(e^{G_C}) - (K e^{G_C-G})^T W) S +
+// (K e^{G_C-G})^T U, and maps compose because the decay is diagonal
+// ("ReplaySSM" analysis, section 2.1): a long sequence's serial chain of
+// chunks is cut into segments whose maps are built side by side, chained by
+// a short scan, and the segments are then re-run from their true starts.
+enum { UNIT_WRITE_HT = 1, UNIT_WRITE_NEXT = 2, UNIT_FROM_START = 4 };
+struct Unit {
+  int seq, c_begin, c_end, flags, slot, pad0, pad1, pad2;
+};
+
+// Chunks per segment of the state pass (0: sequences are never cut).  The
+// host cannot see the sequence lengths, so the choice assumes the worst case
+// for the chain, one sequence of all T tokens, and cuts only when the
+// batch's chains leave part of a 256-CU chip idle: it takes the segment
+// length whose schedule (first segments and maps in one launch, the re-runs
+// in the next; units beyond 256 wait for a second round) has the fewest
+// chunk steps on the critical path.
+constexpr int STATE_CUS = 256;
+int segment_chunks(int64_t T, int N, int H, int D, int C) {
+  const int VT = D >= 32 ? 32 : D;
+  const int64_t NV = D / VT, NM = 2 * NV;
+  const int64_t nch = (T + C - 1) / C;
+  // short chains are left whole: the extra launches would cost more
+  if ((int64_t)N * H * NV >= STATE_CUS || nch < 128) return 0;
+  auto rounds = [](int64_t units) { return (units + STATE_CUS - 1) / STATE_CUS; };
+  int64_t best = nch * rounds((int64_t)N * H * NV);
+  int best_len = 0;
+  for (int64_t len = 32; len < nch; len *= 2) {
+    for (int64_t l2 = len; l2 < 2 * len && l2 < nch; l2 += len / 4) {
+      const int64_t P = (nch + l2 - 1) / l2;
+      if (P < 3) continue;
+      const int64_t a = rounds((int64_t)N * H * NV + (P - 2) * H * NM);
+      const int64_t c = rounds((P - 1) * H * NV);
+      const int64_t cost = (a + c) * l2 + (P - 2) / 2;  // scan steps, ~half a chunk each
+      if (cost < best) {
+        best = cost;
+        best_len = (int)l2;
+      }
+    }
+  }
+  return best_len;
+}
+
+// Header of the workspace: chunk table [NCB], per-sequence entries [N], the
+// state pass's units (first segments [N] in the order the pass takes them,
+// maps and later segments, at most NSEG each), the unit counts, then the per-chunk
+// records, and with segments the start states [NSEG, H, D, D] and maps
+// [NSEG, H, D, 2 D] (fp32).
 struct WsLayout {
-  size_t table_off, seq_off, order_off, rec_off;
-  int64_t ncb;
+  size_t table_off, seq_off, unit_a_off, unit_m_off, unit_c_off, count_off, rec_off,
+      start_off, map_off, total;
+  int64_t ncb, nseg;
+  int seg_len;
 };
 
-WsLayout ws_layout(int64_t T, int N, int C) {
+WsLayout ws_layout(int64_t T, int N, int H, int D, int C, size_t rec) {
   WsLayout w;
   w.ncb = (T + C - 1) / C + N;
+  w.seg_len = segment_chunks(T, N, H, D, C);
+  w.nseg = w.seg_len > 0 ? w.ncb / w.seg_len + N : 0;
   w.table_off = 0;
   w.seq_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
-  w.order_off = w.seq_off + round256((size_t)N * sizeof(SeqInfo));
-  w.rec_off = w.order_off + round256((size_t)N * sizeof(int));
+  w.unit_a_off = w.seq_off + round256((size_t)N * sizeof(SeqInfo));
+  w.unit_m_off = w.unit_a_off + round256((size_t)N * sizeof(Unit));
+  w.unit_c_off = w.unit_m_off + round256((size_t)w.nseg * sizeof(Unit));
+  w.count_off = w.unit_c_off + round256((size_t)w.nseg * sizeof(Unit));
+  w.rec_off = w.count_off + 256;
+  w.start_off = w.rec_off + (size_t)w.ncb * H * rec;
+  w.map_off = w.start_off + (size_t)w.nseg * H * D * D * 4;
+  w.total = w.map_off + (size_t)w.nseg * H * D * 2 * D * 4;
   return w;
 }
 
@@ -249,25 +316,32 @@ __device__ __forceinline__ int block_scan(int x, int* scratch, Op op) {
 // of them.
 __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb, int snap_interval,
-    ChunkEntry* __restrict__ table, SeqInfo* __restrict__ seqs, int* __restrict__ order) {
+    int seg_len, ChunkEntry* __restrict__ table, SeqInfo* __restrict__ seqs,
+    Unit* __restrict__ units_a, Unit* __restrict__ units_m,
+    Unit* __restrict__ units_c, int* __restrict__ counts) {
   __shared__ int scratch[NTHREADS];
-  __shared__ int carry_max, carry_chunks, carry_snaps;
+  __shared__ int carry_max, carry_chunks, carry_snaps, carry_starts, carry_maps;
   __shared__ int bcount[33], bbase[33];
   const int t = threadIdx.x;
   auto clampT = [&](int64_t x) { return (int)(x < 0 ? 0 : (x > T ? T : x)); };
   auto bucket_of = [](int nch) { return nch <= 0 ? 0 : 32 - __clz(nch); };
   auto imax = [](int a, int b) { return a > b ? a : b; };
   auto iadd = [](int a, int b) { return a + b; };
+  // segments of a sequence of nch chunks (one when it is not cut)
+  auto nseg_of = [&](int nch) { return seg_len > 0 && nch > seg_len ? (nch + seg_len - 1) / seg_len : 1; };
   if (t == 0) {
     carry_max = clampT(cu[0]);
     carry_chunks = 0;
     carry_snaps = 0;
+    carry_starts = 0;
+    carry_maps = 0;
   }
   if (t < 33) bcount[t] = 0;
   __syncthreads();
   for (int base = 0; base < N; base += NTHREADS) {
     const int n = base + t;
     const int cm = carry_max, cc = carry_chunks, cs = carry_snaps;
+    const int cst = carry_starts, cmp = carry_maps;
     // hi of sequence n = p_{n+1}; lo = hi of sequence n-1 (p_n)
     const int hi = imax(cm, block_scan(n < N ? clampT(cu[n + 1]) : 0, scratch, imax));
     const int lo = t == 0 ? cm : imax(cm, scratch[t - 1]);
@@ -278,29 +352,65 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int first = cc + block_scan(nch, scratch, iadd) - nch;
     __syncthreads();
     const int sfirst = cs + block_scan(nsn, scratch, iadd) - nsn;
+    // start slots: one per segment after the first; maps: one per middle
+    // segment
+    const int nseg = n < N ? nseg_of(nch) : 1;
+    __syncthreads();
+    const int stfirst = cst + block_scan(nseg - 1, scratch, iadd) - (nseg - 1);
+    const int nmap = nseg > 2 ? nseg - 2 : 0;
+    __syncthreads();
+    const int mfirst = cmp + block_scan(nmap, scratch, iadd) - nmap;
     if (n < N) {
       SeqInfo e;
       e.lo = lo;
       e.hi = hi;
       e.chunk_first = first;
       e.snap_base = sfirst;
+      e.start_slot = stfirst;
+      e.map_slot = mfirst;
+      e.pad0 = e.pad1 = 0;
       seqs[n] = e;
       atomicAdd(&bcount[bucket_of(nch)], 1);
+      // maps of the middle segments and the re-runs of the later ones
+      for (int p = 1; p < nseg; ++p) {
+        const int b0 = first + p * seg_len, b1 = min(first + (p + 1) * seg_len, first + nch);
+        Unit uc;
+        uc.seq = n;
+        uc.c_begin = b0;
+        uc.c_end = b1;
+        uc.flags = UNIT_FROM_START | (p == nseg - 1 ? UNIT_WRITE_HT : 0);
+        uc.slot = stfirst + p - 1;
+        uc.pad0 = uc.pad1 = uc.pad2 = 0;
+        units_c[stfirst + p - 1] = uc;
+        if (p < nseg - 1) {
+          Unit um = uc;
+          um.flags = 0;
+          um.slot = mfirst + p - 1;
+          units_m[mfirst + p - 1] = um;
+        }
+      }
     }
     __syncthreads();
     if (t == NTHREADS - 1) {
       carry_max = hi > cm ? hi : cm;
       carry_chunks = first + nch;
       carry_snaps = sfirst + nsn;
+      carry_starts = stfirst + nseg - 1;
+      carry_maps = mfirst + nmap;
     }
     __syncthreads();
+  }
+  if (t == 0) {
+    counts[0] = N;             // first segments (every sequence)
+    counts[1] = carry_maps;    // middle-segment maps
+    counts[2] = carry_starts;  // later segments
   }
   const int total = carry_chunks;  // <= ncb (see above)
   __threadfence_block();
   __syncthreads();
-  // Longest sequences first: order[] lists the sequences by descending
-  // power-of-two bucket of their chunk count, so the state pass starts the
-  // longest serial chains first.
+  // Longest sequences first: units_a lists the sequences' first segments by
+  // descending power-of-two bucket of their chunk count, so the state pass
+  // starts the longest serial chains first.
   if (t == 0) {
     int acc = 0;
     for (int b = 32; b >= 0; --b) {
@@ -311,7 +421,18 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   __syncthreads();
   for (int n = t; n < N; n += NTHREADS) {
     const SeqInfo e = seqs[n];
-    order[atomicAdd(&bbase[bucket_of((e.hi - e.lo + C - 1) / C)], 1)] = n;
+    const int nch = (e.hi - e.lo + C - 1) / C;
+    const int pos = atomicAdd(&bbase[bucket_of(nch)], 1);
+    // the first (or only) segment of sequence n
+    const int nseg = nseg_of(nch);
+    Unit ua;
+    ua.seq = n;
+    ua.c_begin = e.chunk_first;
+    ua.c_end = e.chunk_first + (nseg > 1 ? seg_len : nch);
+    ua.flags = nseg > 1 ? UNIT_WRITE_NEXT : UNIT_WRITE_HT;
+    ua.slot = e.start_slot;
+    ua.pad0 = ua.pad1 = ua.pad2 = 0;
+    units_a[pos] = ua;
   }
   // entry i belongs to the last sequence whose first chunk is <= i (a
   // binary search over the monotone chunk_first; empty sequences share
@@ -1277,32 +1398,29 @@ struct StateOps {
   f32x4 gc[MS];            // e^{G_C} of the rows of those tiles
 };
 
-template <typename IO, int D, int C, int VT>
-__global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
-    const ChunkEntry* __restrict__ table, const SeqInfo* __restrict__ seqs,
-    const int* __restrict__ order, const char* __restrict__ recs, int ncb, int N, int H,
-    const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o,
-    float* __restrict__ snaps, int64_t snap_rows, int snap_interval) {
+// One work unit (see Unit) on one V tile vt of D / VT (MAP: one column tile
+// vt of the 2 D columns of [M | B]).
+template <typename IO, int D, int C, int VT, bool MAP>
+__device__ __forceinline__ void state_unit(
+    char* smem, const SeqInfo* __restrict__ seqs, const Unit& un, int h, int vt,
+    const char* __restrict__ recs, int ncb, int H, const float* __restrict__ h0,
+    float* __restrict__ ht, IO* __restrict__ o, float* __restrict__ snaps, int64_t snap_rows,
+    int snap_interval, float* __restrict__ starts, float* __restrict__ maps) {
   typedef Geom<D, C> Gm;
   typedef StateSmem<IO, D, C, VT> Sm;
   typedef StateOps<D, C, VT> Ops;
   constexpr int NV = D / VT, NTV = VT / 16, NB = Gm::NB, KTC = Gm::KTC, KTD = Gm::KTD;
   constexpr int MTD = Gm::MTD, MS = Ops::MS;
   constexpr int SK = Sm::SK, DK = Sm::DK;
-  __shared__ __align__(16) char smem[Sm::TOTAL];
+  constexpr int NTILE = MAP ? 2 * NV : NV;  // workgroups per (unit, head)
   bf16* sDh = reinterpret_cast<bf16*>(smem + Sm::D_OFF);
   bf16* sDl = reinterpret_cast<bf16*>(smem + Sm::D_OFF + Sm::D_BYTES);
 
-  // XCD-aware unit mapping: the NV tiles of one (sequence, head) get block
-  // ids congruent mod 8, i.e. the same XCD and L2.  Units are taken in the
-  // plan's longest-sequence-first order.
-  const int b = blockIdx.x;
-  const int vt = (b / 8) % NV;
-  const int u = (b / (8 * NV)) * 8 + (b % 8);
-  if (u >= N * H) return;
   // workgroup-uniform values as scalars, so that every branch on them is
   // uniform and the chunk table is read through scalar loads
-  const int n = __builtin_amdgcn_readfirstlane(order[u / H]), h = u % H;
+  const int n = __builtin_amdgcn_readfirstlane(un.seq);
+  const int flags = __builtin_amdgcn_readfirstlane(un.flags);
+  const int slot = __builtin_amdgcn_readfirstlane(un.slot);
   const int tid = threadIdx.x, l = tid & 63, lg = l >> 4, lr = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // When every wave owns a chunk row tile and the same number of state row
@@ -1317,7 +1435,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
   // zero the LDS padding once (k positions beyond D or C stay zero)
   for (int e = tid; e < (int)(Sm::TOTAL / 4); e += NTHREADS) reinterpret_cast<int*>(smem)[e] = 0;
 
-  // state tiles owned by this wave: ms = w + 4 i, all NTV column tiles
+  // state tiles owned by this wave: ms = w + 4 i, all NTV column tiles.  A
+  // map starts from [I | 0]; a later segment from its start slot; a first
+  // segment from h0 (or zeros).
+  const float* init = nullptr;
+  if (!MAP) {
+    if (flags & UNIT_FROM_START)
+      init = starts + ((size_t)slot * H + h) * D * D;
+    else if (h0 != nullptr)
+      init = h0 + ((size_t)n * H + h) * D * D;
+  }
   f32x4 S[MS][NTV];
 #pragma unroll
   for (int i = 0; i < MS; ++i) {
@@ -1326,23 +1453,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     for (int nt = 0; nt < NTV; ++nt) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
+        const int row = 16 * ms + 4 * lg + e, col = vt * VT + 16 * nt + lr;
         float x = 0.f;
-        if (h0 != nullptr && (ALL_MS || ms < MTD))
-          x = h0[(((int64_t)n * H + h) * D + 16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr];
+        if (MAP)
+          x = row == col ? 1.f : 0.f;
+        else if (init != nullptr && (ALL_MS || ms < MTD))
+          x = init[row * D + col];
         S[i][nt][e] = x;
       }
     }
   }
 
-  // the sequence's chunks and tokens, from the plan (disjoint clamped ranges,
-  // so c_last never passes the workspace's chunk count)
+  // the sequence's tokens and first chunk, from the plan (disjoint clamped
+  // ranges, so no chunk index passes the workspace's chunk count)
   const SeqInfo si = seqs[n];
   const int seq_start = __builtin_amdgcn_readfirstlane(si.lo);
   const int seq_end = __builtin_amdgcn_readfirstlane(si.hi);
   const int c_first = __builtin_amdgcn_readfirstlane(si.chunk_first);
-  const int c_last = min(ncb, c_first + (seq_end - seq_start + C - 1) / C);
+  const int c_begin = __builtin_amdgcn_readfirstlane(un.c_begin);
+  const int c_last = min(ncb, __builtin_amdgcn_readfirstlane(un.c_end));
   // snapshot rows of this sequence follow those of sequences 0 .. n-1
   const int snap_base = __builtin_amdgcn_readfirstlane(si.snap_base);
+  // U's column tile (a map's M columns have no U: D = -W S there)
+  const bool has_u = !MAP || vt >= NV;
+  const int ut = MAP ? vt - NV : vt;
   // Every operand of a chunk is loaded unconditionally (including Aq tiles
   // above the diagonal, which are never multiplied), so the loads form one
   // straight block.
@@ -1359,7 +1493,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
         ops.w[kt] = buffer_frag(r, lane16, Gm::W_OFF + (mt * KTD + kt) * FRAG_BYTES);
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt)
-        ops.u[nt] = buffer_f32x4(r, lane16, Gm::U_OFF + ((mt * MTD + vt * NTV + nt) * 64) * 16);
+        ops.u[nt] = has_u ? buffer_f32x4(r, lane16, Gm::U_OFF + ((mt * MTD + ut * NTV + nt) * 64) * 16)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   auto load_kt = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
@@ -1375,14 +1510,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     }
   };
   auto load_q = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
-    if (has_mt) {
+    if (!MAP && has_mt) {
 #pragma unroll
       for (int kt = 0; kt < KTD; ++kt)
         ops.q[kt] = buffer_frag(r, lane16, Gm::Q_OFF + (mt * KTD + kt) * FRAG_BYTES);
     }
   };
   auto load_aq = [&](Ops& ops, __amdgpu_buffer_rsrc_t r) {
-    if (has_mt) {
+    if (!MAP && has_mt) {
 #pragma unroll
       for (int kt = 0; kt < KTC; ++kt)
         ops.aq[kt] = buffer_frag(r, lane16, Gm::AQ_OFF + (mt * KTC + kt) * FRAG_BYTES);
@@ -1402,13 +1537,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
   // entering S and D fragments stay in registers for the read-out.
   bf16* sSh = reinterpret_cast<bf16*>(smem + Sm::S_OFF);
   bf16* sSl = reinterpret_cast<bf16*>(smem + Sm::S_OFF + Sm::S_BYTES);
-  // L2 prefetch two chunks ahead: the NV workgroups of a (sequence, head)
-  // each touch one word in every NV-th 128-byte line of the record, so the
+  // L2 prefetch two chunks ahead: the NTILE workgroups of a (unit, head)
+  // each touch one word in every NTILE-th 128-byte line of the record, so the
   // operand loads of that chunk, issued one chunk later, hit L2.  The words
   // are read into registers that are consumed one chunk after that, when the
   // loads have long completed.
   constexpr int LINES = (int)(Gm::REC / 128);
-  constexpr int NPF = (LINES + NV * NTHREADS - 1) / (NV * NTHREADS);
+  constexpr int NPF = (LINES + NTILE * NTHREADS - 1) / (NTILE * NTHREADS);
   int pf[NPF];
 #pragma unroll
   for (int i = 0; i < NPF; ++i) pf[i] = 0;
@@ -1418,7 +1553,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     const __amdgpu_buffer_rsrc_t r = rsrc_of(min(ch + 2, c_last - 1));
 #pragma unroll
     for (int i = 0; i < NPF; ++i) {
-      const int line = vt + NV * (tid + NTHREADS * i);
+      const int line = vt + NTILE * (tid + NTHREADS * i);
       // out-of-range offsets read as zero (the buffer bound is the record)
       pf[i] = __builtin_amdgcn_raw_buffer_load_b32(r, (uint32_t)line * 128u, 0, 0);
     }
@@ -1515,7 +1650,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     // (K e^{G_C-G} and e^{G_C} of this chunk are dead: every wave that owns
     // state rows fetches the next ones, spread between the MFMAs below)
     load_kt(ops, rn);
-    if (has_mt) {
+    if (!MAP && has_mt) {
       f32x4 O[NTV];
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) O[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1555,7 +1690,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
     }
     // chunk-boundary snapshot: the state after this chunk, when the chunk
     // ends a whole multiple of snap_interval tokens into the sequence
-    if (snaps != nullptr) {
+    if (!MAP && snaps != nullptr) {
       const int end_tok = (ch - c_first + 1) * C;
       const int64_t row = (int64_t)snap_base + end_tok / snap_interval - 1;
       if (end_tok <= seq_end - seq_start && end_tok % snap_interval == 0 && row < snap_rows) {
@@ -1582,12 +1717,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
   // One operand set in registers: each part is refetched for chunk i+1 as
   // soon as chunk i has used it, so every fetch has about one chunk period
   // to arrive (the last fetch repeats the last chunk and goes unused).
+  // The initial state's loads complete here: otherwise the compiler's wait
+  // analysis, which merges this path with the loop's back edge, can make the
+  // top of every chunk wait for all outstanding loads.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   Ops ops;
-  if (c_first < c_last) load(ops, c_first);
+  if (c_begin < c_last) load(ops, c_begin);
   __syncthreads();
-  for (int ch = c_first; ch < c_last; ++ch) process(ops, ch);
+  for (int ch = c_begin; ch < c_last; ++ch) process(ops, ch);
 
-  if (ht != nullptr) {
+  // the final state: ht (the whole sequence or its last segment), the next
+  // segment's start slot, or the map slot ([K, 2 D] rows per head)
+  float* dst = nullptr;
+  int ld = D;
+  if (MAP) {
+    dst = maps + ((size_t)slot * H + h) * D * 2 * D;
+    ld = 2 * D;
+  } else if (flags & UNIT_WRITE_NEXT) {
+    dst = starts + ((size_t)slot * H + h) * D * D;
+  } else if ((flags & UNIT_WRITE_HT) && ht != nullptr) {
+    dst = ht + ((size_t)n * H + h) * D * D;
+  }
+  if (dst != nullptr) {
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
       const int ms = w + 4 * i;
@@ -1596,10 +1747,85 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            ht[(((int64_t)n * H + h) * D + 16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr] =
-                S[i][nt][e];
+            dst[(size_t)(16 * ms + 4 * lg + e) * ld + vt * VT + 16 * nt + lr] = S[i][nt][e];
       }
     }
+  }
+}
+
+// The state pass over a list of units: blocks 0 .. 8 * NV * ceil(H nu / 8)
+// - 1 take the units of `units` (nu = *n_units of them), each on its NV V
+// tiles; with maps, the blocks after them take the map units (*n_maps), each
+// on the 2 NV column tiles of [M | B].  Block ids are XCD-aware: the tiles
+// of one (unit, head) get ids congruent mod 8, so they share one L2.
+template <typename IO, int D, int C, int VT>
+__global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
+    const SeqInfo* __restrict__ seqs, const Unit* __restrict__ units,
+    const int* __restrict__ n_units, int units_max, const Unit* __restrict__ map_units,
+    const int* __restrict__ n_maps, const char* __restrict__ recs, int ncb, int H,
+    const float* __restrict__ h0, float* __restrict__ ht, IO* __restrict__ o,
+    float* __restrict__ snaps, int64_t snap_rows, int snap_interval, float* __restrict__ starts,
+    float* __restrict__ maps) {
+  typedef StateSmem<IO, D, C, VT> Sm;
+  constexpr int NV = D / VT;
+  __shared__ __align__(16) char smem[Sm::TOTAL];
+  const int norm_blocks = (H * units_max + 7) / 8 * 8 * NV;
+  int b = blockIdx.x;
+  if (b < norm_blocks) {
+    const int vt = (b / 8) % NV;
+    const int u = (b / (8 * NV)) * 8 + (b % 8);
+    if (u >= __builtin_amdgcn_readfirstlane(*n_units) * H) return;
+    state_unit<IO, D, C, VT, false>(smem, seqs, units[u / H], u % H, vt, recs, ncb, H, h0, ht, o,
+                                    snaps, snap_rows, snap_interval, starts, maps);
+  } else {
+    b -= norm_blocks;
+    const int vt = (b / 8) % (2 * NV);
+    const int u = (b / (16 * NV)) * 8 + (b % 8);
+    if (map_units == nullptr || u >= __builtin_amdgcn_readfirstlane(*n_maps) * H) return;
+    state_unit<IO, D, C, VT, true>(smem, seqs, map_units[u / H], u % H, vt, recs, ncb, H, h0, ht,
+                                   o, snaps, snap_rows, snap_interval, starts, maps);
+  }
+}
+
+// Start states of the later segments of every cut sequence: start(p) of
+// segment p + 1 = M_p start(p - 1) + B_p for the middle segments p = 1 ..
+// nseg - 2, in order (start slot 0 of the sequence holds the first segment's
+// final state).  One workgroup per (sequence, head, group of 4 columns), one
+// thread per row; fp32 throughout.
+template <int D>
+__global__ __launch_bounds__(D) void scan_kernel(const SeqInfo* __restrict__ seqs, int N, int H,
+                                                 int C, int seg_len,
+                                                 const float* __restrict__ maps,
+                                                 float* __restrict__ starts) {
+  __shared__ float4 sS[D];
+  const int groups = D / 4;
+  const int b = blockIdx.x;
+  const int cg = b % groups, h = (b / groups) % H, n = b / (groups * H);
+  if (n >= N) return;
+  const SeqInfo si = seqs[n];
+  const int nch = (si.hi - si.lo + C - 1) / C;
+  const int nseg = nch > seg_len ? (nch + seg_len - 1) / seg_len : 1;
+  if (nseg < 3) return;
+  const int i = threadIdx.x;
+  float4 x = *reinterpret_cast<const float4*>(starts + (((size_t)si.start_slot * H + h) * D + i) * D +
+                                              4 * cg);
+  for (int p = 1; p <= nseg - 2; ++p) {
+    sS[i] = x;
+    __syncthreads();
+    const float* M = maps + (((size_t)(si.map_slot + p - 1) * H + h) * D + i) * 2 * D;
+    float4 acc = *reinterpret_cast<const float4*>(M + D + 4 * cg);  // B_p
+#pragma unroll 4
+    for (int j = 0; j < D; j += 4) {
+      const float4 m = *reinterpret_cast<const float4*>(M + j);
+      acc = fma4(m.x, sS[j], acc);
+      acc = fma4(m.y, sS[j + 1], acc);
+      acc = fma4(m.z, sS[j + 2], acc);
+      acc = fma4(m.w, sS[j + 3], acc);
+    }
+    __syncthreads();
+    x = acc;
+    *reinterpret_cast<float4*>(starts + (((size_t)(si.start_slot + p) * H + h) * D + i) * D +
+                               4 * cg) = x;
   }
 }
 
@@ -1616,19 +1842,25 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   typedef Geom<D, C> Gm;
   constexpr int VT = state_vt<D>();
   constexpr int NV = D / VT;
-  const WsLayout ws = ws_layout(a.T, a.N, C);
+  const WsLayout ws = ws_layout(a.T, a.N, a.H, D, C, Gm::REC);
   char* base = reinterpret_cast<char*>(a.ws);
   ChunkEntry* table = reinterpret_cast<ChunkEntry*>(base + ws.table_off);
   SeqInfo* seqs = reinterpret_cast<SeqInfo*>(base + ws.seq_off);
-  int* order = reinterpret_cast<int*>(base + ws.order_off);
+  Unit* units_a = reinterpret_cast<Unit*>(base + ws.unit_a_off);
+  Unit* units_m = reinterpret_cast<Unit*>(base + ws.unit_m_off);
+  Unit* units_c = reinterpret_cast<Unit*>(base + ws.unit_c_off);
+  int* counts = reinterpret_cast<int*>(base + ws.count_off);
   char* recs = base + ws.rec_off;
+  float* starts = reinterpret_cast<float*>(base + ws.start_off);
+  float* maps = reinterpret_cast<float*>(base + ws.map_off);
   auto mark = [&](int i) -> hipError_t {
     return a.marks ? hipEventRecord((hipEvent_t)a.marks[i], st) : hipSuccess;
   };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T,
-                     C, ws.ncb, a.snaps != nullptr ? a.snap_interval : 0, table, seqs, order);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T, C,
+                     ws.ncb, a.snaps != nullptr ? a.snap_interval : 0, ws.seg_len, table, seqs,
+                     units_a, units_m, units_c, counts);
   if ((e = mark(1)) != hipSuccess) return e;
   if (a.T > 0) {
     auto intra = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
@@ -1639,13 +1871,25 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
                        a.per_head_gate, a.qk_l2norm);
   }
   if ((e = mark(2)) != hipSuccess) return e;
-  const int units = a.N * a.H;
-  const int groups = (units + 7) / 8;
-  hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)(groups * 8 * NV)),
-                     dim3(NTHREADS), 0, st, table, seqs, order, recs, (int)ws.ncb, a.N, a.H,
-                     a.h0, a.ht, (IO*)a.o, a.snaps, a.snap_rows, a.snap_interval);
+  // first segments (every sequence, longest first) and, with segments, the
+  // middle segments' maps in the same launch
+  const int64_t blocks_a = (int64_t)(a.H * a.N + 7) / 8 * 8 * NV +
+                           (int64_t)(a.H * ws.nseg + 7) / 8 * 8 * 2 * NV;
+  hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)blocks_a), dim3(NTHREADS), 0, st,
+                     seqs, units_a, counts + 0, a.N, ws.nseg > 0 ? units_m : nullptr, counts + 1,
+                     recs, (int)ws.ncb, a.H, a.h0, a.ht, (IO*)a.o, a.snaps, a.snap_rows,
+                     a.snap_interval, starts, maps);
+  if (ws.nseg > 0) {
+    // chain the start states, then re-run the later segments from them
+    hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)(a.N * a.H * (D / 4))), dim3(D), 0, st,
+                       seqs, a.N, a.H, C, ws.seg_len, maps, starts);
+    const int64_t blocks_c = (int64_t)(a.H * ws.nseg + 7) / 8 * 8 * NV;
+    hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)blocks_c), dim3(NTHREADS), 0,
+                       st, seqs, units_c, counts + 2, (int)ws.nseg, (const Unit*)nullptr,
+                       counts + 1, recs, (int)ws.ncb, a.H, a.h0, a.ht, (IO*)a.o, a.snaps,
+                       a.snap_rows, a.snap_interval, starts, maps);
+  }
   if ((e = mark(3)) != hipSuccess) return e;
-  (void)sizeof(Gm);
   return hipGetLastError();
 }
 
@@ -1674,8 +1918,7 @@ hipError_t prefill_d(const PrefillArgs& a, hipStream_t st) {
 
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C) {
   (void)V;
-  const WsLayout ws = ws_layout(T, N, C);
-  return ws.rec_off + (size_t)ws.ncb * H * rec_bytes(K, C);
+  return ws_layout(T, N, H, K, C, rec_bytes(K, C)).total;
 }
 
 hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream) {
