@@ -115,7 +115,8 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
                            const float* A_log = nullptr, const float* dt_bias = nullptr,
                            float lower_bound = 0.f, float* snaps = nullptr,
                            int snap_interval = 0, int64_t snap_rows = 0, int qk_heads = 0,
-                           int per_head_gate = 0, int qk_l2norm = 0) {
+                           int per_head_gate = 0, int qk_l2norm = 0,
+                           bool single_stream = false) {
   if (io != KDA_F32 && io != KDA_BF16) return KDA_ERR_UNSUPPORTED;
   if (N < 1 || H < 1 || T < 0) return KDA_ERR_INVALID_ARGUMENT;
   if (!head_dim_ok(K) || !head_dim_ok(V) || K != V) return KDA_ERR_UNSUPPORTED;
@@ -137,7 +138,7 @@ kda_status prefill_checked(kda_dtype io, const void* q, const void* k, const voi
   kda::PrefillArgs p{io == KDA_BF16, q, k, v, g, beta, cu_seqlens, N, T, H, K, V,
                      chunk, scale, h0, ht, o, workspace, workspace_bytes, marks,
                      gate_mode, A_log, dt_bias, lower_bound, snaps, snap_interval,
-                     snap_rows, qk_heads, per_head_gate, qk_l2norm};
+                     snap_rows, qk_heads, per_head_gate, qk_l2norm, single_stream};
   return launch_status(kda::run_prefill(p, (hipStream_t)stream));
 }
 
@@ -172,6 +173,39 @@ void* scratch_on(hipStream_t stream) {
     scratch_ptr[dev] = p;
   }
   return scratch_ptr[dev];
+}
+
+kda_status prefill_ex_impl(kda_dtype io, const void* q, const void* k,
+                                const void* v, const float* g, const float* beta,
+                                const int32_t* cu_seqlens, int32_t N, int64_t T,
+                                int32_t H, int32_t K, int32_t V, int32_t chunk,
+                                float scale, const float* h0, float* ht, void* o,
+                                void* workspace, size_t workspace_bytes,
+                                const kda_prefill_opts* opts, void* stream,
+                                bool single_stream) {
+  if (!opts)
+    return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0,
+                           ht, o, workspace, workspace_bytes, stream, nullptr, 0, nullptr,
+                           nullptr, 0.f, nullptr, 0, 0, 0, 0, 0, single_stream);
+  if (opts->gate_mode < 0 || opts->gate_mode > 2) return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->gate_mode == 2 && !(opts->lower_bound < 0.f)) return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->qk_heads < 0 || (opts->qk_heads > 0 && H % opts->qk_heads != 0))
+    return KDA_ERR_INVALID_ARGUMENT;
+  if (opts->per_head_gate && H % 4 != 0) return KDA_ERR_UNSUPPORTED;
+  int interval = 0;
+  if (opts->snapshots) {
+    interval = opts->snapshot_interval;
+    if (interval < 1 || chunk < 1 || interval % chunk != 0) return KDA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(opts->snapshots) || T < 0 || opts->snapshot_rows < T / interval)
+      return KDA_ERR_INVALID_ARGUMENT;
+  }
+  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, stream, nullptr, opts->gate_mode,
+                         opts->A_log, opts->dt_bias,
+                         opts->gate_mode == 2 ? opts->lower_bound : 0.f, opts->snapshots,
+                         interval, opts->snapshots ? opts->snapshot_rows : 0, opts->qk_heads,
+                         opts->per_head_gate != 0,
+                         opts->qk_l2norm != 0, single_stream);
 }
 
 }  // namespace
@@ -249,28 +283,8 @@ kda_status kda_chunk_prefill_ex(kda_dtype io, const void* q, const void* k,
                                 float scale, const float* h0, float* ht, void* o,
                                 void* workspace, size_t workspace_bytes,
                                 const kda_prefill_opts* opts, void* stream) {
-  if (!opts)
-    return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0,
-                           ht, o, workspace, workspace_bytes, stream, nullptr);
-  if (opts->gate_mode < 0 || opts->gate_mode > 2) return KDA_ERR_INVALID_ARGUMENT;
-  if (opts->gate_mode == 2 && !(opts->lower_bound < 0.f)) return KDA_ERR_INVALID_ARGUMENT;
-  if (opts->qk_heads < 0 || (opts->qk_heads > 0 && H % opts->qk_heads != 0))
-    return KDA_ERR_INVALID_ARGUMENT;
-  if (opts->per_head_gate && H % 4 != 0) return KDA_ERR_UNSUPPORTED;
-  int interval = 0;
-  if (opts->snapshots) {
-    interval = opts->snapshot_interval;
-    if (interval < 1 || chunk < 1 || interval % chunk != 0) return KDA_ERR_INVALID_ARGUMENT;
-    if (!aligned16(opts->snapshots) || T < 0 || opts->snapshot_rows < T / interval)
-      return KDA_ERR_INVALID_ARGUMENT;
-  }
-  return prefill_checked(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
-                         o, workspace, workspace_bytes, stream, nullptr, opts->gate_mode,
-                         opts->A_log, opts->dt_bias,
-                         opts->gate_mode == 2 ? opts->lower_bound : 0.f, opts->snapshots,
-                         interval, opts->snapshots ? opts->snapshot_rows : 0, opts->qk_heads,
-                         opts->per_head_gate != 0,
-                         opts->qk_l2norm != 0);
+  return prefill_ex_impl(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, workspace, workspace_bytes, opts, stream, false);
 }
 
 kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
@@ -286,7 +300,8 @@ kda_status kda_chunk_prefill_marked(kda_dtype io, const void* q, const void* k,
   if (!(lower_bound <= 0.f)) return KDA_ERR_INVALID_ARGUMENT;
   return prefill_checked(io, q, k, v, a, b, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
                          o, workspace, workspace_bytes, stream, marks,
-                         lower_bound < 0.f ? 2 : 1, A_log, dt_bias, lower_bound);
+                         lower_bound < 0.f ? 2 : 1, A_log, dt_bias, lower_bound, nullptr, 0, 0,
+                         0, 0, 0, /*single_stream=*/true);
 }
 
 kda_status kda_chunk_prefill_gated(kda_dtype io, const void* q, const void* k,
@@ -436,8 +451,9 @@ kda_status kda_chunk_prefill_noalloc(kda_dtype io, const void* q, const void* k,
   if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH_LIMIT;
   void* ws = scratch_on((hipStream_t)stream);
   if (ws == nullptr) return KDA_ERR_LAUNCH;
-  return kda_chunk_prefill_ex(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0,
-                              ht, o, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, opts, stream);
+  return prefill_ex_impl(io, q, k, v, g, beta, cu_seqlens, N, T, H, K, V, chunk, scale, h0, ht,
+                         o, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, opts, stream,
+                         /*single_stream=*/true);
 }
 
 }  // extern "C"

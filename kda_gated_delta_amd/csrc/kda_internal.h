@@ -93,6 +93,10 @@ struct PrefillArgs {
   int qk_heads;       // heads of q and k (0: H)
   int per_head_gate;  // g (or a) is [T, H] and dt_bias [H]
   int qk_l2norm;      // q, k L2-normalised in the kernel
+  // Every kernel on `stream` (no second stream, nothing created): the same
+  // kernels and results, without the overlap of the intra-chunk work of one
+  // wave of a long chain with the state pass of the previous.
+  bool single_stream;
 };
 
 hipError_t run_gate(const GateArgs& a, hipStream_t stream);

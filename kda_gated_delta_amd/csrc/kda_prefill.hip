@@ -38,7 +38,10 @@
 #include "kda_gate_math.h"
 #include "kda_internal.h"
 
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
+#include <vector>
 
 namespace kda {
 namespace {
@@ -192,91 +195,121 @@ struct SeqInfo {
   int lo, hi, chunk_first, snap_base, start_slot, map_slot, pad0, pad1;
 };
 
-// A work unit of the state pass: the chunks c_begin .. c_end-1 of sequence
-// `seq`, in one of three roles.
-//  - first segment (or the whole sequence): from h0 (or zeros); writes ht
-//    when it is the whole sequence, else its final state into start slot
-//    `slot` (the next segment's start);
-//  - map of a middle segment: the affine map S -> M S + B of its chunks,
+// A work unit of the state pass: the chunk-table entries c_begin .. c_end-1,
+// chunks r_begin, r_begin + 1, .. of sequence `seq`, in one of three roles.
+//  - a segment of the chain (the whole sequence when it is not cut): from
+//    h0 (or zeros) or, with UNIT_FROM_START, from start slot in_slot; it
+//    writes ht when it ends the sequence (UNIT_WRITE_HT), else its final
+//    state into start slot out_slot (UNIT_WRITE_NEXT), the next segment's
+//    start;
+//  - the map of a middle segment: the affine map S -> M S + B of its chunks,
 //    computed as the state pass over the K + V columns of [M | B] from
-//    [I | 0] with no read-out, into map slot `slot`;
-//  - later segment: from start slot `slot`; writes ht when it is the last.
+//    [I | 0] with no read-out, into map slot out_slot.
+// A unit without flags (a wave the sequence does not reach) does nothing.
 // A chunk is the affine map S -> (Diag(e^{G_C}) - (K e^{G_C-G})^T W) S +
 // (K e^{G_C-G})^T U, and maps compose because the decay is diagonal
 // ("ReplaySSM" analysis, section 2.1): a long sequence's serial chain of
-// chunks is cut into segments whose maps are built side by side, chained by
-// a short scan, and the segments are then re-run from their true starts.
+// chunks can be cut into segments whose maps are built side by side, chained
+// by a short scan, and re-run from their true starts.  Cut into waves of
+// consecutive segments instead, the chain stays whole (the state is handed
+// on exactly through the start slots) and wave p's state pass can run while
+// the intra-chunk work of wave p + 1 is still being done.
 enum { UNIT_WRITE_HT = 1, UNIT_WRITE_NEXT = 2, UNIT_FROM_START = 4 };
 struct Unit {
-  int seq, c_begin, c_end, flags, slot, pad0, pad1, pad2;
+  int seq, c_begin, c_end, flags, in_slot, out_slot, r_begin, pad;
 };
 
-// Chunks per segment of the state pass (0: sequences are never cut).  The
-// host cannot see the sequence lengths, so the choice assumes the worst case
-// for the chain, one sequence of all T tokens, and cuts only when the
-// batch's chains leave part of a 256-CU chip idle (one workgroup per CU).
-// It takes the number of segments P whose schedule has the fewest chunk
-// steps on the critical path: the first launch runs the first segments and
-// the maps (a map step costs about 0.6 of a full step: no read-out), the
-// maps beyond the chip's width in further rounds; the second launch re-runs
-// the P - 1 later segments; the scan adds about half a step per segment.
-// P is taken from 3, 4, 6, 8, 12, ... (measured on one 65536-token sequence:
-// 16 even segments of 64 chunks beat 17 of 61 by 15%, which the round count
-// alone does not see).
+// How the state pass is cut (decided on the host from T, N, H, D, C alone:
+// the host never reads the sequence lengths, so every choice assumes the
+// worst case for the chain, one sequence of all T tokens).
+//  - maps: when the batch's (sequence, head) chains leave most of a 256-CU
+//    chip idle (one state workgroup per CU), middle segments build their
+//    chunk maps side by side.  The segment count P (smooth values; 16 even
+//    segments of 64 chunks beat 17 of 61 by 15% on one 65536-token
+//    sequence) minimises the chunk steps on the critical path: the first
+//    launch runs the first segments and the maps (a map step costs about 0.6
+//    of a full step: no read-out), the maps beyond the chip's width in
+//    further rounds; the second launch re-runs the P - 1 later segments; the
+//    scan adds about half a step per segment.  Taken only when that beats
+//    the whole chain by a quarter.
+//  - waves: otherwise, when the chains still leave CUs free (so that the
+//    intra-chunk kernel has room beside the state pass) and a chain can
+//    reach 128 chunks, the chain is cut into about 8 waves of at least 16
+//    chunks, handed on exactly, and the intra-chunk work of each wave
+//    overlaps the state pass of the previous.  (On the packed 7680-token
+//    batch, whose 512 chains fill the chip, waves cost 30% more than they
+//    save; on one 65536-token sequence they save 13%.)
 constexpr int STATE_CUS = 256;
-int segment_chunks(int64_t T, int N, int H, int D, int C) {
+struct StateCut {
+  int seg_len;   // chunks per segment (0: the chain is never cut)
+  bool maps;     // segments chained by maps (else: waves)
+  int n_waves;   // waves of the pipelined schedule (1 without)
+};
+
+StateCut state_cut(int64_t T, int N, int H, int D, int C) {
+  StateCut cut{0, false, 1};
   const int VT = D >= 32 ? 32 : D;
   const int64_t NV = D / VT, NM = 2 * NV;
   const int64_t nch = (T + C - 1) / C;
-  // short chains are left whole: the extra launches would cost more
-  if ((int64_t)N * H * NV >= STATE_CUS || nch < 128) return 0;
-  auto rounds = [](int64_t units) { return (units + STATE_CUS - 1) / STATE_CUS; };
-  double best = (double)nch;
-  int best_len = 0;
-  static const int64_t kSegments[] = {3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
-  for (const int64_t P : kSegments) {
-    const int64_t len = (nch + P - 1) / P;
-    if (len < 32) break;
-    const int64_t first = (int64_t)N * H * NV, maps = (P - 2) * H * NM;
-    const int64_t spill = first + maps > STATE_CUS ? first + maps - STATE_CUS : 0;
-    const double a = 1.0 + 0.6 * (double)rounds(spill);
-    const double c = (double)rounds((P - 1) * H * NV);
-    const double cost = (a + c) * (double)len + 0.5 * (double)(P - 2);
-    if (cost < best) {
-      best = cost;
-      best_len = (int)len;
+  if ((int64_t)N * H * NV < STATE_CUS && nch >= 128) {
+    auto rounds = [](int64_t units) { return (units + STATE_CUS - 1) / STATE_CUS; };
+    double best = 0.75 * (double)nch;
+    static const int64_t kSegments[] = {3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+    for (const int64_t P : kSegments) {
+      const int64_t len = (nch + P - 1) / P;
+      if (len < 32) break;
+      const int64_t first = (int64_t)N * H * NV, maps = (P - 2) * H * NM;
+      const int64_t spill = first + maps > STATE_CUS ? first + maps - STATE_CUS : 0;
+      const double a = 1.0 + 0.6 * (double)rounds(spill);
+      const double c = (double)rounds((P - 1) * H * NV);
+      const double cost = (a + c) * (double)len + 0.5 * (double)(P - 2);
+      if (cost < best) {
+        best = cost;
+        cut.seg_len = (int)len;
+        cut.maps = true;
+      }
     }
   }
-  return best_len;
+  if (!cut.maps && (int64_t)N * H * NV <= STATE_CUS && nch >= 128) {
+    cut.seg_len = (int)std::max<int64_t>(16, (nch + 7) / 8);
+    cut.n_waves = (int)((nch + cut.seg_len - 1) / cut.seg_len);
+  }
+  return cut;
 }
 
-// Header of the workspace: chunk table [NCB], per-sequence entries [N], the
-// state pass's units (first segments [N] in the order the pass takes them,
-// maps and later segments, at most NSEG each), the unit counts, then the per-chunk
-// records, and with segments the start states [NSEG, H, D, D] and maps
+// Header of the workspace: chunk table [NCB] (wave-major with waves,
+// sequence-major otherwise), per-sequence entries [N], the state pass's
+// units (first segments [N] in the order the pass takes them, maps and later
+// segments, at most NSEG each; with waves, [waves, N] units instead), the
+// unit counts and the waves' chunk-table offsets, then the per-chunk
+// records, and with a cut chain the start states [NSEG, H, D, D] and maps
 // [NSEG, H, D, 2 D] (fp32).
 struct WsLayout {
-  size_t table_off, seq_off, unit_a_off, unit_m_off, unit_c_off, count_off, rec_off,
-      start_off, map_off, total;
+  size_t table_off, seq_off, unit_a_off, unit_m_off, unit_c_off, unit_w_off, count_off,
+      wave_off, rec_off, start_off, map_off, total;
   int64_t ncb, nseg;
-  int seg_len;
+  StateCut cut;
 };
 
 WsLayout ws_layout(int64_t T, int N, int H, int D, int C, size_t rec) {
   WsLayout w;
   w.ncb = (T + C - 1) / C + N;
-  w.seg_len = segment_chunks(T, N, H, D, C);
-  w.nseg = w.seg_len > 0 ? w.ncb / w.seg_len + N : 0;
+  w.cut = state_cut(T, N, H, D, C);
+  w.nseg = w.cut.seg_len > 0 ? w.ncb / w.cut.seg_len + N : 0;
+  const int64_t nmaps = w.cut.maps ? w.nseg : 0;
+  const int64_t nwunits = w.cut.n_waves > 1 ? (int64_t)w.cut.n_waves * N : 0;
   w.table_off = 0;
   w.seq_off = round256((size_t)w.ncb * sizeof(ChunkEntry));
   w.unit_a_off = w.seq_off + round256((size_t)N * sizeof(SeqInfo));
   w.unit_m_off = w.unit_a_off + round256((size_t)N * sizeof(Unit));
-  w.unit_c_off = w.unit_m_off + round256((size_t)w.nseg * sizeof(Unit));
-  w.count_off = w.unit_c_off + round256((size_t)w.nseg * sizeof(Unit));
-  w.rec_off = w.count_off + 256;
+  w.unit_c_off = w.unit_m_off + round256((size_t)nmaps * sizeof(Unit));
+  w.unit_w_off = w.unit_c_off + round256((size_t)(w.cut.maps ? w.nseg : 0) * sizeof(Unit));
+  w.count_off = w.unit_w_off + round256((size_t)nwunits * sizeof(Unit));
+  w.wave_off = w.count_off + 256;
+  w.rec_off = w.wave_off + round256((size_t)(w.cut.n_waves + 1) * sizeof(int));
   w.start_off = w.rec_off + (size_t)w.ncb * H * rec;
   w.map_off = w.start_off + (size_t)w.nseg * H * D * D * 4;
-  w.total = w.map_off + (size_t)w.nseg * H * D * 2 * D * 4;
+  w.total = w.map_off + (size_t)nmaps * H * D * 2 * D * 4;
   return w;
 }
 
@@ -316,25 +349,46 @@ __device__ __forceinline__ int block_scan(int x, int* scratch, Op op) {
 // valid cu_seqlens (cu[0] = 0 <= cu[1] <= .. <= cu[N] = T) that is exactly
 // cu[n] .. cu[n+1]-1; for any other array the ranges still partition a part
 // of [0, T), so the chunks never outnumber the workspace's ceil(T/C) + N.
-// Sequence n owns chunks seqs[n].chunk_first .. + ceil((hi - lo) / C) - 1;
-// table entries past the last chunk get len = 0.  With snapshots, sequence n
+// Table entries past the last chunk get len = 0.  With snapshots, sequence n
 // owns the rows from seqs[n].snap_base on, floor((hi - lo) / snap_interval)
-// of them.
+// of them.  The state pass's units follow the cut (see StateCut): with
+// segments of seg_len chunks, a sequence of nch chunks has ceil(nch /
+// seg_len) of them (one when nch <= seg_len) and one start slot per segment
+// after its first.  Without waves the table is sequence-major (sequence n
+// owns entries chunk_first .. + nch - 1); with n_waves > 1 it is wave-major:
+// wave p holds segment p of every sequence that has one, sequence after
+// sequence, from entry wave_off[p] on.
 __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int32_t* __restrict__ cu, int N, int64_t T, int C, int64_t ncb, int snap_interval,
-    int seg_len, ChunkEntry* __restrict__ table, SeqInfo* __restrict__ seqs,
-    Unit* __restrict__ units_a, Unit* __restrict__ units_m,
-    Unit* __restrict__ units_c, int* __restrict__ counts) {
+    int seg_len, int maps, int n_waves, ChunkEntry* __restrict__ table,
+    SeqInfo* __restrict__ seqs, Unit* __restrict__ units_a, Unit* __restrict__ units_m,
+    Unit* __restrict__ units_c, Unit* __restrict__ units_w, int* __restrict__ counts,
+    int* __restrict__ wave_off) {
   __shared__ int scratch[NTHREADS];
-  __shared__ int carry_max, carry_chunks, carry_snaps, carry_starts, carry_maps;
+  __shared__ int carry_max, carry_chunks, carry_snaps, carry_starts, carry_maps, carry_wave;
   __shared__ int bcount[33], bbase[33];
   const int t = threadIdx.x;
+  const bool waves = n_waves > 1;
   auto clampT = [&](int64_t x) { return (int)(x < 0 ? 0 : (x > T ? T : x)); };
   auto bucket_of = [](int nch) { return nch <= 0 ? 0 : 32 - __clz(nch); };
   auto imax = [](int a, int b) { return a > b ? a : b; };
   auto iadd = [](int a, int b) { return a + b; };
-  // segments of a sequence of nch chunks (one when it is not cut)
-  auto nseg_of = [&](int nch) { return seg_len > 0 && nch > seg_len ? (nch + seg_len - 1) / seg_len : 1; };
+  auto nseg_of = [&](int nch) {
+    return seg_len > 0 && nch > seg_len ? (nch + seg_len - 1) / seg_len : 1;
+  };
+  auto unit = [](int seq, int c_begin, int c_end, int flags, int in_slot, int out_slot,
+                 int r_begin) {
+    Unit u;
+    u.seq = seq;
+    u.c_begin = c_begin;
+    u.c_end = c_end;
+    u.flags = flags;
+    u.in_slot = in_slot;
+    u.out_slot = out_slot;
+    u.r_begin = r_begin;
+    u.pad = 0;
+    return u;
+  };
   if (t == 0) {
     carry_max = clampT(cu[0]);
     carry_chunks = 0;
@@ -344,6 +398,7 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   }
   if (t < 33) bcount[t] = 0;
   __syncthreads();
+  // ---- per sequence: bounds, chunks, snapshot rows, start and map slots
   for (int base = 0; base < N; base += NTHREADS) {
     const int n = base + t;
     const int cm = carry_max, cc = carry_chunks, cs = carry_snaps;
@@ -358,12 +413,10 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const int first = cc + block_scan(nch, scratch, iadd) - nch;
     __syncthreads();
     const int sfirst = cs + block_scan(nsn, scratch, iadd) - nsn;
-    // start slots: one per segment after the first; maps: one per middle
-    // segment
     const int nseg = n < N ? nseg_of(nch) : 1;
     __syncthreads();
     const int stfirst = cst + block_scan(nseg - 1, scratch, iadd) - (nseg - 1);
-    const int nmap = nseg > 2 ? nseg - 2 : 0;
+    const int nmap = maps && nseg > 2 ? nseg - 2 : 0;
     __syncthreads();
     const int mfirst = cmp + block_scan(nmap, scratch, iadd) - nmap;
     if (n < N) {
@@ -377,22 +430,15 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
       e.pad0 = e.pad1 = 0;
       seqs[n] = e;
       atomicAdd(&bcount[bucket_of(nch)], 1);
-      // maps of the middle segments and the re-runs of the later ones
-      for (int p = 1; p < nseg; ++p) {
-        const int b0 = first + p * seg_len, b1 = min(first + (p + 1) * seg_len, first + nch);
-        Unit uc;
-        uc.seq = n;
-        uc.c_begin = b0;
-        uc.c_end = b1;
-        uc.flags = UNIT_FROM_START | (p == nseg - 1 ? UNIT_WRITE_HT : 0);
-        uc.slot = stfirst + p - 1;
-        uc.pad0 = uc.pad1 = uc.pad2 = 0;
-        units_c[stfirst + p - 1] = uc;
-        if (p < nseg - 1) {
-          Unit um = uc;
-          um.flags = 0;
-          um.slot = mfirst + p - 1;
-          units_m[mfirst + p - 1] = um;
+      if (maps) {
+        // the maps of the middle segments and the re-runs of the later ones
+        for (int p = 1; p < nseg; ++p) {
+          const int b0 = first + p * seg_len, b1 = min(first + (p + 1) * seg_len, first + nch);
+          units_c[stfirst + p - 1] = unit(n, b0, b1,
+                                          UNIT_FROM_START | (p == nseg - 1 ? UNIT_WRITE_HT : 0),
+                                          stfirst + p - 1, -1, p * seg_len);
+          if (p < nseg - 1)
+            units_m[mfirst + p - 1] = unit(n, b0, b1, 0, -1, mfirst + p - 1, p * seg_len);
         }
       }
     }
@@ -414,6 +460,46 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
   const int total = carry_chunks;  // <= ncb (see above)
   __threadfence_block();
   __syncthreads();
+  // ---- waves: segment p of every sequence, in wave-major table order
+  if (waves) {
+    if (t == 0) carry_wave = 0;
+    __syncthreads();
+    for (int p = 0; p < n_waves; ++p) {
+      if (t == 0) wave_off[p] = carry_wave;
+      for (int base = 0; base < N; base += NTHREADS) {
+        const int n = base + t;
+        const int cw = carry_wave;
+        SeqInfo e{};
+        int cnt = 0;
+        if (n < N) {
+          e = seqs[n];
+          const int nch = (e.hi - e.lo + C - 1) / C;
+          cnt = min(max(nch - p * seg_len, 0), seg_len);
+        }
+        __syncthreads();
+        const int off = cw + block_scan(cnt, scratch, iadd) - cnt;
+        if (n < N) {
+          const int nch = (e.hi - e.lo + C - 1) / C;
+          const int nseg = nseg_of(nch);
+          int flags = 0;
+          if (p < nseg)
+            flags = (p > 0 ? UNIT_FROM_START : 0) |
+                    (p < nseg - 1 ? UNIT_WRITE_NEXT : UNIT_WRITE_HT);
+          units_w[(size_t)p * N + n] =
+              unit(n, off, off + cnt, flags, e.start_slot + p - 1, e.start_slot + p, p * seg_len);
+        }
+        __syncthreads();
+        if (t == NTHREADS - 1) carry_wave = off + cnt;
+        __syncthreads();
+      }
+    }
+    if (t == 0) wave_off[n_waves] = carry_wave;
+    __threadfence_block();
+    __syncthreads();
+  } else if (t == 0) {
+    wave_off[0] = 0;
+    wave_off[1] = total;
+  }
   // Longest sequences first: units_a lists the sequences' first segments by
   // descending power-of-two bucket of their chunk count, so the state pass
   // starts the longest serial chains first.
@@ -429,20 +515,15 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     const SeqInfo e = seqs[n];
     const int nch = (e.hi - e.lo + C - 1) / C;
     const int pos = atomicAdd(&bbase[bucket_of(nch)], 1);
-    // the first (or only) segment of sequence n
+    // the first (or only) segment of sequence n, sequence-major
     const int nseg = nseg_of(nch);
-    Unit ua;
-    ua.seq = n;
-    ua.c_begin = e.chunk_first;
-    ua.c_end = e.chunk_first + (nseg > 1 ? seg_len : nch);
-    ua.flags = nseg > 1 ? UNIT_WRITE_NEXT : UNIT_WRITE_HT;
-    ua.slot = e.start_slot;
-    ua.pad0 = ua.pad1 = ua.pad2 = 0;
-    units_a[pos] = ua;
+    units_a[pos] = unit(n, e.chunk_first, e.chunk_first + (nseg > 1 ? seg_len : nch),
+                        nseg > 1 ? UNIT_WRITE_NEXT : UNIT_WRITE_HT, -1, e.start_slot, 0);
   }
-  // entry i belongs to the last sequence whose first chunk is <= i (a
-  // binary search over the monotone chunk_first; empty sequences share
-  // their successor's first chunk and lose the search)
+  // table entry i: sequence-major, entry i belongs to the last sequence
+  // whose first chunk is <= i; wave-major, to the last unit of its wave that
+  // begins at or before i (binary searches over monotone offsets: empty
+  // sequences or units share their successor's offset and lose them)
   for (int64_t i = t; i < ncb; i += NTHREADS) {
     ChunkEntry e;
     e.seq = 0;
@@ -450,14 +531,33 @@ __global__ __launch_bounds__(NTHREADS) void plan_kernel(
     e.len = 0;
     e.pad = 0;
     if (i < total) {
-      int a = 0, b = N - 1;  // last m with chunk_first <= i
-      while (a < b) {
-        const int m = (a + b + 1) >> 1;
-        if (seqs[m].chunk_first <= i) a = m; else b = m - 1;
+      int n, r;
+      if (waves) {
+        int a = 0, b = n_waves - 1;  // last wave p with wave_off[p] <= i
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (wave_off[m] <= i) a = m; else b = m - 1;
+        }
+        const Unit* U = units_w + (size_t)a * N;
+        int c = 0, d = N - 1;  // last n with U[n].c_begin <= i
+        while (c < d) {
+          const int m = (c + d + 1) >> 1;
+          if (U[m].c_begin <= i) c = m; else d = m - 1;
+        }
+        n = c;
+        r = U[c].r_begin + ((int)i - U[c].c_begin);
+      } else {
+        int a = 0, b = N - 1;  // last m with chunk_first <= i
+        while (a < b) {
+          const int m = (a + b + 1) >> 1;
+          if (seqs[m].chunk_first <= i) a = m; else b = m - 1;
+        }
+        n = a;
+        r = (int)i - seqs[a].chunk_first;
       }
-      const SeqInfo s = seqs[a];
-      e.seq = a;
-      e.start = s.lo + ((int)i - s.chunk_first) * C;
+      const SeqInfo s = seqs[n];
+      e.seq = n;
+      e.start = s.lo + r * C;
       e.len = (s.hi - e.start < C) ? s.hi - e.start : C;
     }
     table[i] = e;
@@ -591,7 +691,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
     const ChunkEntry* __restrict__ table, char* __restrict__ recs, int gate_mode,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound,
-    int HK, int per_head_gate, int qk_l2norm) {
+    int HK, int per_head_gate, int qk_l2norm, int ncb, const int* __restrict__ wave_off,
+    int wave) {
   typedef Geom<D, C> Gm;
   typedef IntraSmem<IO, D, C> Sm;
   constexpr int NT = NT_INTRA, NW = NT / 64;
@@ -613,12 +714,14 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   auto iP = [](int t, int c) { return t * D + c; };          // sG from step 5 (plain)
   auto iW = [](int r, int c) { return swz<D, 8>(r, c); };    // sW
 
-  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+  // the launch covers table entries wave_off[wave] .. wave_off[wave + 1] - 1
+  // (every entry without waves); blocks past them return
+  const int chunk = wave_off[wave] + (int)(blockIdx.x / H), h = blockIdx.x % H;
+  if (chunk >= wave_off[wave + 1]) return;
   const ChunkEntry ce = table[chunk];
   if (ce.len <= 0) return;
   const int L = ce.len;
   // records are head-major, so that one head's chain of chunks is contiguous
-  const int ncb = gridDim.x / H;
   char* rec = recs + ((size_t)h * ncb + chunk) * Gm::REC;
   // Record stores go through one buffer resource per tile: the lane's byte
   // offset is their only per-lane operand and stays in one register for the
@@ -1426,7 +1529,9 @@ __device__ __forceinline__ void state_unit(
   // uniform and the chunk table is read through scalar loads
   const int n = __builtin_amdgcn_readfirstlane(un.seq);
   const int flags = __builtin_amdgcn_readfirstlane(un.flags);
-  const int slot = __builtin_amdgcn_readfirstlane(un.slot);
+  const int in_slot = __builtin_amdgcn_readfirstlane(un.in_slot);
+  const int out_slot = __builtin_amdgcn_readfirstlane(un.out_slot);
+  if (!MAP && flags == 0) return;  // a wave this sequence does not reach
   const int tid = threadIdx.x, l = tid & 63, lg = l >> 4, lr = l & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   // When every wave owns a chunk row tile and the same number of state row
@@ -1447,7 +1552,7 @@ __device__ __forceinline__ void state_unit(
   const float* init = nullptr;
   if (!MAP) {
     if (flags & UNIT_FROM_START)
-      init = starts + ((size_t)slot * H + h) * D * D;
+      init = starts + ((size_t)in_slot * H + h) * D * D;
     else if (h0 != nullptr)
       init = h0 + ((size_t)n * H + h) * D * D;
   }
@@ -1475,7 +1580,9 @@ __device__ __forceinline__ void state_unit(
   const SeqInfo si = seqs[n];
   const int seq_start = __builtin_amdgcn_readfirstlane(si.lo);
   const int seq_end = __builtin_amdgcn_readfirstlane(si.hi);
-  const int c_first = __builtin_amdgcn_readfirstlane(si.chunk_first);
+  // chunk ch of the unit is chunk r_begin + (ch - c_begin) of its sequence
+  const int r_shift = __builtin_amdgcn_readfirstlane(un.r_begin) -
+                      __builtin_amdgcn_readfirstlane(un.c_begin);
   const int c_begin = __builtin_amdgcn_readfirstlane(un.c_begin);
   const int c_last = min(ncb, __builtin_amdgcn_readfirstlane(un.c_end));
   // snapshot rows of this sequence follow those of sequences 0 .. n-1
@@ -1681,7 +1788,7 @@ __device__ __forceinline__ void state_unit(
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int c_start = seq_start + (ch - c_first) * C;
+      const int c_start = seq_start + (ch + r_shift) * C;
       const int c_len = min(C, seq_end - c_start);
       constexpr int ROW16 = VT * (int)sizeof(IO) / 16;  // 16-byte pieces per row
 #pragma unroll
@@ -1697,7 +1804,7 @@ __device__ __forceinline__ void state_unit(
     // chunk-boundary snapshot: the state after this chunk, when the chunk
     // ends a whole multiple of snap_interval tokens into the sequence
     if (!MAP && snaps != nullptr) {
-      const int end_tok = (ch - c_first + 1) * C;
+      const int end_tok = (ch + r_shift + 1) * C;
       const int64_t row = (int64_t)snap_base + end_tok / snap_interval - 1;
       if (end_tok <= seq_end - seq_start && end_tok % snap_interval == 0 && row < snap_rows) {
         float* P = snaps + (row * H + h) * D * D;
@@ -1737,10 +1844,10 @@ __device__ __forceinline__ void state_unit(
   float* dst = nullptr;
   int ld = D;
   if (MAP) {
-    dst = maps + ((size_t)slot * H + h) * D * 2 * D;
+    dst = maps + ((size_t)out_slot * H + h) * D * 2 * D;
     ld = 2 * D;
   } else if (flags & UNIT_WRITE_NEXT) {
-    dst = starts + ((size_t)slot * H + h) * D * D;
+    dst = starts + ((size_t)out_slot * H + h) * D * D;
   } else if ((flags & UNIT_WRITE_HT) && ht != nullptr) {
     dst = ht + ((size_t)n * H + h) * D * D;
   }
@@ -1843,57 +1950,155 @@ __global__ __launch_bounds__(D) void scan_kernel(const SeqInfo* __restrict__ seq
 template <int D>
 constexpr int state_vt() { return D >= 32 ? 32 : D; }
 
+// The second stream of the wave schedule: one per device, created on first
+// use (non-blocking, default priority), with a pool of events.  Events are
+// only borrowed while a call enqueues its work: a wait binds to the record
+// that precedes it in enqueue order, so reusing an event in a later call
+// cannot disturb an earlier call's waits.
+struct AuxStream {
+  hipStream_t stream = nullptr;
+  std::vector<hipEvent_t> free_events;
+};
+constexpr int kMaxDevices = 64;
+std::mutex aux_mu;
+AuxStream aux_streams[kMaxDevices];
+
+hipError_t aux_acquire(int n_events, hipStream_t& aux, std::vector<hipEvent_t>& ev) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(aux_mu);
+  AuxStream& a = aux_streams[dev];
+  if (a.stream == nullptr &&
+      (e = hipStreamCreateWithFlags(&a.stream, hipStreamNonBlocking)) != hipSuccess)
+    return e;
+  aux = a.stream;
+  ev.clear();
+  while ((int)ev.size() < n_events) {
+    hipEvent_t x;
+    if (!a.free_events.empty()) {
+      x = a.free_events.back();
+      a.free_events.pop_back();
+    } else if ((e = hipEventCreateWithFlags(&x, hipEventDisableTiming)) != hipSuccess) {
+      for (hipEvent_t y : ev) a.free_events.push_back(y);
+      ev.clear();
+      return e;
+    }
+    ev.push_back(x);
+  }
+  return hipSuccess;
+}
+
+void aux_release(const std::vector<hipEvent_t>& ev) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lock(aux_mu);
+  for (hipEvent_t x : ev) aux_streams[dev].free_events.push_back(x);
+}
+
+// Stream of the caller's device: the aux stream must belong to the same
+// device as `st` (the current device); a stream of another device runs the
+// schedule on that one stream.
+bool stream_on_current_device(hipStream_t st) {
+  if (st == nullptr) return true;
+  int cur = 0;
+  hipDevice_t dev = 0;
+  return hipGetDevice(&cur) == hipSuccess && hipStreamGetDevice(st, &dev) == hipSuccess &&
+         dev == cur;
+}
+
 template <typename IO, int D, int C>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   typedef Geom<D, C> Gm;
   constexpr int VT = state_vt<D>();
   constexpr int NV = D / VT;
   const WsLayout ws = ws_layout(a.T, a.N, a.H, D, C, Gm::REC);
+  const StateCut& cut = ws.cut;
   char* base = reinterpret_cast<char*>(a.ws);
   ChunkEntry* table = reinterpret_cast<ChunkEntry*>(base + ws.table_off);
   SeqInfo* seqs = reinterpret_cast<SeqInfo*>(base + ws.seq_off);
   Unit* units_a = reinterpret_cast<Unit*>(base + ws.unit_a_off);
   Unit* units_m = reinterpret_cast<Unit*>(base + ws.unit_m_off);
   Unit* units_c = reinterpret_cast<Unit*>(base + ws.unit_c_off);
+  Unit* units_w = reinterpret_cast<Unit*>(base + ws.unit_w_off);
   int* counts = reinterpret_cast<int*>(base + ws.count_off);
+  int* wave_off = reinterpret_cast<int*>(base + ws.wave_off);
   char* recs = base + ws.rec_off;
   float* starts = reinterpret_cast<float*>(base + ws.start_off);
   float* maps = reinterpret_cast<float*>(base + ws.map_off);
   auto mark = [&](int i) -> hipError_t {
     return a.marks ? hipEventRecord((hipEvent_t)a.marks[i], st) : hipSuccess;
   };
+  auto intra = [&](int wave, int64_t chunks, hipStream_t s) {
+    if (a.T <= 0 || chunks <= 0) return;
+    auto k = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
+    hipLaunchKernelGGL(k, dim3((unsigned)(chunks * a.H)), dim3(NT_INTRA), 0, s, (const IO*)a.q,
+                       (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs,
+                       a.gate_mode, a.A_log, a.dt_bias, a.lower_bound,
+                       a.qk_heads > 0 ? a.qk_heads : a.H, a.per_head_gate, a.qk_l2norm,
+                       (int)ws.ncb, wave_off, wave);
+  };
+  // a state launch over `nu_max` units of `units` (count *n_units) and, in
+  // the first launch of a cut chain, the map units
+  auto state = [&](const Unit* units, const int* n_units, int nu_max, const Unit* mu,
+                   int nm_max) {
+    const int64_t blocks = (int64_t)(a.H * nu_max + 7) / 8 * 8 * NV +
+                           (int64_t)(a.H * nm_max + 7) / 8 * 8 * 2 * NV;
+    hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)blocks), dim3(NTHREADS), 0,
+                       st, seqs, units, n_units, nu_max, mu, counts + 1, recs, (int)ws.ncb, a.H,
+                       a.h0, a.ht, (IO*)a.o, a.snaps, a.snap_rows, a.snap_interval, starts, maps);
+  };
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(NTHREADS), 0, st, a.cu_seqlens, a.N, a.T, C,
-                     ws.ncb, a.snaps != nullptr ? a.snap_interval : 0, ws.seg_len, table, seqs,
-                     units_a, units_m, units_c, counts);
+                     ws.ncb, a.snaps != nullptr ? a.snap_interval : 0, cut.seg_len,
+                     cut.maps ? 1 : 0, cut.n_waves, table, seqs, units_a, units_m, units_c,
+                     units_w, counts, wave_off);
   if ((e = mark(1)) != hipSuccess) return e;
-  if (a.T > 0) {
-    auto intra = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
-    hipLaunchKernelGGL(intra, dim3((unsigned)(ws.ncb * a.H)),
-                       dim3(NT_INTRA), 0, st, (const IO*)a.q, (const IO*)a.k,
-                       (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs, a.gate_mode,
-                       a.A_log, a.dt_bias, a.lower_bound, a.qk_heads > 0 ? a.qk_heads : a.H,
-                       a.per_head_gate, a.qk_l2norm);
-  }
-  if ((e = mark(2)) != hipSuccess) return e;
-  // first segments (every sequence, longest first) and, with segments, the
-  // middle segments' maps in the same launch
-  const int64_t blocks_a = (int64_t)(a.H * a.N + 7) / 8 * 8 * NV +
-                           (int64_t)(a.H * ws.nseg + 7) / 8 * 8 * 2 * NV;
-  hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)blocks_a), dim3(NTHREADS), 0, st,
-                     seqs, units_a, counts + 0, a.N, ws.nseg > 0 ? units_m : nullptr, counts + 1,
-                     recs, (int)ws.ncb, a.H, a.h0, a.ht, (IO*)a.o, a.snaps, a.snap_rows,
-                     a.snap_interval, starts, maps);
-  if (ws.nseg > 0) {
-    // chain the start states, then re-run the later segments from them
-    hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)(a.N * a.H * (D / 4))), dim3(D), 0, st,
-                       seqs, a.N, a.H, C, ws.seg_len, maps, starts);
-    const int64_t blocks_c = (int64_t)(a.H * ws.nseg + 7) / 8 * 8 * NV;
-    hipLaunchKernelGGL((state_kernel<IO, D, C, VT>), dim3((unsigned)blocks_c), dim3(NTHREADS), 0,
-                       st, seqs, units_c, counts + 2, (int)ws.nseg, (const Unit*)nullptr,
-                       counts + 1, recs, (int)ws.ncb, a.H, a.h0, a.ht, (IO*)a.o, a.snaps,
-                       a.snap_rows, a.snap_interval, starts, maps);
+  if (cut.n_waves > 1) {
+    // waves: at most N segments of seg_len chunks each per wave
+    const int64_t wave_chunks = std::min<int64_t>(ws.ncb, (int64_t)a.N * cut.seg_len);
+    hipStream_t aux = nullptr;
+    std::vector<hipEvent_t> ev;
+    const bool two = !a.single_stream && stream_on_current_device(st) &&
+                     aux_acquire(cut.n_waves + 1, aux, ev) == hipSuccess;
+    if (two) {
+      // wave p's intra-chunk work on the second stream, its state pass on
+      // the caller's stream once that is done
+      if ((e = hipEventRecord(ev[cut.n_waves], st)) == hipSuccess &&
+          (e = hipStreamWaitEvent(aux, ev[cut.n_waves], 0)) == hipSuccess) {
+        for (int p = 0; p < cut.n_waves && e == hipSuccess; ++p) {
+          intra(p, wave_chunks, aux);
+          e = hipEventRecord(ev[p], aux);
+        }
+        if (e == hipSuccess && (e = mark(2)) == hipSuccess) {
+          for (int p = 0; p < cut.n_waves && e == hipSuccess; ++p) {
+            if ((e = hipStreamWaitEvent(st, ev[p], 0)) == hipSuccess)
+              state(units_w + (size_t)p * a.N, counts + 0, a.N, nullptr, 0);
+          }
+        }
+      }
+      aux_release(ev);
+      if (e != hipSuccess) return e;
+    } else {
+      for (int p = 0; p < cut.n_waves; ++p) intra(p, wave_chunks, st);
+      if ((e = mark(2)) != hipSuccess) return e;
+      for (int p = 0; p < cut.n_waves; ++p)
+        state(units_w + (size_t)p * a.N, counts + 0, a.N, nullptr, 0);
+    }
+  } else {
+    intra(0, ws.ncb, st);
+    if ((e = mark(2)) != hipSuccess) return e;
+    // first segments (every sequence, longest first) and, with maps, the
+    // middle segments' maps in the same launch
+    state(units_a, counts + 0, a.N, cut.maps ? units_m : nullptr, cut.maps ? (int)ws.nseg : 0);
+    if (cut.maps) {
+      // chain the start states, then re-run the later segments from them
+      hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)(a.N * a.H * (D / 4))), dim3(D), 0, st,
+                         seqs, a.N, a.H, C, cut.seg_len, maps, starts);
+      state(units_c, counts + 2, (int)ws.nseg, nullptr, 0);
+    }
   }
   if ((e = mark(3)) != hipSuccess) return e;
   return hipGetLastError();

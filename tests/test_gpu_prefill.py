@@ -79,8 +79,10 @@ def test_varlen_workload(regime):
 
 
 def test_long_workload_segments_vs_full_vs_oracle():
-    """65536 tokens: 16 carried segments of 4096 equal one full run, and
-    both equal the oracle (sampled heads)."""
+    """65536 tokens: 16 carried segments of 4096 equal one full run bit for
+    bit (the full run's state pass is cut into waves that hand the state on
+    exactly, the 4096-token calls likewise), and both match the oracle
+    (sampled heads)."""
     w = kda_synth.WORKLOADS["long_prefill_65536"]
     c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"],
                                seed=w["seed"], regime="long",
@@ -107,8 +109,9 @@ def test_long_workload_segments_vs_full_vs_oracle():
     sub = lambda x: np.ascontiguousarray(x[:, heads])
     o_ref, ht_ref = oracle.prefill(sub(c["q"]), sub(c["k"]), sub(c["v"]), sub(g),
                                    sub(beta), c["cu"], scale, sub(c["h0"]))
-    assert_io_output(host(o_full)[:, heads], o_ref, "bf16", 1)
-    assert rel_err_blocks(host(ht_full)[:, heads], ht_ref, 2) <= TOL["bf16"]
+    for o_, ht_ in ((o_full, ht_full), (o_seg, state)):
+        assert_io_output(host(o_)[:, heads], o_ref, "bf16", 1)
+        assert rel_err_blocks(host(ht_)[:, heads], ht_ref, 2) <= TOL["bf16"]
 
 
 # ---------------------------------------------------------- shapes, edges
@@ -280,3 +283,39 @@ def test_malformed_cu_seqlens_stay_in_bounds(cu_bad, T):
     o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, p, 0.125, c["h0"])
     assert_io_output(host(outs[1][0]), o_ref, "bf16", 1)
     assert rel_err_blocks(host(outs[1][1]), ht_ref, 2) <= TOL["bf16"]
+
+
+def test_wave_schedule_equals_single_stream_and_oracle():
+    """A batch whose longest possible chain has at least 32 chunks runs its
+    state pass in waves, the intra-chunk work of each wave on a second
+    stream: the results equal the single-stream order (the timing-marks call
+    runs every kernel on one stream) bit for bit, with and without the gate
+    in the kernel and with snapshots, and match the oracle."""
+    seqlens = [3000, 50, 1200, 0]
+    c = kda_synth.prefill_case(seqlens, 32, 64, 64, "bf16", seed=51, regime="long", h0_std=0.05)
+    t, g, beta = _inputs(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    A_log, dt_bias = dev(c["A_log"]), dev(c["dt_bias"])
+    o1, ht1 = kda.kda_chunk_prefill_gated(t["q"], t["k"], t["v"], a, b, A_log, dt_bias, t["cu"],
+                                          0.125, h0=t["h0"], chunk=64)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    o2, ht2 = kda.kda_chunk_prefill_marked(marks, t["q"], t["k"], t["v"], a, b, A_log, dt_bias,
+                                           t["cu"], 0.125, h0=t["h0"], chunk=64)
+    o3, ht3, snaps = kda.kda_chunk_prefill_snapshots(t["q"], t["k"], t["v"], t["g"], t["beta"],
+                                                     t["cu"], 0.125, 256, h0=t["h0"], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+    heads = [0, 17, 31]
+    sub = lambda x: None if x is None else np.ascontiguousarray(x[:, heads])
+    o_ref, ht_ref = oracle.prefill(sub(c["q"]), sub(c["k"]), sub(c["v"]), sub(g), sub(beta),
+                                   c["cu"], 0.125, sub(c["h0"]))
+    assert_io_output(host(o3)[:, heads], o_ref, "bf16", 1)
+    assert rel_err_blocks(host(ht3)[:, heads], ht_ref, 2) <= TOL["bf16"]
+    # a snapshot deep in the first sequence (in a later wave): the final
+    # state of a prefill of that prefix alone
+    L = 256 * 9
+    cu1 = torch.tensor([0, L], dtype=torch.int32, device="cuda")
+    _, ht_pre = kda.kda_chunk_prefill(t["q"][:L], t["k"][:L], t["v"][:L], t["g"][:L],
+                                      t["beta"][:L], cu1, 0.125, h0=t["h0"][:1], chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(snaps[8], ht_pre[0])
