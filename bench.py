@@ -237,8 +237,13 @@ def _stats(ms):
 
 
 def bench_prefill_workload(name, steps, warmup, seqlens=None, H=None, keep_inputs=False):
-    """Gate + prefill (kda_chunk_prefill_marked: the gated call with events
-    between its stages) as K cache-cold single calls."""
+    """Gate + prefill as K cache-cold single calls of kda_chunk_prefill_gated
+    (the step: with long chains the library overlaps the intra-chunk kernel
+    of one wave of chunks with the state pass of the previous one, on a
+    second stream).  The per-stage durations come from a further set of
+    cache-cold calls of kda_chunk_prefill_marked, which runs the same kernels
+    with the same plan on the caller's stream alone, stage after stage, with
+    events between the stages."""
     w, c, t = prefill_setup(name, seqlens, H)
     T, N, H, K, V, C = c["T"], c["N"], w["H"], w["K"], w["V"], w["chunk"]
     scale = K ** -0.5
@@ -246,16 +251,21 @@ def bench_prefill_workload(name, steps, warmup, seqlens=None, H=None, keep_input
     ht = torch.empty_like(t["h0"])
     ws = torch.empty(kda.kda_chunk_prefill_workspace_size(T, N, H, K, V, C),
                      dtype=torch.uint8, device="cuda")
+    args = (t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"], t["dt_bias"], t["cu"], scale)
+    kw = dict(h0=t["h0"], chunk=C, o=o, ht=ht, workspace=ws)
 
-    def step(marks):
-        kda.kda_chunk_prefill_marked(marks, t["q"], t["k"], t["v"], t["a"], t["b"], t["A_log"],
-                                     t["dt_bias"], t["cu"], scale, h0=t["h0"], chunk=C, o=o,
-                                     ht=ht, workspace=ws)
+    def step(_):
+        kda.kda_chunk_prefill_gated(*args, **kw)
 
-    calls, parts = time_steps(step, steps, warmup, nmarks=4)
+    def marked(marks):
+        kda.kda_chunk_prefill_marked(marks, *args, **kw)
+
+    calls, _ = time_steps(step, steps, warmup)
+    single, parts = time_steps(marked, max(10, steps // 2), 2, nmarks=4)
     names = ("plan", "intra", "state")
     kernel_ms = {n: float(np.mean([p[i] for p in parts])) for i, n in enumerate(names)}
     r = dict(workload=w, T=T, N=N, H=H, **_stats(calls), kernel_ms=kernel_ms,
+             single_stream_ms=float(np.median(single)),
              prefill_bytes=prefill_bytes(T, N, H, K, V), intra_bytes=intra_bytes(T, H, K, V),
              state_bytes=state_bytes(T, N, H, K, V), flops=prefill_flops(T, H, K, V, C))
     r["tokens_per_s"] = T / (r["ms_median"] * 1e-3)
@@ -627,7 +637,10 @@ def _prefill_entry(r, what):
     w = r["workload"]
     out = {"workload": what, "tokens_per_s": r["tokens_per_s"], "ms": r["ms_median"],
            "ms_min": r["ms_min"], "ms_mean": r["ms_mean"], "reps": r["reps"],
-           "kernel_ms": r["kernel_ms"], "algorithmic_bytes": r["prefill_bytes"],
+           "kernel_ms": r["kernel_ms"], "single_stream_ms": r["single_stream_ms"],
+           "kernel_ms_from": "kda_chunk_prefill_marked: the same kernels on one stream, "
+                             "stage after stage, events between the stages",
+           "algorithmic_bytes": r["prefill_bytes"],
            "gbs": r["prefill_bytes"] / (r["ms_median"] * 1e-3) / 1e9,
            "algorithmic_flops": r["flops"],
            "tflops": r["flops"] / (r["ms_median"] * 1e-3) / 1e12}

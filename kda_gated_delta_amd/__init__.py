@@ -24,6 +24,13 @@ _IO = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 _lib = None
 
 
+class PrefillSchedule(ctypes.Structure):
+    """kda_prefill_schedule of include/kda_profile.h."""
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_waves", "segment_chunks", "uses_maps",
+                                               "intra_launches", "state_launches",
+                                               "other_launches")]
+
+
 class PrefillOpts(ctypes.Structure):
     """kda_prefill_opts of include/kda.h (model-layer options of prefill)."""
     _fields_ = [("gate_mode", ctypes.c_int32), ("A_log", ctypes.c_void_p),
@@ -103,6 +110,9 @@ def lib() -> ctypes.CDLL:
     L.kda_replay_decode_ex.argtypes = L.kda_replay_decode.argtypes[:-1] + [
         ctypes.POINTER(StepOpts), vp]
     L.kda_replay_decode_ex.restype = ctypes.c_int
+    L.kda_chunk_prefill_schedule.argtypes = [i64, i32, i32, i32, i32, i32,
+                                             ctypes.POINTER(PrefillSchedule)]
+    L.kda_chunk_prefill_schedule.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -113,7 +123,7 @@ EXPORTED = ("kda_status_string", "kda_gate_prep", "kda_chunk_prefill_workspace_s
             "kda_chunk_prefill_snapshots",
             "kda_recurrent_decode", "kda_verify", "kda_replay_decode",
             "kda_recurrent_decode_ex", "kda_verify_ex", "kda_chunk_prefill_ex",
-            "kda_replay_decode_ex", "kda_chunk_prefill_noalloc")
+            "kda_replay_decode_ex", "kda_chunk_prefill_noalloc", "kda_chunk_prefill_schedule")
 
 # Bytes of the static scratch array behind kda_chunk_prefill_noalloc
 # (KDA_NOALLOC_SCRATCH_BYTES of include/kda.h).
@@ -183,6 +193,17 @@ def kda_chunk_prefill_workspace_size(T: int, N: int, H: int, K: int, V: int,
     _check("kda_chunk_prefill_workspace_size",
            lib().kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk, ctypes.byref(n)))
     return int(n.value)
+
+
+def kda_chunk_prefill_schedule(T: int, N: int, H: int, K: int, V: int,
+                               chunk: int = 64) -> dict:
+    """Kernels a prefill call of these sizes launches (include/kda_profile.h):
+    n_waves, segment_chunks, uses_maps, intra_launches, state_launches,
+    other_launches."""
+    out = PrefillSchedule()
+    _check("kda_chunk_prefill_schedule",
+           lib().kda_chunk_prefill_schedule(T, N, H, K, V, chunk, ctypes.byref(out)))
+    return {name: int(getattr(out, name)) for name, _ in PrefillSchedule._fields_}
 
 
 def kda_chunk_prefill(q, k, v, g, beta, cu_seqlens, scale: float, h0=None,

@@ -248,6 +248,18 @@ kda_status kda_chunk_prefill_workspace_size(int64_t T, int32_t N, int32_t H,
   return KDA_OK;
 }
 
+kda_status kda_chunk_prefill_schedule(int64_t T, int32_t N, int32_t H, int32_t K, int32_t V,
+                                      int32_t chunk, kda_prefill_schedule* out) {
+  size_t bytes = 0;
+  const kda_status st = kda_chunk_prefill_workspace_size(T, N, H, K, V, chunk, &bytes);
+  if (st != KDA_OK) return st;
+  if (!out) return KDA_ERR_INVALID_ARGUMENT;
+  int s[6];
+  kda::prefill_schedule(T, N, H, K, chunk, s);
+  *out = kda_prefill_schedule{s[0], s[1], s[2], s[3], s[4], s[5]};
+  return KDA_OK;
+}
+
 kda_status kda_chunk_prefill(kda_dtype io, const void* q, const void* k,
                              const void* v, const float* g, const float* beta,
                              const int32_t* cu_seqlens, int32_t N, int64_t T,

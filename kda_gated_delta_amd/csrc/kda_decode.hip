@@ -265,8 +265,9 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void decode_ke
   for (int i = 0; i < Sh::RPT; ++i) store4_nt(S + (rg + Sh::RG * i) * V + c0, s[i]);
 }
 
-// Draft tokens are staged TVB at a time.
-constexpr int TVB = 4;
+// Draft tokens are staged TVB at a time: q, k, exp(g), beta and v of a batch
+// go to LDS before its first token, so the token steps issue no loads.
+constexpr int TVB = 8;
 
 template <typename IO, int K, int V>
 __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_kernel(
@@ -278,13 +279,15 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
   constexpr int VS = slice_cols<V>(), NS = V / VS;
   typedef StepShape<K, VS> Sh;
   __shared__ float sq[TVB][K], sk[TVB][K], sa[TVB][K], sb[TVB];
+  __shared__ __align__(16) float sv[TVB][VS];
   __shared__ float sqn[TVB], skn[TVB];
   __shared__ __align__(16) float sout[TVB][V];
   __shared__ float red[2][Sh::RED];
   const int t = threadIdx.x, cg = t % Sh::CG, rg = t / Sh::CG;
   const int rh = blockIdx.x / NS;  // r * H + h
   const int r = rh / H, h = rh % H;
-  const int c0 = (blockIdx.x % NS) * VS + 4 * cg;  // this thread's first state column
+  const int v0 = (blockIdx.x % NS) * VS;  // first state column of the workgroup
+  const int c0 = v0 + 4 * cg;             // this thread's first state column
   const int64_t slot = slot_idx[r];
   if (slot < 0 || slot >= n_slots) {
     // padding row: o = 0; a slot past the pool: o = NaN.  inter stays unwritten.
@@ -320,17 +323,23 @@ __global__ __launch_bounds__((StepShape<K, slice_cols<V>()>::NT)) void verify_ke
       sk[j][c] = to_f32(k[qrow * K + c]) * kn;
       sa[j][c] = expf(decay_of(g, row, c, K, h, op));
     }
+    for (int e = t; e < nb * VS; e += Sh::NT) {
+      const int j = e / VS, c = e % VS;
+      sv[j][c] = to_f32(v[(((int64_t)r * Tv + s0 + j) * H + h) * V + v0 + c]);
+    }
     if (t < nb) sb[t] = strength_of(beta[((int64_t)r * Tv + s0 + t) * H + h], op);
-    float4 vv[TVB];
-#pragma unroll
-    for (int j = 0; j < TVB; ++j)
-      if (j < nb) vv[j] = load4(v + (((int64_t)r * Tv + s0 + j) * H + h) * V + c0);
     __syncthreads();
+    // Every load of the batch (and the initial state) has landed here.  The
+    // explicit wait keeps the compiler from waiting inside the token steps,
+    // where stores are in flight and any wait on the memory counter would
+    // also wait for them.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 #pragma unroll
     for (int j = 0; j < TVB; ++j) {
       if (j < nb) {
         const int64_t rsh = ((int64_t)r * Tv + s0 + j) * H + h;
-        const float4 oq = token_step<K, VS>(st, sq[j], sk[j], sa[j], vv[j], sb[j],
+        const float4 vv = *reinterpret_cast<const float4*>(&sv[j][4 * cg]);
+        const float4 oq = token_step<K, VS>(st, sq[j], sk[j], sa[j], vv, sb[j],
                                             red[step & 1]);
         ++step;
         if (rg == 0) {

@@ -105,5 +105,8 @@ hipError_t run_verify(const DecodeArgs& a, hipStream_t stream);
 hipError_t run_replay(const ReplayArgs& a, hipStream_t stream);
 hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream);
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C);
+// Schedule of a prefill call: {n_waves, segment chunks, maps, intra launches,
+// state launches, other launches}.
+void prefill_schedule(int64_t T, int N, int H, int K, int C, int out[6]);
 
 }  // namespace kda

@@ -682,14 +682,15 @@ __device__ __forceinline__ void butterfly_step(float (&v)[16], int upper) {
 // LDS use (bf16 io, C = 64, D = 128: 80 KB, two workgroups per CU): see
 // IntraSmem.  Every input is staged once; the work units read their rows
 // from LDS into registers and take reference rows by lane broadcast.
-// GATED: the instance that applies the gate to raw inputs (gate_mode 1 or
-// 2); the other one is compiled without the gate code, and the two show up
-// as separate kernels in a profile.
-template <typename IO, int D, int C, bool GATED>
+// GATE: the gate form compiled into the instance: 0 = g and beta are given,
+// 1 = softplus gate, 2 = safe gate applied to the raw inputs (one form per
+// instance, so that no instance carries another's code; the three show up as
+// separate kernels in a profile).
+template <typename IO, int D, int C, int GATE>
 __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     const IO* __restrict__ q, const IO* __restrict__ k, const IO* __restrict__ v,
     const float* __restrict__ g, const float* __restrict__ beta, int H, float scale,
-    const ChunkEntry* __restrict__ table, char* __restrict__ recs, int gate_mode,
+    const ChunkEntry* __restrict__ table, char* __restrict__ recs,
     const float* __restrict__ A_log, const float* __restrict__ dt_bias, float lower_bound,
     int HK, int per_head_gate, int qk_l2norm, int ncb, const int* __restrict__ wave_off,
     int wave) {
@@ -755,7 +756,7 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
     return buffer_rsrc(static_cast<const char*>(base) + ((size_t)ce.start * HK + hk) * D * esz,
                        (uint32_t)L * (uint32_t)(HK * D * esz));
   };
-  if (!GATED) gate_mode = 0;
+  constexpr int gate_mode = GATE;
   // gate_mode 0: g and beta are given.  1 (softplus gate) and 2 (safe gate):
   // g and beta hold the raw inputs a and b, activated here with the gate
   // kernel's own functions (the same values it would have written); beta is
@@ -835,12 +836,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
       for (int i = 0; i < RPT; ++i) {
         const float4 x = gg[i] + db;
         float4 y;
-        if (gate_mode == 2)
-          y = make_float4(gate1<true>(x.x, rate, lower_bound), gate1<true>(x.y, rate, lower_bound),
-                          gate1<true>(x.z, rate, lower_bound), gate1<true>(x.w, rate, lower_bound));
-        else
-          y = make_float4(gate1<false>(x.x, rate, lower_bound), gate1<false>(x.y, rate, lower_bound),
-                          gate1<false>(x.z, rate, lower_bound), gate1<false>(x.w, rate, lower_bound));
+        constexpr bool SAFE = GATE == 2;
+        y = make_float4(gate1<SAFE>(x.x, rate, lower_bound), gate1<SAFE>(x.y, rate, lower_bound),
+                        gate1<SAFE>(x.z, rate, lower_bound), gate1<SAFE>(x.w, rate, lower_bound));
         gg[i] = grp * RPT + i < L ? y : f4(0.f);  // rows past the sequence keep g = 0
       }
     }
@@ -2032,10 +2030,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   };
   auto intra = [&](int wave, int64_t chunks, hipStream_t s) {
     if (a.T <= 0 || chunks <= 0) return;
-    auto k = a.gate_mode != 0 ? intra_kernel<IO, D, C, true> : intra_kernel<IO, D, C, false>;
+    auto k = a.gate_mode == 2   ? intra_kernel<IO, D, C, 2>
+             : a.gate_mode == 1 ? intra_kernel<IO, D, C, 1>
+                                : intra_kernel<IO, D, C, 0>;
     hipLaunchKernelGGL(k, dim3((unsigned)(chunks * a.H)), dim3(NT_INTRA), 0, s, (const IO*)a.q,
                        (const IO*)a.k, (const IO*)a.v, a.g, a.beta, a.H, a.scale, table, recs,
-                       a.gate_mode, a.A_log, a.dt_bias, a.lower_bound,
+                       a.A_log, a.dt_bias, a.lower_bound,
                        a.qk_heads > 0 ? a.qk_heads : a.H, a.per_head_gate, a.qk_l2norm,
                        (int)ws.ncb, wave_off, wave);
   };
@@ -2130,6 +2130,17 @@ hipError_t prefill_d(const PrefillArgs& a, hipStream_t st) {
 size_t prefill_workspace_bytes(int64_t T, int N, int H, int K, int V, int C) {
   (void)V;
   return ws_layout(T, N, H, K, C, rec_bytes(K, C)).total;
+}
+
+void prefill_schedule(int64_t T, int N, int H, int K, int C, int out[6]) {
+  const StateCut cut = state_cut(T, N, H, K, C);
+  const bool any = T > 0;
+  out[0] = cut.n_waves;
+  out[1] = cut.seg_len;
+  out[2] = cut.maps ? 1 : 0;
+  out[3] = any ? cut.n_waves : 0;
+  out[4] = cut.maps ? 2 : cut.n_waves;
+  out[5] = cut.maps ? 2 : 1;
 }
 
 hipError_t run_prefill(const PrefillArgs& a, hipStream_t stream) {

@@ -287,3 +287,28 @@ def test_noalloc_prefill_validation():
     assert call(T=1 << 20, H=32) == SCRATCH_LIMIT
     ws = kda.kda_chunk_prefill_workspace_size(8192, 1, 32, 128, 128, 64)
     assert ws > kda.NOALLOC_SCRATCH_BYTES and call(T=8192, H=32) == SCRATCH_LIMIT
+
+
+def test_prefill_schedule():
+    L = kda.lib()
+    out = kda.PrefillSchedule()
+    assert L.kda_chunk_prefill_schedule(4096, 1, 4, 128, 128, 64, None) == INVALID
+    assert L.kda_chunk_prefill_schedule(4096, 1, 4, 128, 64, 64, ctypes.byref(out)) == UNSUPPORTED
+    assert L.kda_chunk_prefill_schedule(4096, 0, 4, 128, 128, 64, ctypes.byref(out)) == INVALID
+    # a short batch: one launch of each kernel, chain not cut
+    s = kda.kda_chunk_prefill_schedule(7680, 4, 32, 128, 128, 64)
+    assert s == dict(n_waves=1, segment_chunks=0, uses_maps=0, intra_launches=1,
+                     state_launches=1, other_launches=1)
+    # empty input: the chunk table and state pass still run (ht = h0)
+    s = kda.kda_chunk_prefill_schedule(0, 1, 4, 128, 128, 64)
+    assert s["intra_launches"] == 0 and s["state_launches"] == 1
+    # a long chain is cut: waves or maps, with launch counts to match
+    for H in (4, 32):
+        s = kda.kda_chunk_prefill_schedule(65536, 1, H, 128, 128, 64)
+        assert s["segment_chunks"] > 0
+        if s["uses_maps"]:
+            assert s["n_waves"] == 1 and s["state_launches"] == 2 and s["other_launches"] == 2
+        else:
+            assert s["n_waves"] > 1
+            assert s["intra_launches"] == s["state_launches"] == s["n_waves"]
+            assert s["n_waves"] * s["segment_chunks"] >= 1024
