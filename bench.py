@@ -74,21 +74,41 @@ def _time(fn, steps: int, warmup: int, settle_s: float | None = None) -> float:
     return e0.elapsed_time(e1) / steps
 
 
+def _time_rotating(fns, steps: int, warmup: int) -> float:
+    """Mean milliseconds per call of a steady stream of calls that cycles
+    over `fns`, one callable per private copy of a workload's buffers, the
+    copies together several times larger than the last-level cache: each call
+    finds none of its inputs cached (the calls in between moved far more
+    bytes than the cache holds), and each call's write-backs of dirty lines
+    fall inside the timed stream (in the next call) instead of after it, as
+    they would after a single timed call with write-back stores."""
+    n = len(fns)
+    for i in range(max(warmup, n)):
+        fns[i % n]()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < SETTLE_S:  # clocks up from idle
+        fns[i % n]()
+        i += 1
+        torch.cuda.synchronize()
+    steps = max(steps, 4 * n)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for j in range(steps):
+        fns[(i + j) % n]()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+ROTATE_SETS = 4  # private buffer copies per decode-family workload
+
+
 # ------------------------------------------------------------ byte models
 
 _FLUSH = None
-
-
-def _fresh_memory():
-    """Returns torch's cached device blocks to the driver before a workload
-    allocates its own buffers, so that each workload's buffers are fresh
-    allocations.  Without it, a buffered-decode run that followed the other
-    workloads in one process, on a GPU that other processes had just used,
-    was measured 7-8x slower (0.84-0.90 ms against 0.112 ms in every other
-    arrangement) with unchanged kernels: the timing of its scattered
-    per-slot reads depended on where the allocation history put them."""
-    torch.cuda.synchronize()
-    torch.cuda.empty_cache()
 
 
 def _time_flushed(fn, reps: int = 20) -> float:
@@ -338,24 +358,35 @@ def bench_gate_and_snapshots(steps, warmup):
 
 
 def bench_decode(steps, warmup):
+    """kda_recurrent_decode on decode_256: `ms` over a steady stream of calls
+    rotating over ROTATE_SETS private copies of the buffers (cold inputs,
+    write-backs paid); `ms_flushed` the median of single calls after emptying
+    the cache; `ms_b2b` the same buffers back to back."""
     w = kda_synth.WORKLOADS["decode_256"]
     c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
                               seed=w["seed"], dt_bias_std=w["dt_bias_std"],
                               state_std=w["state_std"])
-    a, b = _dev(c["a"]), _dev(c["b"])
-    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
-    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
-    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
-    o = torch.empty_like(v)
-    fn = lambda: kda.kda_recurrent_decode(q, k, v, g, beta, w["K"] ** -0.5, pool, idx, o=o)
-    ms = _time(fn, max(steps, 20), warmup)
-    ms_flushed = _time_flushed(fn)
     B, H, K, V = w["B"], w["H"], w["K"], w["V"]
+
+    def make(_):
+        a, b = _dev(c["a"]), _dev(c["b"])
+        g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+        q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+        pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+        o = torch.empty_like(v)
+        return lambda: kda.kda_recurrent_decode(q, k, v, g, beta, K ** -0.5, pool, idx, o=o)
+
+    fns = [make(i) for i in range(ROTATE_SETS)]
+    ms = _time_rotating(fns, steps, warmup)
+    ms_flushed = _time_flushed(fns[0])
+    ms_b2b = _time(fns[0], max(steps, 20), warmup)
     nbytes = decode_bytes(B, H, K, V)
     state = 2 * B * H * K * V * 4
+    del fns
     return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes,
                 gbs=nbytes / (ms * 1e-3) / 1e9, state_gbs=state / (ms * 1e-3) / 1e9,
-                ms_flushed=ms_flushed, gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9)
+                ms_flushed=ms_flushed, gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9,
+                ms_b2b=ms_b2b, gbs_b2b=nbytes / (ms_b2b * 1e-3) / 1e9)
 
 
 def bench_decode_layer(steps, warmup):
@@ -384,61 +415,80 @@ def bench_decode_layer(steps, warmup):
 def bench_replay(steps, warmup, L=16):
     """kda_replay_decode on the decode_256 shapes with a ring of L: cursors
     staggered over the rows (row r at r % L, so 1/L of the rows write their
-    checkpoint per call), rings filled by L earlier calls."""
+    checkpoint per call), rings filled by L earlier calls.  Timed as
+    bench_decode (rotating copies, cache-cold single calls, back to back)."""
     w = kda_synth.WORKLOADS["decode_256"]
     c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
                               seed=w["seed"], dt_bias_std=w["dt_bias_std"],
                               state_std=w["state_std"])
     B, H, K, V = w["B"], w["H"], w["K"], w["V"]
-    a, b = _dev(c["a"]), _dev(c["b"])
-    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
-    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
-    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
     n = w["n_slots"]
-    ring_d = torch.zeros((n, H, L, V), device="cuda")
-    ring_k = torch.zeros((n, H, L, K), dtype=torch.bfloat16, device="cuda")
-    ring_g = torch.zeros((n, H, L, K), device="cuda")
-    o = torch.empty_like(v)
-    rows = torch.arange(B, device="cuda", dtype=torch.int32)
-    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
-    nxt = torch.empty_like(pos)
-    for s in range(L):  # row r first writes its checkpoint at call r % L
-        force = ((rows % L) == s).to(torch.int32)
-        kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d, ring_k,
-                              ring_g, force_flush=force, o=o, next_write_pos=nxt)
-        pos, nxt = nxt, pos
-    wp = pos.cpu().numpy()
-    fn = lambda: kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d,
-                                       ring_k, ring_g, o=o, next_write_pos=nxt)
-    ms = _time(fn, max(steps, 20), warmup)
-    ms_flushed = _time_flushed(fn)
+    wps = []
+
+    def make(_):
+        a, b = _dev(c["a"]), _dev(c["b"])
+        g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+        q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+        pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+        ring_d = torch.zeros((n, H, L, V), device="cuda")
+        ring_k = torch.zeros((n, H, L, K), dtype=torch.bfloat16, device="cuda")
+        ring_g = torch.zeros((n, H, L, K), device="cuda")
+        o = torch.empty_like(v)
+        rows = torch.arange(B, device="cuda", dtype=torch.int32)
+        pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+        nxt = torch.empty_like(pos)
+        for s in range(L):  # row r first writes its checkpoint at call r % L
+            force = ((rows % L) == s).to(torch.int32)
+            kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d, ring_k,
+                                  ring_g, force_flush=force, o=o, next_write_pos=nxt)
+            pos, nxt = nxt, pos
+        wps.append(pos.cpu().numpy())
+        return lambda: kda.kda_replay_decode(q, k, v, g, beta, K ** -0.5, pool, idx, pos, ring_d,
+                                             ring_k, ring_g, o=o, next_write_pos=nxt)
+
+    fns = [make(i) for i in range(ROTATE_SETS)]
+    ms = _time_rotating(fns, steps, warmup)
+    ms_flushed = _time_flushed(fns[0])
+    ms_b2b = _time(fns[0], max(steps, 20), warmup)
+    wp = wps[0]
     nbytes = replay_bytes(wp, wp == L - 1, H, K, V)
+    del fns
     return dict(ms=ms, tokens_per_s=B / (ms * 1e-3), bytes=nbytes, L=L,
                 mean_ring_entries=float(wp.mean()), flush_frac=float((wp == L - 1).mean()),
                 gbs=nbytes / (ms * 1e-3) / 1e9, ms_flushed=ms_flushed,
-                gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9)
+                gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9, ms_b2b=ms_b2b,
+                gbs_b2b=nbytes / (ms_b2b * 1e-3) / 1e9)
 
 
 def bench_verify(steps, warmup):
+    """kda_verify on verify_64x8, timed as bench_decode."""
     w = kda_synth.WORKLOADS["verify_64x8"]
     c = kda_synth.decode_case(w["B"], w["H"], w["K"], w["V"], w["n_slots"], w["io"],
                               seed=w["seed"], dt_bias_std=w["dt_bias_std"],
                               state_std=w["state_std"], Tv=w["Tv"])
     B, Tv, H, K, V = w["B"], w["Tv"], w["H"], w["K"], w["V"]
-    a, b = _dev(c["a"]).reshape(B * Tv, H, K), _dev(c["b"]).reshape(B * Tv, H)
-    g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
-    g, beta = g.reshape(B, Tv, H, K), beta.reshape(B, Tv, H)
-    q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
-    pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
-    inter = torch.empty((B, Tv, H, K, V), device="cuda")
-    o = torch.empty_like(v)
-    fn = lambda: kda.kda_verify(q, k, v, g, beta, K ** -0.5, pool, idx, inter_states=inter, o=o)
-    ms = _time(fn, max(steps, 20), warmup)
-    ms_flushed = _time_flushed(fn)
+
+    def make(_):
+        a, b = _dev(c["a"]).reshape(B * Tv, H, K), _dev(c["b"]).reshape(B * Tv, H)
+        g, beta = kda.kda_gate_prep(a, b, _dev(c["A_log"]), _dev(c["dt_bias"]))
+        g, beta = g.reshape(B, Tv, H, K), beta.reshape(B, Tv, H)
+        q, k, v = (_dev(c[x], torch.bfloat16) for x in "qkv")
+        pool, idx = _dev(c["pool"]), _dev(c["slot_idx"], torch.int32)
+        inter = torch.empty((B, Tv, H, K, V), device="cuda")
+        o = torch.empty_like(v)
+        return lambda: kda.kda_verify(q, k, v, g, beta, K ** -0.5, pool, idx, inter_states=inter,
+                                      o=o)
+
+    fns = [make(i) for i in range(ROTATE_SETS)]
+    ms = _time_rotating(fns, steps, warmup)
+    ms_flushed = _time_flushed(fns[0])
+    ms_b2b = _time(fns[0], max(steps, 20), warmup)
     nbytes = verify_bytes(B, Tv, H, K, V)
+    del fns
     return dict(ms=ms, tokens_per_s=B * Tv / (ms * 1e-3), bytes=nbytes,
                 gbs=nbytes / (ms * 1e-3) / 1e9, ms_flushed=ms_flushed,
-                gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9)
+                gbs_flushed=nbytes / (ms_flushed * 1e-3) / 1e9, ms_b2b=ms_b2b,
+                gbs_b2b=nbytes / (ms_b2b * 1e-3) / 1e9)
 
 
 def _event_ms(fn, reps: int = 5) -> float:
@@ -525,6 +575,8 @@ def roofline(r):
     (or flops) / the stage's mean duration per call."""
     w, T, N, H = r["workload"], r["T"], r["N"], r["H"]
     K, V, C = w["K"], w["V"], w["chunk"]
+    sched = kda.kda_chunk_prefill_schedule(T, N, H, K, V, C)
+    launches = {"intra": max(1, sched["intra_launches"]), "state": max(1, sched["state_launches"])}
     kern = max(("intra", "state"), key=lambda n: r["kernel_ms"][n])
     nbytes = r["intra_bytes"] if kern == "intra" else r["state_bytes"]
     flops = (intra_flops if kern == "intra" else state_flops)(T, H, K, V, C)
@@ -538,7 +590,10 @@ def roofline(r):
            "peak": peak, "unit": unit, "frac": achieved / peak,
            "traffic": None if ctr is None else ctr["bytes_per_launch"],
            "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-           "avg_ms": r["kernel_ms"][kern]}
+           "stage_ms": r["kernel_ms"][kern], "launches": launches[kern],
+           "avg_ms": r["kernel_ms"][kern] / launches[kern],
+           "algorithmic_bytes_per_launch": nbytes / launches[kern],
+           "schedule": sched}
     if ctr is not None:
         out["traffic_source"] = {"copied_from": ctr["copied_from"],
                                  "file_sha256": ctr["copied_from_sha256"],
@@ -685,6 +740,13 @@ def main():
         "ceilings": measure_ceilings,
     }
     if args.only is not None:
+        # one plain copy of known size first (64 Mi fp32 elements: 256 MiB
+        # read, 256 MiB written), against which profiler byte counters of
+        # the same run are scaled
+        x = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        torch.neg(x)
+        torch.cuda.synchronize()
+        del x
         r = only[args.only]()
         if isinstance(r, dict):
             r.pop("workload", None)
@@ -715,71 +777,58 @@ def main():
         "roofline": roofline(lp),
         "prefill": _prefill_entry(lp, "long_prefill_65536 (the step)"),
     }
-    _fresh_memory()
     line["prefill_share"] = _prefill_entry(
         bench_prefill_workload("long_prefill_65536", args.steps, args.warmup, H=4),
         "one GPU's share of long_prefill_65536 under an 8-way head split: T=65536, H=4")
-    _fresh_memory()
     cr = bench_carried(args.steps, args.warmup)
     line["prefill_carried"] = {"workload": "long_prefill_65536 as 16 consecutive 4096-token "
                                            "calls, the state carried in place",
                                "tokens_per_s": cr["tokens_per_s"], "ms": cr["ms_median"],
                                "ms_min": cr["ms_min"], "reps": cr["reps"]}
-    _fresh_memory()
     vp = bench_prefill_workload("varlen_prefill_7680", args.steps, args.warmup)
     line["prefill_varlen"] = _prefill_entry(
         vp, "varlen_prefill_7680: 4 packed sequences {512,1024,2048,4096}, H=32, K=V=128")
-    _fresh_memory()
     gs = bench_gate_and_snapshots(args.steps, args.warmup)
     line["prefill_varlen"].update(
         ms_gate_prep=gs["ms_gate"], gate_gbs=gs["gate_gbs"],
         ms_gate_prep_then_prefill=gs["ms_gate_prep_then_prefill"],
         with_snapshots_every_256={"ms": gs["ms_with_snapshots_every_256"],
                                   "snapshot_bytes": gs["snapshot_bytes"]})
-    _fresh_memory()
+    timing_rot = (f"mean over a steady stream of calls rotating over {ROTATE_SETS} private "
+                  "copies of the buffers, each call's inputs cold in every cache and its "
+                  "write-backs paid inside the stream")
+    timing_cold = ("median of single calls, each after a 512 MiB write and read that empty "
+                   "the last-level cache (dirty lines a call leaves in the caches are written "
+                   "back after the timed region)")
+
+    def family(r, what, n_tok, **extra):
+        out = {"workload": what, "timing": timing_rot,
+               "tokens_per_s": n_tok / (r["ms"] * 1e-3), "ms": r["ms"],
+               "algorithmic_bytes": r["bytes"], "total_gbs": r["gbs"],
+               "frac_of_hbm_peak": r["gbs"] / HBM_PEAK_GBS,
+               "cache_cold_single_call": {"timing": timing_cold, "ms": r["ms_flushed"],
+                                          "total_gbs": r["gbs_flushed"],
+                                          "frac_of_hbm_peak": r["gbs_flushed"] / HBM_PEAK_GBS},
+               "back_to_back_same_buffers": {"ms": r["ms_b2b"], "total_gbs": r["gbs_b2b"]}}
+        out.update(extra)
+        return out
+
     d = bench_decode(args.steps, args.warmup)
-    line["decode"] = {"workload": "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",
-                      "timing": "median of single calls, each after a 512 MiB write and read "
-                                "that empty the last-level cache",
-                      "tokens_per_s": 256 / (d["ms_flushed"] * 1e-3), "ms": d["ms_flushed"],
-                      "state_gbs": d["state_gbs"] * d["ms"] / d["ms_flushed"],
-                      "total_gbs": d["gbs_flushed"],
-                      "frac_of_hbm_peak": d["gbs_flushed"] / HBM_PEAK_GBS,
-                      "back_to_back": {"ms": d["ms"], "tokens_per_s": d["tokens_per_s"],
-                                       "total_gbs": d["gbs"]}}
-    _fresh_memory()
+    line["decode"] = family(d, "decode_256: 256 requests, 512-slot fp32 pool, H=32, K=V=128",
+                            256, state_gbs=d["state_gbs"])
     dl = bench_decode_layer(args.steps, args.warmup)
     line["decode"]["with_layer_options"] = {
-        "what": "raw gate in the kernel, q/k L2 norm, gated RMSNorm of o (kda_recurrent_decode_ex)",
+        "what": "raw gate in the kernel, q/k L2 norm, gated RMSNorm of o (kda_recurrent_decode_ex), "
+                "same buffers back to back",
         "ms": dl["ms"], "tokens_per_s": dl["tokens_per_s"], "total_gbs": dl["gbs"],
         "frac_of_hbm_peak": dl["gbs"] / HBM_PEAK_GBS}
-    _fresh_memory()
     rp = bench_replay(args.steps, args.warmup)
-    line["replay_decode"] = {"workload": "decode_256 with a 16-entry ring per slot, cursors "
-                                         "staggered over the rows (kda_replay_decode)",
-                             "timing": "median of cache-cold single calls (as decode); "
-                                       "back to back beside it",
-                             "tokens_per_s": 256 / (rp["ms_flushed"] * 1e-3),
-                             "ms": rp["ms_flushed"], "algorithmic_bytes": rp["bytes"],
-                             "total_gbs": rp["gbs_flushed"],
-                             "frac_of_hbm_peak": rp["gbs_flushed"] / HBM_PEAK_GBS,
-                             "back_to_back": {"ms": rp["ms"], "tokens_per_s": rp["tokens_per_s"],
-                                              "total_gbs": rp["gbs"]},
-                             "mean_ring_entries": rp["mean_ring_entries"],
-                             "flush_frac": rp["flush_frac"],
-                             "speedup_vs_decode": d["ms_flushed"] / rp["ms_flushed"]}
-    _fresh_memory()
+    line["replay_decode"] = family(
+        rp, "decode_256 with a 16-entry ring per slot, cursors staggered over the rows "
+            "(kda_replay_decode)", 256, mean_ring_entries=rp["mean_ring_entries"],
+        flush_frac=rp["flush_frac"], speedup_vs_decode=d["ms"] / rp["ms"])
     vr = bench_verify(args.steps, args.warmup)
-    line["verify"] = {"workload": "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool",
-                      "timing": "median of single calls, each after a 512 MiB write and read "
-                                "that empty the last-level cache (the 134 MB of pool a call "
-                                "reads would otherwise stay cached between calls)",
-                      "tokens_per_s": 512 / (vr["ms_flushed"] * 1e-3), "ms": vr["ms_flushed"],
-                      "total_gbs": vr["gbs_flushed"],
-                      "frac_of_hbm_peak": vr["gbs_flushed"] / HBM_PEAK_GBS,
-                      "back_to_back": {"ms": vr["ms"], "tokens_per_s": vr["tokens_per_s"],
-                                       "total_gbs": vr["gbs"]}}
-    _fresh_memory()
+    line["verify"] = family(vr, "verify_64x8: 64 requests x 8 draft tokens, 128-slot pool", 512)
     cl = measure_ceilings()
     line["measured_ceilings"] = cl
     # each path against the measured stream of its access pattern: the decode
@@ -788,9 +837,9 @@ def main():
     mf = cl["bf16_mfma_16x16x32_tflops"]
     line["roofline"]["frac_of_measured"] = line["roofline"]["achieved"] / (
         cl["hbm_copy_gbs"] if line["roofline"]["unit"] == "GB/s" else mf)
-    line["decode"]["frac_of_measured_rmw"] = d["gbs_flushed"] / cl["hbm_rmw_gbs"]
-    line["replay_decode"]["frac_of_measured_copy"] = rp["gbs_flushed"] / cl["hbm_copy_gbs"]
-    line["verify"]["frac_of_measured_copy"] = vr["gbs_flushed"] / cl["hbm_copy_gbs"]
+    line["decode"]["frac_of_measured_rmw"] = d["gbs"] / cl["hbm_rmw_gbs"]
+    line["replay_decode"]["frac_of_measured_copy"] = rp["gbs"] / cl["hbm_copy_gbs"]
+    line["verify"]["frac_of_measured_copy"] = vr["gbs"] / cl["hbm_copy_gbs"]
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baselines(long_inputs, lp["workload"])
     print(json.dumps(line))

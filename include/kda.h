@@ -21,10 +21,24 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer owned by the caller, to a
  *     row-major contiguous array, 16-byte aligned.  The library allocates no
- *     memory, keeps no global mutable state, never synchronises the stream,
- *     and may be called from several host threads at once.
+ *     memory for the caller's data, never synchronises the stream, and may
+ *     be called from several host threads at once.  Its only global state is
+ *     per device: one library-owned second stream with a pool of events
+ *     (created on first use, kept until the process ends; see below), and
+ *     the static scratch array of kda_chunk_prefill_noalloc.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
- *     All work is enqueued on it; a return of KDA_OK means "enqueued".
+ *     All work is ordered on it; a return of KDA_OK means "enqueued".  One
+ *     exception to "all work runs on it": a prefill whose state chain is cut
+ *     into waves (long sequences, few of them; kda_chunk_prefill_schedule in
+ *     kda_profile.h tells) runs the intra-chunk kernel of each wave on the
+ *     library's second stream of the current device (non-blocking, default
+ *     priority), so that it overlaps the state pass of the previous wave.
+ *     That stream first waits for the work already on `stream`, and the
+ *     call's last kernel on `stream` waits for all it ran, so work enqueued
+ *     on `stream` afterwards sees the finished results, exactly as with one
+ *     stream.  The call keeps to `stream` alone when `stream` belongs to
+ *     another device than the current one, when it is being captured into a
+ *     graph, and in kda_chunk_prefill_noalloc.
  *   - States and gates are always fp32.  q, k, v and o share the io dtype.
  *   - State layout is [.., H, K, V] with V contiguous: row i of a head's
  *     state belongs to key channel i.

@@ -2006,6 +2006,14 @@ bool stream_on_current_device(hipStream_t st) {
          dev == cur;
 }
 
+// A stream being captured into a graph keeps the whole schedule: the second
+// stream is used only for eager work.
+bool stream_capturing(hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return st != nullptr && (hipStreamIsCapturing(st, &cs) != hipSuccess ||
+                           cs != hipStreamCaptureStatusNone);
+}
+
 template <typename IO, int D, int C>
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   typedef Geom<D, C> Gm;
@@ -2062,6 +2070,7 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     hipStream_t aux = nullptr;
     std::vector<hipEvent_t> ev;
     const bool two = !a.single_stream && stream_on_current_device(st) &&
+                     !stream_capturing(st) &&
                      aux_acquire(cut.n_waves + 1, aux, ev) == hipSuccess;
     if (two) {
       // wave p's intra-chunk work on the second stream, its state pass on

@@ -319,3 +319,47 @@ def test_wave_schedule_equals_single_stream_and_oracle():
                                       t["beta"][:L], cu1, 0.125, h0=t["h0"][:1], chunk=64)
     torch.cuda.synchronize()
     assert torch.equal(snaps[8], ht_pre[0])
+
+
+def test_wave_schedule_under_graph_capture():
+    """A waved prefill captured into a HIP graph keeps to the capturing
+    stream (the second stream is for eager calls only).  Every replay, with
+    eager work and a cleared output between replays, equals the eager call
+    bit for bit, and so does an eager call on a side stream."""
+    seqlens = [3000, 50, 1200, 0]
+    assert kda.kda_chunk_prefill_schedule(sum(seqlens), len(seqlens), 32, 64, 64)["n_waves"] > 1
+    c = kda_synth.prefill_case(seqlens, 32, 64, 64, "bf16", seed=53, regime="long", h0_std=0.05)
+    t, _, _ = _inputs(c)
+    a, b = dev(c["a"]), dev(c["b"])
+    A_log, dt_bias = dev(c["A_log"]), dev(c["dt_bias"])
+    T, N = int(c["T"]), len(seqlens)
+    o = torch.empty_like(t["v"])
+    ht = torch.empty_like(t["h0"])
+    ws = torch.empty(kda.kda_chunk_prefill_workspace_size(T, N, 32, 64, 64, 64),
+                     dtype=torch.uint8, device="cuda")
+    call = lambda: kda.kda_chunk_prefill_gated(t["q"], t["k"], t["v"], a, b, A_log, dt_bias,
+                                               t["cu"], 0.125, h0=t["h0"], chunk=64, o=o, ht=ht,
+                                               workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    o_ref, ht_ref = o.clone(), ht.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        o.zero_()
+        call()
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    for _ in range(3):
+        o.zero_()
+        ht.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(ht, ht_ref)
+        call()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref)
