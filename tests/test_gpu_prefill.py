@@ -286,12 +286,13 @@ def test_malformed_cu_seqlens_stay_in_bounds(cu_bad, T):
 
 
 def test_wave_schedule_equals_single_stream_and_oracle():
-    """A batch whose longest possible chain has at least 32 chunks runs its
+    """A batch of few sequences with at least 128 chunks in all runs its
     state pass in waves, the intra-chunk work of each wave on a second
     stream: the results equal the single-stream order (the timing-marks call
     runs every kernel on one stream) bit for bit, with and without the gate
     in the kernel and with snapshots, and match the oracle."""
-    seqlens = [3000, 50, 1200, 0]
+    seqlens = [6000, 50, 2400, 0]
+    assert kda.kda_chunk_prefill_schedule(sum(seqlens), len(seqlens), 32, 64, 64)["n_waves"] > 1
     c = kda_synth.prefill_case(seqlens, 32, 64, 64, "bf16", seed=51, regime="long", h0_std=0.05)
     t, g, beta = _inputs(c)
     a, b = dev(c["a"]), dev(c["b"])
@@ -326,7 +327,7 @@ def test_wave_schedule_under_graph_capture():
     stream (the second stream is for eager calls only).  Every replay, with
     eager work and a cleared output between replays, equals the eager call
     bit for bit, and so does an eager call on a side stream."""
-    seqlens = [3000, 50, 1200, 0]
+    seqlens = [6000, 50, 2400, 0]
     assert kda.kda_chunk_prefill_schedule(sum(seqlens), len(seqlens), 32, 64, 64)["n_waves"] > 1
     c = kda_synth.prefill_case(seqlens, 32, 64, 64, "bf16", seed=53, regime="long", h0_std=0.05)
     t, _, _ = _inputs(c)
