@@ -107,3 +107,21 @@ def test_cut_chain_snapshots():
                                    np.array([0, L]), 0.125, c["h0"][n:n + 1])
         row = j if n == 0 else rows0 + j
         assert rel_err_blocks(snaps[row:row + 1], st_ref, 2) <= TOL["bf16"], (n, j)
+
+
+def test_cut_chain_long_memory_eight_heads():
+    # one 16384-token sequence on 8 heads at K = V = 128 (affine maps, eight
+    # segments of 32 chunks), every head against the oracle in the
+    # slow-decay regime, whose carried state reaches across the cuts
+    s = kda.kda_chunk_prefill_schedule(16384, 1, 8, 128, 128, 64)
+    assert s["uses_maps"] == 1 and s["segment_chunks"] > 0
+    c = kda_synth.prefill_case([16384], 8, 128, 128, "bf16", seed=45, regime="long",
+                               h0_std=0.05)
+    t, g, beta = _run(c, 64, 128 ** -0.5)
+    scale = 128 ** -0.5
+    o, ht = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], scale,
+                                  h0=t["h0"], chunk=64)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, c["cu"], scale, c["h0"])
+    assert_io_output(host(o), o_ref, "bf16", 1)
+    assert rel_err_blocks(host(ht), ht_ref, 2) <= TOL["bf16"]
