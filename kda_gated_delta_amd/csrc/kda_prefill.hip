@@ -283,7 +283,7 @@ StateCut state_cut(int64_t T, int N, int H, int D, int C) {
 // segments, at most NSEG each; with waves, [waves, N] units instead), the
 // unit counts and the waves' chunk-table offsets, then the per-chunk
 // records, and with a cut chain the start states [NSEG, H, D, D] and maps
-// [NSEG, H, D, 2 D] (fp32).
+// [NSEG, H, D, 2 D] (fp32; each map in 4-column tiles, see state_unit).
 struct WsLayout {
   size_t table_off, seq_off, unit_a_off, unit_m_off, unit_c_off, unit_w_off, count_off,
       wave_off, rec_off, start_off, map_off, total;
@@ -1838,12 +1838,26 @@ __device__ __forceinline__ void state_unit(
   for (int ch = c_begin; ch < c_last; ++ch) process(ops, ch);
 
   // the final state: ht (the whole sequence or its last segment), the next
-  // segment's start slot, or the map slot ([K, 2 D] rows per head)
+  // segment's start slot, or the map slot.  A map [M | B] (D rows, 2 D
+  // columns per head) is stored in 4-column tiles, element (i, j) at
+  // ((j / 4) D + i) 4 + j % 4, so that the scan's row-per-thread reads of
+  // four columns are contiguous across threads.
   float* dst = nullptr;
-  int ld = D;
   if (MAP) {
-    dst = maps + ((size_t)out_slot * H + h) * D * 2 * D;
-    ld = 2 * D;
+    float* mp = maps + ((size_t)out_slot * H + h) * D * 2 * D;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      const int ms = w + 4 * i;
+      if (ALL_MS || ms < MTD) {
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int row = 16 * ms + 4 * lg + e, col = vt * VT + 16 * nt + lr;
+            mp[((size_t)(col >> 2) * D + row) * 4 + (col & 3)] = S[i][nt][e];
+          }
+      }
+    }
   } else if (flags & UNIT_WRITE_NEXT) {
     dst = starts + ((size_t)out_slot * H + h) * D * D;
   } else if ((flags & UNIT_WRITE_HT) && ht != nullptr) {
@@ -1858,7 +1872,7 @@ __device__ __forceinline__ void state_unit(
         for (int nt = 0; nt < NTV; ++nt)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            dst[(size_t)(16 * ms + 4 * lg + e) * ld + vt * VT + 16 * nt + lr] = S[i][nt][e];
+            dst[(size_t)(16 * ms + 4 * lg + e) * D + vt * VT + 16 * nt + lr] = S[i][nt][e];
       }
     }
   }
@@ -1902,7 +1916,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void state_kernel(
 // segment p + 1 = M_p start(p - 1) + B_p for the middle segments p = 1 ..
 // nseg - 2, in order (start slot 0 of the sequence holds the first segment's
 // final state).  One workgroup per (sequence, head, group of 4 columns), one
-// thread per row; fp32 throughout.
+// thread per row; fp32 throughout.  The maps' 4-column tiles make a wave's
+// reads of 16-byte row pieces contiguous.  A thread holds its row of M_p in
+// registers, and each 16-byte piece of the next map's row is requested as
+// soon as this step has used that piece: the loads of step p + 1 are in
+// flight while step p computes, so the serial chain pays the load latency
+// once instead of at every step.
 template <int D>
 __global__ __launch_bounds__(D) void scan_kernel(const SeqInfo* __restrict__ seqs, int N, int H,
                                                  int C, int seg_len,
@@ -1918,23 +1937,64 @@ __global__ __launch_bounds__(D) void scan_kernel(const SeqInfo* __restrict__ seq
   const int nseg = nch > seg_len ? (nch + seg_len - 1) / seg_len : 1;
   if (nseg < 3) return;
   const int i = threadIdx.x;
+  // row i of map p, [M_p | B_p] in 4-column tiles: columns 4 j4 .. 4 j4 + 3
+  // of row i at float4 j4 D + i
+  auto map_row = [&](int p) {
+    return reinterpret_cast<const float4*>(maps + ((size_t)(si.map_slot + p - 1) * H + h) * D * 2 * D) + i;
+  };
+  float4 m[D / 4];
+  float4 bp;
+  {
+    const float4* M = map_row(1);
+#pragma unroll
+    for (int j4 = 0; j4 < D / 4; ++j4) m[j4] = M[j4 * D];
+    bp = M[(D / 4 + cg) * D];
+  }
   float4 x = *reinterpret_cast<const float4*>(starts + (((size_t)si.start_slot * H + h) * D + i) * D +
                                               4 * cg);
+  // L2 prefetch two maps ahead: the groups workgroups of a (sequence, head)
+  // each touch one word of every groups-th 128-byte line of that map; the
+  // word is consumed a step later, when it has long arrived
+  constexpr int LINES = D * 2 * D * 4 / 128;
+  constexpr int NPF = (LINES / groups + D - 1) / D;
+  int pf[NPF];
+#pragma unroll
+  for (int q = 0; q < NPF; ++q) pf[q] = 0;
   for (int p = 1; p <= nseg - 2; ++p) {
+#pragma unroll
+    for (int q = 0; q < NPF; ++q) asm volatile("" ::"v"(pf[q]));
+    {
+      const int pp = p + 2 <= nseg - 2 ? p + 2 : nseg - 2;
+      const int* mw = reinterpret_cast<const int*>(
+          maps + ((size_t)(si.map_slot + pp - 1) * H + h) * D * 2 * D);
+#pragma unroll
+      for (int q = 0; q < NPF; ++q) {
+        // unconditional (a line past the map repeats line 0): a select on
+        // the loaded word would make the wave wait for it here
+        const int line = cg + groups * (i + D * q);
+        pf[q] = mw[(line < LINES ? line : 0) * 32];
+      }
+    }
     sS[i] = x;
     __syncthreads();
-    const float* M = maps + (((size_t)(si.map_slot + p - 1) * H + h) * D + i) * 2 * D;
-    float4 acc = *reinterpret_cast<const float4*>(M + D + 4 * cg);  // B_p
-#pragma unroll 4
-    for (int j = 0; j < D; j += 4) {
-      const float4 m = *reinterpret_cast<const float4*>(M + j);
-      acc = fma4(m.x, sS[j], acc);
-      acc = fma4(m.y, sS[j + 1], acc);
-      acc = fma4(m.z, sS[j + 2], acc);
-      acc = fma4(m.w, sS[j + 3], acc);
+    // the next map's row (the last step re-reads its own: never used)
+    const float4* Mn = map_row(p + 1 <= nseg - 2 ? p + 1 : p);
+    // four partial sums (j4 mod 4), so that no single fma chain runs the
+    // length of the row
+    float4 acc[4] = {bp, f4(0.f), f4(0.f), f4(0.f)};
+    bp = Mn[(D / 4 + cg) * D];
+#pragma unroll
+    for (int j4 = 0; j4 < D / 4; ++j4) {
+      const float4 mm = m[j4];
+      float4& a = acc[j4 & 3];
+      a = fma4(mm.x, sS[4 * j4], a);
+      a = fma4(mm.y, sS[4 * j4 + 1], a);
+      a = fma4(mm.z, sS[4 * j4 + 2], a);
+      a = fma4(mm.w, sS[4 * j4 + 3], a);
+      m[j4] = Mn[j4 * D];
     }
     __syncthreads();
-    x = acc;
+    x = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     *reinterpret_cast<float4*>(starts + (((size_t)(si.start_slot + p) * H + h) * D + i) * D +
                                4 * cg) = x;
   }
