@@ -227,11 +227,13 @@ struct Unit {
 //    chunk maps side by side.  The segment count P (smooth values; 16 even
 //    segments of 64 chunks beat 17 of 61 by 15% on one 65536-token
 //    sequence) minimises the chunk steps on the critical path: the first
-//    launch runs the first segments and the maps (a map step costs about 0.6
-//    of a full step: no read-out), the maps beyond the chip's width in
-//    further rounds; the second launch re-runs the P - 1 later segments; the
-//    scan adds about half a step per segment.  Taken only when that beats
-//    the whole chain by a quarter.
+//    launch runs the first segments and the maps, the maps beyond the chip's
+//    width in further rounds (a full step per round: a map workgroup carries
+//    as many columns as a state one, without the read-out but with twice the
+//    workgroups); the second launch re-runs the P - 1 later segments; the
+//    scan adds about 0.6 of a step per segment.  (Fitted to the 65536-token
+//    sequence at H = 4: 32, 16 and 8 segments measured 459, 421 and 545 us.)
+//    Taken only when that beats the whole chain by a quarter.
 //  - waves: otherwise, when the chains still leave CUs free (so that the
 //    intra-chunk kernel has room beside the state pass) and a chain can
 //    reach 128 chunks, the chain is cut into about 8 waves of at least 16
@@ -260,9 +262,9 @@ StateCut state_cut(int64_t T, int N, int H, int D, int C) {
       if (len < 32) break;
       const int64_t first = (int64_t)N * H * NV, maps = (P - 2) * H * NM;
       const int64_t spill = first + maps > STATE_CUS ? first + maps - STATE_CUS : 0;
-      const double a = 1.0 + 0.6 * (double)rounds(spill);
+      const double a = 1.0 + (double)rounds(spill);
       const double c = (double)rounds((P - 1) * H * NV);
-      const double cost = (a + c) * (double)len + 0.5 * (double)(P - 2);
+      const double cost = (a + c) * (double)len + 0.6 * (double)(P - 2);
       if (cost < best) {
         best = cost;
         cut.seg_len = (int)len;
