@@ -125,3 +125,19 @@ def test_cut_chain_long_memory_eight_heads():
     o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, c["cu"], scale, c["h0"])
     assert_io_output(host(o), o_ref, "bf16", 1)
     assert rel_err_blocks(host(ht), ht_ref, 2) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("T,H,chunk,io", [(8192, 2, 16, "bf16"), (65536, 1, 16, "f32")])
+def test_cut_chain_small_heads_long_scan(T, H, chunk, io):
+    # K = V = 16: one V tile per head; the 65536-token case cuts 4096 chunks
+    # into 64 segments, so the scan chains 62 maps
+    s = kda.kda_chunk_prefill_schedule(T, 1, H, 16, 16, chunk)
+    assert s["uses_maps"] == 1
+    c = kda_synth.prefill_case([T], H, 16, 16, io, seed=46, regime="long", h0_std=0.1)
+    t, g, beta = _run(c, chunk, 0.25)
+    o, ht = kda.kda_chunk_prefill(t["q"], t["k"], t["v"], t["g"], t["beta"], t["cu"], 0.25,
+                                  h0=t["h0"], chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle.prefill(c["q"], c["k"], c["v"], g, beta, c["cu"], 0.25, c["h0"])
+    assert_io_output(host(o), o_ref, io, 1)
+    assert rel_err_blocks(host(ht), ht_ref, 2) <= TOL[io]
