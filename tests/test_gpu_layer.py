@@ -141,10 +141,12 @@ def test_l2norm_and_output_norm_match_oracle(io, act):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-def test_verify_with_every_option(io):
+@pytest.mark.parametrize("Tv", [5, 11])
+def test_verify_with_every_option(io, Tv):
     # raw safe gate, grouped heads, in-kernel L2 norm and the output norm,
-    # against the oracle, and each step against the same options in decode
-    Tv, B, H, HK, K, V = 5, 4, 4, 2, 64, 64
+    # against the oracle, and each step against the same options in decode;
+    # 11 draft tokens span two staged batches of 8, the second ragged
+    B, H, HK, K, V = 4, 4, 2, 64, 64
     c = _case(io, B=B, H=H, K=K, V=V, seed=7, Tv=Tv, regime="long")
     q, k = _raw_qk(c, 7)
     q, k = q[:, :, :HK], k[:, :, :HK]
