@@ -656,17 +656,6 @@ __device__ __forceinline__ float sumsq16(const uint4 x) {
   return s;
 }
 
-// Lane-broadcast helpers (DPP, no LDS): row_newbcast:n gives every lane of a
-// 16-lane row the value of lane n of that row; quad_perm[0,0,0,0] gives every
-// lane of a 4-lane quad the value of the quad's first lane.
-template <int N>
-__device__ __forceinline__ float bcast_row(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x150 + N, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float bcast_quad0(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x00, 0xf, 0xf, false));
-}
-
 // One step of a transposing reduction over a 16-lane row: the lane's first
 // 2 H sums are halved into H, keeping the upper half when `upper` (the index
 // bit of this step) is set and adding the partner lane's copy of the same
@@ -961,14 +950,20 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll 2
       for (int kt = 0; kt < KTD; ++kt) {
         const int c0 = 32 * kt + 8 * lg;
-        float k8[8], q8[8], g8[8];
+        // the reference rows' G come from LDS (the 16 lanes of a row read
+        // one address, a broadcast): r' = the first token of t's sub-block,
+        // and the first tokens 16 I + 4 sb of sub-blocks 1 .. 3
+        float k8[8], q8[8], g8[8], g0[8], gs[3][8];
         row_io8(sK, t, c0, k8);
         row_io8(sQ, t, c0, q8);
         row_g8(t, c0, g8);
+        row_g8(t & ~3, c0, g0);
+#pragma unroll
+        for (int sb = 1; sb < 4; ++sb) row_g8(16 * I + 4 * sb, c0, gs[sb - 1]);
         float ra[8], rq[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float e = ex2(g8[j] - bcast_quad0(g8[j]));  // G_t - G_r' <= 0
+          const float e = ex2(g8[j] - g0[j]);  // G_t - G_r' <= 0
           ra[j] = k8[j] * e;
           rq[j] = q8[j] * e;
         }
@@ -977,13 +972,8 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
         for (int sb = 1; sb < 4; ++sb) {
           float b8[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            float gref;
-            if (sb == 1) gref = bcast_row<4>(g8[j]);
-            else if (sb == 2) gref = bcast_row<8>(g8[j]);
-            else gref = bcast_row<12>(g8[j]);
-            b8[j] = k8[j] * ex2(gref - g8[j]);  // G_ref - G_j <= 0 for kept columns
-          }
+          for (int j = 0; j < 8; ++j)
+            b8[j] = k8[j] * ex2(gs[sb - 1][j] - g8[j]);  // G_ref - G_j <= 0 for kept columns
           const Frag fb = split8(b8);
           accA[sb - 1] = mma3(accA[sb - 1], fa, fb);
           accQ[sb - 1] = mma3(accQ[sb - 1], fq, fb);
@@ -1017,9 +1007,9 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
             row_g8(jr, c0, gj[u]);
           }
           float gr[8], ra[8], rq[8];
+          row_g8(16 * I, c0, gr);  // G at r = 16 I (a broadcast LDS read)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            gr[j] = bcast_row<0>(g8[j]);  // G at r = 16 I
             const float e = ex2(g8[j] - gr[j]);
             ra[j] = k8[j] * e;
             rq[j] = q8[j] * e;
@@ -1366,24 +1356,31 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
   __syncthreads();
 
   // ---- 8. W = M (K e^G), 32 rows at a time staged in LDS (over sAA) and
-  // written out as A fragments; a wave owns a 16-channel column tile and
-  // splits its B fragments once
+  // written out as A fragments; a wave owns 16-channel column tiles and
+  // splits their B fragments once, before the first half
+  constexpr int NTW = (MTD + NW - 1) / NW;  // column tiles per wave
+  Frag fbw[NTW][KTC];
+  #pragma unroll
+  for (int it_ = 0; it_ < NTW; ++it_) {
+    const int nt = w + it_ * NW;
+    if (nt >= MTD) break;
+#pragma unroll
+    for (int kt = 0; kt < KTC; ++kt) {
+      float b8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int jj = 32 * kt + 8 * lg + j;
+        b8[j] = jj < C ? sG[iP(jj, 16 * nt + lr)] : 0.f;
+      }
+      fbw[it_][kt] = split8(b8);
+    }
+  }
   for (int half = 0; half < (NB + 1) / 2; ++half) {
     #pragma unroll
-    for (int it_ = 0; it_ < (MTD + NW - 1) / NW; ++it_) {
+    for (int it_ = 0; it_ < NTW; ++it_) {
       const int nt = w + it_ * NW;
       if (nt >= MTD) break;
-      Frag fb[KTC];
-#pragma unroll
-      for (int kt = 0; kt < KTC; ++kt) {
-        float b8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int jj = 32 * kt + 8 * lg + j;
-          b8[j] = jj < C ? sG[iP(jj, 16 * nt + lr)] : 0.f;
-        }
-        fb[kt] = split8(b8);
-      }
+      const Frag (&fb)[KTC] = fbw[it_];
 #pragma unroll
       for (int m2 = 0; m2 < 2; ++m2) {
         const int mt = 2 * half + m2;
