@@ -950,9 +950,10 @@ __global__ __launch_bounds__(NT_INTRA, 4) void intra_kernel(
 #pragma unroll 2
       for (int kt = 0; kt < KTD; ++kt) {
         const int c0 = 32 * kt + 8 * lg;
-        // the reference rows' G come from LDS (the 16 lanes of a row read
-        // one address, a broadcast): r' = the first token of t's sub-block,
-        // and the first tokens 16 I + 4 sb of sub-blocks 1 .. 3
+        // the reference rows' G come from LDS, read as broadcasts (lanes
+        // that share a reference row read one address): r' = the first
+        // token of t's sub-block (4 lanes), and the first tokens 16 I + 4 sb
+        // of sub-blocks 1 .. 3 (16 lanes)
         float k8[8], q8[8], g8[8], g0[8], gs[3][8];
         row_io8(sK, t, c0, k8);
         row_io8(sQ, t, c0, q8);
