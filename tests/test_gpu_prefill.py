@@ -125,6 +125,23 @@ def test_head_dims_and_chunk_sizes(io, D, chunk):
     _check(c, chunk)
 
 
+def _many_lengths(n):
+    """n sequence lengths 0 .. 60 in a fixed scrambled order (zeros, ones and
+    lengths on both sides of the 16-token chunk boundary included)."""
+    return [(i * 37) % 61 for i in range(n)]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_many_sequences_across_plan_blocks(io):
+    # 700 sequences: the chunk-table kernel takes them 256 at a time and
+    # carries the token, chunk and slot offsets from block to block; each
+    # sequence has its own initial state
+    c = kda_synth.prefill_case(_many_lengths(700), 2, 32, 32, io, seed=77, regime="long",
+                               h0_std=0.1)
+    assert len(c["cu"]) == 701 and int(c["cu"][-1]) > 16 * 700
+    _check(c, 16)
+
+
 @pytest.mark.parametrize("T", [1, 8, 64, 65, 128, 1024])
 def test_single_sequence_lengths(T):
     for io in ("f32", "bf16"):

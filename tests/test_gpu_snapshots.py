@@ -92,3 +92,11 @@ def test_snapshots_varlen_workload():
     c = kda_synth.prefill_case(w["seqlens"], w["H"], w["K"], w["V"], w["io"], seed=w["seed"],
                                dt_bias_std=w["dt_bias_std"], h0_std=w["h0_std"])
     _check(c, w["chunk"], 1024, against_oracle=False)
+
+
+def test_snapshots_many_sequences():
+    # 700 sequences of 0 .. 60 tokens: snapshot rows are numbered across the
+    # chunk-table kernel's blocks of 256 sequences
+    lengths = [(i * 37) % 61 for i in range(700)]
+    c = kda_synth.prefill_case(lengths, 2, 32, 32, "bf16", seed=78, h0_std=0.05)
+    _check(c, 16, 16)
