@@ -116,6 +116,55 @@ def test_decode_long_memory_many_steps(io):
     _check_decode(c, steps=12)
 
 
+def test_pool_past_4gib_byte_offsets():
+    """A 3000-slot pool at H = 32, K = V = 128 (6.3 GB, slot s at s x 2 MiB):
+    decode, then verify, on slots past 4 GiB and near the start, against the
+    oracle on copies of those slots; every other slot is left as it was."""
+    H, K, V, n_pool = 32, 128, 128, 3000
+    big = np.array([2999, 2048, 2500, 7, 2047, 2990, 0, 2049, 1500, 2995, 12, 2400])
+    assert big.max() * H * K * V * 4 > (1 << 32)
+    big_d = torch.from_numpy(big).cuda()
+    c = kda_synth.decode_case(10, H, K, V, n_slots=len(big), io="bf16", seed=33, n_padding=1)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(34)
+    pool = torch.empty((n_pool, H, K, V), device="cuda").normal_(0.0, 0.02, generator=gen)
+    pool[big_d] = dev(c["pool"])  # the case's compact pool at the mapped slots
+    before = pool.clone()
+    to_big = lambda idx: np.where(idx >= 0, big[np.maximum(idx, 0)], -1).astype(np.int32)
+    t, g, beta = _decode_inputs(c)
+    o = kda.kda_recurrent_decode(t["q"], t["k"], t["v"], t["g"], t["beta"], _scale(K), pool,
+                                 dev(to_big(c["slot_idx"]), torch.int32))
+    o_ref, pool_ref = oracle.decode(c["q"], c["k"], c["v"], g, beta, _scale(K), c["pool"],
+                                    c["slot_idx"])
+    torch.cuda.synchronize()
+    assert_io_output(host(o), o_ref, "bf16", 1)
+    live = c["slot_idx"][c["slot_idx"] >= 0]
+    live_d = torch.from_numpy(big[live]).cuda()
+    assert rel_err_blocks(host(pool[live_d]), pool_ref[live], 2) <= TOL["bf16"]
+    others = torch.ones(n_pool, dtype=torch.bool, device="cuda")
+    others[live_d] = False
+    assert torch.equal(pool[others], before[others])
+    del before
+    # verify from the updated pool: read only, each step against the oracle
+    cv = kda_synth.decode_case(10, H, K, V, n_slots=len(big), io="bf16", seed=35, Tv=4,
+                               n_padding=1)
+    tv, gv, betav = _verify_inputs(cv)
+    compact = host(pool[big_d]).astype(np.float32)
+    before = pool.clone()
+    inter = torch.full((10, 4, H, K, V), float("nan"), device="cuda")
+    ov, inter = kda.kda_verify(tv["q"], tv["k"], tv["v"], tv["g"], tv["beta"], _scale(K), pool,
+                               dev(to_big(cv["slot_idx"]), torch.int32), inter_states=inter)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, before)
+    ov_ref, inter_ref = oracle.verify(cv["q"], cv["k"], cv["v"], gv, betav, _scale(K), compact,
+                                      cv["slot_idx"])
+    lv = cv["slot_idx"] >= 0
+    assert_io_output(host(ov)[lv], ov_ref[lv], "bf16", 1)
+    assert rel_err_blocks(host(inter)[lv], inter_ref[lv], 2) <= TOL["bf16"]
+    del pool, before, inter
+    torch.cuda.empty_cache()
+
+
 # ---------------------------------------------------------------- verify
 
 def _verify_inputs(c):
