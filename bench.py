@@ -625,7 +625,8 @@ def cpu_baselines(long_inputs, workload):
     all host cores (one thread per (sequence or request, head)), by wall
     clock: the 65536-token sequence on 16 of its 32 heads (gate +
     recurrence; tokens/s scaled to 32 heads), the varlen batch whole, the
-    decode and verify workloads whole."""
+    decode and verify workloads whole.  Each also gets a single-thread rate,
+    from a smaller slice on one thread scaled to the whole workload."""
     import oracle  # test infrastructure: used only for these reported baselines
 
     nthreads = os.cpu_count() or 1
@@ -645,6 +646,18 @@ def cpu_baselines(long_inputs, workload):
         value=c["T"] / (dt * H / Hs), unit="tokens/s", cores=nthreads, kind="oracle",
         sample=f"the 65536-token sequence on {Hs} of its {H} heads (gate + token-serial fp64 "
                f"recurrence), {dt:.1f} s wall, scaled to {H} heads; CPU: {cpu}")
+    # one thread: head 0, the first quarter of the sequence
+    Tq = c["T"] // 4
+    one = lambda x: np.ascontiguousarray(x[:Tq, :1])
+    t0 = time.time()
+    g1, b1 = oracle.gate(one(c["a"]), one(c["b"]), c["A_log"][:1], c["dt_bias"][:1])
+    oracle.prefill(one(c["q"]), one(c["k"]), one(c["v"]), g1.astype(np.float32),
+                   b1.astype(np.float32), np.array([0, Tq]), workload["K"] ** -0.5,
+                   np.ascontiguousarray(c["h0"][:, :1]), nthreads=1)
+    dt1 = time.time() - t0
+    out["long_prefill_65536"]["single_thread"] = dict(
+        value=Tq / (dt1 * H), unit="tokens/s",
+        sample=f"head 0 on its first {Tq} tokens on one thread, {dt1:.2f} s, scaled to {H} heads")
     del g, beta
     # varlen batch, whole
     _, cv, _ = prefill_setup("varlen_prefill_7680")
@@ -655,6 +668,17 @@ def cpu_baselines(long_inputs, workload):
     dt = time.time() - t0
     out["varlen_prefill_7680"] = dict(value=cv["T"] / dt, unit="tokens/s", cores=nthreads,
                                       kind="oracle", sample=f"the whole batch, {dt:.2f} s wall")
+    Hv = cv["q"].shape[1]
+    one = lambda x: np.ascontiguousarray(x[:, :1])
+    t0 = time.time()
+    g1, b1 = oracle.gate(one(cv["a"]), one(cv["b"]), cv["A_log"][:1], cv["dt_bias"][:1])
+    oracle.prefill(one(cv["q"]), one(cv["k"]), one(cv["v"]), g1.astype(np.float32),
+                   b1.astype(np.float32), cv["cu"], 128 ** -0.5,
+                   np.ascontiguousarray(cv["h0"][:, :1]), nthreads=1)
+    dt1 = time.time() - t0
+    out["varlen_prefill_7680"]["single_thread"] = dict(
+        value=cv["T"] / (dt1 * Hv), unit="tokens/s",
+        sample=f"head 0 of the batch on one thread, {dt1:.2f} s, scaled to {Hv} heads")
     # decode and verify workloads, whole
     wd = kda_synth.WORKLOADS["decode_256"]
     cd = kda_synth.decode_case(wd["B"], wd["H"], wd["K"], wd["V"], wd["n_slots"], wd["io"],
@@ -668,6 +692,19 @@ def cpu_baselines(long_inputs, workload):
     dt = time.time() - t0
     out["decode_256"] = dict(value=wd["B"] / dt, unit="tokens/s", cores=nthreads, kind="oracle",
                              sample=f"one decode call of the workload, {dt:.3f} s wall")
+    # (the single-thread samples take a pool of just their own slots: the
+    # oracle converts the whole pool it is given, a cost per call, not per
+    # request)
+    Bs = 16
+    pool_s = np.ascontiguousarray(cd["pool"][cd["slot_idx"][:Bs]])
+    t0 = time.time()
+    oracle.decode(cd["q"][:Bs], cd["k"][:Bs], cd["v"][:Bs], gd[:Bs].astype(np.float32),
+                  bd[:Bs].astype(np.float32), wd["K"] ** -0.5, pool_s,
+                  np.arange(Bs, dtype=np.int32), nthreads=1)
+    dt1 = time.time() - t0
+    out["decode_256"]["single_thread"] = dict(
+        value=Bs / dt1, unit="tokens/s",
+        sample=f"{Bs} of the {wd['B']} requests on one thread, {dt1:.3f} s")
     wv = kda_synth.WORKLOADS["verify_64x8"]
     cvv = kda_synth.decode_case(wv["B"], wv["H"], wv["K"], wv["V"], wv["n_slots"], wv["io"],
                                 seed=wv["seed"], dt_bias_std=wv["dt_bias_std"],
@@ -683,6 +720,17 @@ def cpu_baselines(long_inputs, workload):
     dt = time.time() - t0
     out["verify_64x8"] = dict(value=B * Tv / dt, unit="tokens/s", cores=nthreads, kind="oracle",
                               sample=f"one verify call of the workload, {dt:.3f} s wall")
+    Bs = 8
+    pool_s = np.ascontiguousarray(cvv["pool"][cvv["slot_idx"][:Bs]])
+    t0 = time.time()
+    oracle.verify(cvv["q"][:Bs], cvv["k"][:Bs], cvv["v"][:Bs],
+                  gv.astype(np.float32).reshape(B, Tv, wv["H"], wv["K"])[:Bs],
+                  bv.astype(np.float32).reshape(B, Tv, wv["H"])[:Bs], wv["K"] ** -0.5,
+                  pool_s, np.arange(Bs, dtype=np.int32), nthreads=1)
+    dt1 = time.time() - t0
+    out["verify_64x8"]["single_thread"] = dict(
+        value=Bs * Tv / dt1, unit="tokens/s",
+        sample=f"{Bs} of the {B} requests on one thread, {dt1:.3f} s")
     head = dict(out["long_prefill_65536"])
     head["others"] = {k: v for k, v in out.items() if k != "long_prefill_65536"}
     return head
